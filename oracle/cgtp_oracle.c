@@ -1,0 +1,402 @@
+/*
+ * cgtp_oracle.c -- fp64 CPU oracle for the Clebsch-Gordan tensor-product (CGTP)
+ * convolution of equivariant interatomic potentials.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The GPU library
+ * (libcgtp.so) shares no code, header, table or constant with this file.
+ *
+ * What it computes and where that is stated:
+ *   - the CG selection rules |l1-l2| <= l3 <= l1+l2, m3 = m1+m2 ("Tensor
+ *     Decomposition Networks ...", rebuttal to reviewer S6y1, first answer);
+ *     the CG tensor as the coordinates of the SO(3) tensor product in the
+ *     coupled basis (same page, rebuttal to reviewer 7Mvd, last answer);
+ *   - the CGTP convolution whose cost LunaTP attacks ("LunaTP: Enabling
+ *     Efficient and Scalable Tensor Product for Equivariant MLIPs",
+ *     Abstract): for every edge j->i, node features of j are coupled with the
+ *     spherical harmonics of the edge through the real-basis CG coefficients,
+ *     scaled by per-edge, per-path, per-channel weights and summed into i;
+ *   - the gradient of a bilinear map with respect to each of its inputs
+ *     (TDN rebuttal to S6y1, the backward formulas after Equation (3)),
+ *     applied to the trilinear form <G, out(x, Y, W)>.
+ * Formulas the pages leave open are textbook: Racah's closed formula for the
+ * complex CG coefficients (Condon-Shortley phase), the unitary change from the
+ * complex to the real spherical-harmonic basis, and the closed forms of the
+ * orthonormal real spherical harmonics for l <= 3.
+ *
+ * Conventions:
+ *   component index k(l,m) = l*l + l + m, m = -l..l
+ *   paths (l1,l2,l3) in lexicographic order, no parity filter
+ *   x[N][D_in][C], Y[E][D_sh], W[E][P][C], out/G/dx[N][D][C], dW[E][P][C],
+ *   dY[E][D_sh]; receiver-sorted CSR row_ptr[N+1], src[E] (int64 here).
+ * Everything is fp64.  Loops are the plain definition: no blocking, fusion or
+ * reordering.  OpenMP only splits independent output rows across threads
+ * (per-thread buffers for the scattered dx, summed at the end).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_MAXL 6
+
+static double orc_fact(int n)
+{
+    double r = 1.0;
+    for (int i = 2; i <= n; ++i) r *= (double)i;
+    return r;
+}
+
+/* <j1 m1 j2 m2 | J M> in the complex basis (Racah's closed formula). */
+double orc_cg_complex(int j1, int m1, int j2, int m2, int J, int M)
+{
+    if (M != m1 + m2) return 0.0;
+    if (j1 < 0 || j2 < 0 || J < 0) return 0.0;
+    if (J < abs(j1 - j2) || J > j1 + j2) return 0.0;
+    if (abs(m1) > j1 || abs(m2) > j2 || abs(M) > J) return 0.0;
+    double pre = sqrt((2.0 * J + 1.0) * orc_fact(J + j1 - j2) * orc_fact(J - j1 + j2) *
+                      orc_fact(j1 + j2 - J) / orc_fact(j1 + j2 + J + 1));
+    pre *= sqrt(orc_fact(J + M) * orc_fact(J - M) * orc_fact(j1 - m1) * orc_fact(j1 + m1) *
+                orc_fact(j2 - m2) * orc_fact(j2 + m2));
+    double sum = 0.0;
+    for (int k = 0; k <= j1 + j2 + J; ++k) {
+        int a = j1 + j2 - J - k, b = j1 - m1 - k, c = j2 + m2 - k;
+        int d = J - j2 + m1 + k, e = J - j1 - m2 + k;
+        if (a < 0 || b < 0 || c < 0 || d < 0 || e < 0) continue;
+        double term = 1.0 / (orc_fact(k) * orc_fact(a) * orc_fact(b) * orc_fact(c) *
+                             orc_fact(d) * orc_fact(e));
+        sum += (k & 1) ? -term : term;
+    }
+    return pre * sum;
+}
+
+/* Row m (real), column mu (complex) of the unitary complex->real change of
+ * basis for degree l, so that Y_real[m] = sum_mu U[m][mu] Y_complex[mu]. */
+static void orc_U(int l, int m, int mu, double* re, double* im)
+{
+    const double s = 1.0 / sqrt(2.0);
+    const double sgn = (abs(m) & 1) ? -1.0 : 1.0; /* (-1)^m */
+    *re = 0.0;
+    *im = 0.0;
+    (void)l;
+    if (m == 0) {
+        if (mu == 0) *re = 1.0;
+    } else if (m > 0) {
+        if (mu == m) *re = sgn * s;
+        else if (mu == -m) *re = s;
+    } else {
+        if (mu == m) *im = s;
+        else if (mu == -m) *im = -sgn * s;
+    }
+}
+
+/* Real-basis coupling tensor of path (l1,l2,l3) before taking a real part:
+ * S[m1][m2][m3] = sum U1[m1][mu1] U2[m2][mu2] conj(U3[m3][mu3]) <l1 mu1 l2 mu2|l3 mu3>.
+ * Dense, index ((m1+l1)*(2l2+1) + (m2+l2))*(2l3+1) + (m3+l3). */
+void orc_real_cg_parts(int l1, int l2, int l3, double* re_out, double* im_out)
+{
+    const int d1 = 2 * l1 + 1, d2 = 2 * l2 + 1, d3 = 2 * l3 + 1;
+    for (int m1 = -l1; m1 <= l1; ++m1)
+        for (int m2 = -l2; m2 <= l2; ++m2)
+            for (int m3 = -l3; m3 <= l3; ++m3) {
+                double sre = 0.0, sim = 0.0;
+                for (int u1 = -l1; u1 <= l1; ++u1)
+                    for (int u2 = -l2; u2 <= l2; ++u2) {
+                        int u3 = u1 + u2;
+                        if (u3 < -l3 || u3 > l3) continue;
+                        double cg = orc_cg_complex(l1, u1, l2, u2, l3, u3);
+                        if (cg == 0.0) continue;
+                        double ar, ai, br, bi, cr, ci;
+                        orc_U(l1, m1, u1, &ar, &ai);
+                        orc_U(l2, m2, u2, &br, &bi);
+                        orc_U(l3, m3, u3, &cr, &ci);
+                        ci = -ci; /* conjugate */
+                        /* (a*b) */
+                        double abr = ar * br - ai * bi, abi = ar * bi + ai * br;
+                        /* (a*b)*c */
+                        double pr = abr * cr - abi * ci, pi = abr * ci + abi * cr;
+                        sre += pr * cg;
+                        sim += pi * cg;
+                    }
+                int idx = ((m1 + l1) * d2 + (m2 + l2)) * d3 + (m3 + l3);
+                re_out[idx] = sre;
+                im_out[idx] = sim;
+            }
+    (void)d1;
+}
+
+/* Real CG tensor T of path (l1,l2,l3): Re S for even l1+l2+l3, Im S for odd;
+ * entries below 1e-14 in magnitude are set to exactly zero. */
+void orc_real_cg(int l1, int l2, int l3, double* T)
+{
+    const int n = (2 * l1 + 1) * (2 * l2 + 1) * (2 * l3 + 1);
+    double* re = (double*)malloc(sizeof(double) * n);
+    double* im = (double*)malloc(sizeof(double) * n);
+    orc_real_cg_parts(l1, l2, l3, re, im);
+    const int odd = (l1 + l2 + l3) & 1;
+    for (int i = 0; i < n; ++i) {
+        double v = odd ? im[i] : re[i];
+        T[i] = fabs(v) < 1e-14 ? 0.0 : v;
+    }
+    free(re);
+    free(im);
+}
+
+/* Paths (l1,l2,l3), l1<=lin, l2<=lsh, l3<=lout, |l1-l2|<=l3<=l1+l2, in
+ * lexicographic order.  Writes [P][3] into paths when non-NULL; returns P. */
+int orc_paths(int lin, int lsh, int lout, int* paths)
+{
+    int P = 0;
+    for (int l1 = 0; l1 <= lin; ++l1)
+        for (int l2 = 0; l2 <= lsh; ++l2)
+            for (int l3 = 0; l3 <= lout; ++l3) {
+                if (l3 < abs(l1 - l2) || l3 > l1 + l2) continue;
+                if (paths) {
+                    paths[3 * P + 0] = l1;
+                    paths[3 * P + 1] = l2;
+                    paths[3 * P + 2] = l3;
+                }
+                ++P;
+            }
+    return P;
+}
+
+/* Orthonormal real spherical harmonics (Condon-Shortley phase folded into the
+ * real basis), degrees 0..L (L <= 3), of the unit vector along each r[e].
+ * Y[e][l*l+l+m]. */
+void orc_sh(int L, int64_t E, const double* r, double* Y)
+{
+    const double pi = 3.14159265358979323846;
+    const int D = (L + 1) * (L + 1);
+    for (int64_t e = 0; e < E; ++e) {
+        double rx = r[3 * e + 0], ry = r[3 * e + 1], rz = r[3 * e + 2];
+        double n = sqrt(rx * rx + ry * ry + rz * rz);
+        double x = rx / n, y = ry / n, z = rz / n;
+        double* o = Y + e * D;
+        o[0] = 0.5 * sqrt(1.0 / pi);
+        if (L >= 1) {
+            double c1 = sqrt(3.0 / (4.0 * pi));
+            o[1] = c1 * y;
+            o[2] = c1 * z;
+            o[3] = c1 * x;
+        }
+        if (L >= 2) {
+            o[4] = 0.5 * sqrt(15.0 / pi) * x * y;
+            o[5] = 0.5 * sqrt(15.0 / pi) * y * z;
+            o[6] = 0.25 * sqrt(5.0 / pi) * (3.0 * z * z - 1.0);
+            o[7] = 0.5 * sqrt(15.0 / pi) * x * z;
+            o[8] = 0.25 * sqrt(15.0 / pi) * (x * x - y * y);
+        }
+        if (L >= 3) {
+            o[9] = 0.25 * sqrt(35.0 / (2.0 * pi)) * y * (3.0 * x * x - y * y);
+            o[10] = 0.5 * sqrt(105.0 / pi) * x * y * z;
+            o[11] = 0.25 * sqrt(21.0 / (2.0 * pi)) * y * (5.0 * z * z - 1.0);
+            o[12] = 0.25 * sqrt(7.0 / pi) * (5.0 * z * z * z - 3.0 * z);
+            o[13] = 0.25 * sqrt(21.0 / (2.0 * pi)) * x * (5.0 * z * z - 1.0);
+            o[14] = 0.25 * sqrt(105.0 / pi) * z * (x * x - y * y);
+            o[15] = 0.25 * sqrt(35.0 / (2.0 * pi)) * x * (x * x - 3.0 * y * y);
+        }
+    }
+}
+
+/* Per-plan tables: path list and dense real CG tensors. */
+typedef struct {
+    int P;
+    int paths[3 * 64];
+    double* T[64];
+} orc_tables;
+
+static int orc_tables_make(int lin, int lsh, int lout, orc_tables* t)
+{
+    if (lin < 0 || lsh < 0 || lout < 0 || lin > ORC_MAXL || lsh > ORC_MAXL || lout > ORC_MAXL)
+        return -1;
+    t->P = orc_paths(lin, lsh, lout, NULL);
+    if (t->P > 64) return -1;
+    orc_paths(lin, lsh, lout, t->paths);
+    for (int p = 0; p < t->P; ++p) {
+        int l1 = t->paths[3 * p], l2 = t->paths[3 * p + 1], l3 = t->paths[3 * p + 2];
+        t->T[p] = (double*)malloc(sizeof(double) * (2 * l1 + 1) * (2 * l2 + 1) * (2 * l3 + 1));
+        orc_real_cg(l1, l2, l3, t->T[p]);
+    }
+    return 0;
+}
+
+static void orc_tables_free(orc_tables* t)
+{
+    for (int p = 0; p < t->P; ++p) free(t->T[p]);
+}
+
+/* Forward:
+ * out[i][k(l3,m3)][u] = sum_{e in seg(i)} sum_{p=(l1,l2,l3)} W[e][p][u]
+ *     sum_{m1,m2} T_p[m1][m2][m3] x[src e][k(l1,m1)][u] Y[e][k(l2,m2)].
+ * out is overwritten.  Returns 0, or -1 on unsupported degrees. */
+int orc_conv_fwd(int lin, int lsh, int lout, int C, int64_t N, int64_t E,
+                 const int64_t* row_ptr, const int64_t* src, const double* x,
+                 const double* Y, const double* W, double* out)
+{
+    orc_tables t;
+    if (orc_tables_make(lin, lsh, lout, &t)) return -1;
+    const int Din = (lin + 1) * (lin + 1), Dsh = (lsh + 1) * (lsh + 1);
+    const int Dout = (lout + 1) * (lout + 1);
+    const int P = t.P;
+    (void)E;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < N; ++i) {
+        double* o = out + i * Dout * C;
+        for (int q = 0; q < Dout * C; ++q) o[q] = 0.0;
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+            const int64_t j = src[e];
+            for (int p = 0; p < P; ++p) {
+                const int l1 = t.paths[3 * p], l2 = t.paths[3 * p + 1], l3 = t.paths[3 * p + 2];
+                const double* T = t.T[p];
+                for (int u = 0; u < C; ++u) {
+                    const double w = W[(e * P + p) * C + u];
+                    for (int m1 = -l1; m1 <= l1; ++m1)
+                        for (int m2 = -l2; m2 <= l2; ++m2)
+                            for (int m3 = -l3; m3 <= l3; ++m3) {
+                                double c = T[((m1 + l1) * (2 * l2 + 1) + (m2 + l2)) * (2 * l3 + 1) +
+                                             (m3 + l3)];
+                                if (c == 0.0) continue;
+                                double xv = x[(j * Din + l1 * l1 + l1 + m1) * C + u];
+                                double yv = Y[e * Dsh + l2 * l2 + l2 + m2];
+                                o[(l3 * l3 + l3 + m3) * C + u] += w * c * xv * yv;
+                            }
+                }
+            }
+        }
+    }
+    orc_tables_free(&t);
+    return 0;
+}
+
+/* Backward of L = <G, out>:
+ *   dx[j][k(l1,m1)][u] = sum_{e: src e = j} sum_p W[e][p][u]
+ *                          sum_{m2,m3} T_p[m1][m2][m3] Y[e][k(l2,m2)] G[dst e][k(l3,m3)][u]
+ *   dW[e][p][u]       = sum_{m1,m2,m3} T x[src e][k(l1,m1)][u] Y[e][k(l2,m2)] G[dst e][k(l3,m3)][u]
+ *   dY[e][k(l2,m2)]   = sum_u sum_p W[e][p][u] sum_{m1,m3} T x[src e][.][u] G[dst e][.][u]
+ * Any of dx, dW, dY may be NULL (skipped).  Outputs are overwritten. */
+int orc_conv_bwd(int lin, int lsh, int lout, int C, int64_t N, int64_t E,
+                 const int64_t* row_ptr, const int64_t* src, const double* x,
+                 const double* Y, const double* W, const double* G, double* dx,
+                 double* dW, double* dY)
+{
+    orc_tables t;
+    if (orc_tables_make(lin, lsh, lout, &t)) return -1;
+    const int Din = (lin + 1) * (lin + 1), Dsh = (lsh + 1) * (lsh + 1);
+    const int Dout = (lout + 1) * (lout + 1);
+    const int P = t.P;
+
+    /* receiver of every edge, from the CSR */
+    int64_t* dst = (int64_t*)malloc(sizeof(int64_t) * (E > 0 ? E : 1));
+    for (int64_t i = 0; i < N; ++i)
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) dst[e] = i;
+
+    /* dW and dY: independent per edge */
+    if (dW || dY) {
+#pragma omp parallel for schedule(dynamic, 64)
+        for (int64_t e = 0; e < E; ++e) {
+            const int64_t j = src[e], i = dst[e];
+            if (dY)
+                for (int q = 0; q < Dsh; ++q) dY[e * Dsh + q] = 0.0;
+            for (int p = 0; p < P; ++p) {
+                const int l1 = t.paths[3 * p], l2 = t.paths[3 * p + 1], l3 = t.paths[3 * p + 2];
+                const double* T = t.T[p];
+                for (int u = 0; u < C; ++u) {
+                    const double w = W[(e * P + p) * C + u];
+                    double acc = 0.0;
+                    for (int m1 = -l1; m1 <= l1; ++m1)
+                        for (int m2 = -l2; m2 <= l2; ++m2)
+                            for (int m3 = -l3; m3 <= l3; ++m3) {
+                                double c = T[((m1 + l1) * (2 * l2 + 1) + (m2 + l2)) * (2 * l3 + 1) +
+                                             (m3 + l3)];
+                                if (c == 0.0) continue;
+                                double xv = x[(j * Din + l1 * l1 + l1 + m1) * C + u];
+                                double yv = Y[e * Dsh + l2 * l2 + l2 + m2];
+                                double gv = G[(i * Dout + l3 * l3 + l3 + m3) * C + u];
+                                acc += c * xv * yv * gv;
+                                if (dY) dY[e * Dsh + l2 * l2 + l2 + m2] += w * c * xv * gv;
+                            }
+                    if (dW) dW[(e * P + p) * C + u] = acc;
+                }
+            }
+        }
+    }
+
+    /* dx: scatter over edges into per-thread buffers, then sum */
+    if (dx) {
+        const int64_t rowlen = (int64_t)Din * C;
+        for (int64_t q = 0; q < N * rowlen; ++q) dx[q] = 0.0;
+#pragma omp parallel
+        {
+            double* mine = dx;
+            int nthr = 1;
+#ifdef _OPENMP
+            nthr = omp_get_num_threads();
+#endif
+            if (nthr > 1) mine = (double*)calloc((size_t)(N * rowlen > 0 ? N * rowlen : 1), sizeof(double));
+#pragma omp for schedule(static)
+            for (int64_t e = 0; e < E; ++e) {
+                const int64_t j = src[e], i = dst[e];
+                for (int p = 0; p < P; ++p) {
+                    const int l1 = t.paths[3 * p], l2 = t.paths[3 * p + 1], l3 = t.paths[3 * p + 2];
+                    const double* T = t.T[p];
+                    for (int u = 0; u < C; ++u) {
+                        const double w = W[(e * P + p) * C + u];
+                        for (int m1 = -l1; m1 <= l1; ++m1)
+                            for (int m2 = -l2; m2 <= l2; ++m2)
+                                for (int m3 = -l3; m3 <= l3; ++m3) {
+                                    double c = T[((m1 + l1) * (2 * l2 + 1) + (m2 + l2)) * (2 * l3 + 1) +
+                                                 (m3 + l3)];
+                                    if (c == 0.0) continue;
+                                    double yv = Y[e * Dsh + l2 * l2 + l2 + m2];
+                                    double gv = G[(i * Dout + l3 * l3 + l3 + m3) * C + u];
+                                    mine[(j * Din + l1 * l1 + l1 + m1) * C + u] += w * c * yv * gv;
+                                }
+                    }
+                }
+            }
+            if (nthr > 1) {
+#pragma omp critical
+                for (int64_t q = 0; q < N * rowlen; ++q) dx[q] += mine[q];
+                free(mine);
+            }
+        }
+    }
+    free(dst);
+    orc_tables_free(&t);
+    return 0;
+}
+
+/* Sender-sorted view of a receiver-sorted CSR (the graph preparation the
+ * backward needs): a stable counting sort of the edges by sender.
+ *   srow_ptr[N+1]  offsets of each sender's out-edges
+ *   perm[E]        edge ids, grouped by sender, ascending edge id within a sender
+ *   sdst[E]        receiver of edge perm[k]                                    */
+void orc_graph_transpose(int64_t N, int64_t E, const int64_t* row_ptr, const int64_t* src,
+                         int64_t* srow_ptr, int64_t* perm, int64_t* sdst)
+{
+    for (int64_t j = 0; j <= N; ++j) srow_ptr[j] = 0;
+    for (int64_t e = 0; e < E; ++e) srow_ptr[src[e] + 1] += 1;
+    for (int64_t j = 0; j < N; ++j) srow_ptr[j + 1] += srow_ptr[j];
+    int64_t* cursor = (int64_t*)malloc(sizeof(int64_t) * (N > 0 ? N : 1));
+    for (int64_t j = 0; j < N; ++j) cursor[j] = srow_ptr[j];
+    for (int64_t i = 0; i < N; ++i)
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+            int64_t k = cursor[src[e]]++;
+            perm[k] = e;
+            sdst[k] = i;
+        }
+    free(cursor);
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
