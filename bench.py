@@ -1,0 +1,221 @@
+"""Throughput of the CGTP convolution on one MI355X.
+
+One step = one pass of the whole hot path over one synthetic layer: real
+spherical harmonics of the edge vectors, graph preparation (sender-sorted
+view), forward convolution and backward convolution (grad_x, grad_W, grad_Y).
+The plan (paths and CG tables) is built once before timing.  Inputs are
+resident in HBM before the timed region.  Prints one JSON line on stdout;
+diagnostics go to stderr.
+
+Default workload: 2000 atoms at 0.1 atoms/A^3 with a 5 A cutoff (about 106k
+directed edges), features, SH and outputs l = 0..2, C = 128, uvu weights.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["clebsch_gordan_tensor_cgtp_amd/csrc/cgtp_kernels.h",
+                  "clebsch_gordan_tensor_cgtp_amd/csrc/cgtp_math.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(N, E, P, C, d_in, d_sh, d_out):
+    """Bytes the method must move (each node row once; per-edge tensors once)."""
+    fwd = E * (4 * P * C + 4 * d_sh + 4) + N * (4 * C * (d_in + d_out) + 4)
+    bwd = E * (8 * P * C + 8 * d_sh + 8) + N * (4 * C * (2 * d_in + d_out) + 4)
+    sh = E * (12 + 4 * d_sh)
+    prep = E * 4 * 6 + N * 4 * 4
+    return {"fwd": fwd, "bwd": bwd, "sh": sh, "prep": prep}
+
+
+def read_traffic(kernel: str, workload: str):
+    """Measured HBM bytes per launch from a committed PMC summary, or None if
+    absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for ln in open(path):
+        if "=" in ln and not ln.startswith("#"):
+            k, v = ln.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_inputs(torch, dev, key, seed=0):
+    import numpy as np
+    from clebsch_gordan_tensor_cgtp_amd import synth
+
+    w = synth.WORKLOADS[key]
+    g = synth.make_graph(w, seed)
+    N, E, L, C = g.n_nodes, g.n_edges, w.l_max, w.channels
+    if E * w.num_paths * C <= 400_000_000:
+        x, W, G = (torch.from_numpy(a).to(dev) for a in synth.make_tensors_numpy(N, E, L, C, seed))
+    else:
+        x, W, G = synth.make_tensors_torch(N, E, L, C, dev, seed)
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    return w, g, T(g.row_ptr), T(g.src), T(g.r), x, W, G
+
+
+def cpu_baseline(w, g, x, W, G):
+    """The fp64 oracle on one full step of the same workload (host cores)."""
+    import numpy as np
+
+    import oracle
+
+    L = w.l_max
+    xh, Wh, Gh = (t.cpu().numpy() for t in (x, W, G))
+    t0 = time.perf_counter()
+    Y = oracle.sh(L, g.r)
+    oracle.graph_transpose(g.row_ptr, g.src)
+    Yf = Y.astype(np.float32)
+    oracle.conv_fwd(L, L, L, g.row_ptr, g.src, xh, Yf, Wh)
+    oracle.conv_bwd(L, L, L, g.row_ptr, g.src, xh, Yf, Wh, Gh)
+    dt = time.perf_counter() - t0
+    return {"value": g.n_edges / dt, "unit": "edges/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"one full step (SH, transpose, fwd, bwd) of the {w.key} workload, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy kernel (PMC byte calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU sharding is "
+              "not built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = (1 << 30) // 4
+        a = torch.randn(n, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 launches of neg(), {4 * n} bytes read and {4 * n} written per launch")
+        return
+
+    from clebsch_gordan_tensor_cgtp_amd.ops import Plan
+
+    w, g, rp, src, r, x, W, G = make_inputs(torch, dev, args.workload)
+    N, E, L, C = g.n_nodes, g.n_edges, w.l_max, w.channels
+    plan = Plan(L, L, L, C)
+    P = plan.num_paths
+    Y = torch.empty((E, plan.dim_sh), device=dev)
+    out = torch.empty((N, plan.dim_out, C), device=dev)
+    dx = torch.empty((N, plan.dim_in, C), device=dev)
+    dW = torch.empty((E, P, C), device=dev)
+    dY = torch.empty((E, plan.dim_sh), device=dev)
+    ws = torch.empty(plan.workspace_size(N, E), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        plan.sh(r, Y)
+        plan.graph_prepare(rp, src, ws)
+        if ev:
+            ev[0].record(stream)
+        plan.conv_fwd(rp, src, x, Y, W, ws, out=out)
+        if ev:
+            ev[1].record(stream)
+        plan.conv_bwd(rp, src, x, Y, W, G, ws, grad_x=dx, grad_W=dW, grad_Y=dY)
+        if ev:
+            ev[2].record(stream)
+
+    log(f"workload {w.key}: N={N} E={E} L={L} C={C} P={P}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = max(ms_total, wall * 1e3) / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+
+    ab = algorithmic_bytes(N, E, P, C, plan.dim_in, plan.dim_sh, plan.dim_out)
+    step_bytes = sum(ab.values())
+    kern, kms, kbytes = ("conv_bwd", bwd_ms, ab["bwd"]) if bwd_ms >= fwd_ms else ("conv_fwd", fwd_ms, ab["fwd"])
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    traffic = read_traffic(kern, w.key)
+    log(f"step {ms_step:.3f} ms | fwd {fwd_ms:.3f} ms ({ab['fwd'] / fwd_ms / 1e6:.0f} GB/s alg) | "
+        f"bwd {bwd_ms:.3f} ms ({ab['bwd'] / bwd_ms / 1e6:.0f} GB/s alg)")
+
+    res = {
+        "metric": "CGTP conv fwd+bwd edges/sec and achieved HBM GB/s (% peak), L=2 C=128 fp32",
+        "value": E / (ms_step * 1e-3),
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "n_atoms": N, "n_edges": E, "l_max": L, "channels": C, "paths": P,
+            "storage": "f32", "step": "sh + graph_prepare + conv_fwd + conv_bwd(dx, dW, dY)",
+            "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+            "fwd_bwd_edges_per_s": E / ((fwd_ms + bwd_ms) * 1e-3),
+            "step_alg_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
+            "fwd_bwd_alg_gbs": (ab["fwd"] + ab["bwd"]) / ((fwd_ms + bwd_ms) * 1e-3) / 1e9,
+            "fwd_bwd_hbm_frac": (ab["fwd"] + ab["bwd"]) / ((fwd_ms + bwd_ms) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        },
+        "roofline": {
+            "kernel": kern, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+            "alg_bytes_per_launch": kbytes, "avg_launch_ms": kms,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(w, g, x, W, G)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
