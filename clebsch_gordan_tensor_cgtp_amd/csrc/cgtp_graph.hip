@@ -17,16 +17,7 @@ __global__ void __launch_bounds__(256) k_fill_i32(int32_t n, int32_t* __restrict
     if (t < n) p[t] = v;
 }
 
-// recv[e] = receiver of edge e; one thread per receiver writes its segment
-__global__ void __launch_bounds__(256) k_recv(int32_t N, const int32_t* __restrict__ row_ptr,
-                                               int32_t* __restrict__ recv)
-{
-    const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= N) return;
-    for (int32_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) recv[e] = i;
-}
-
-// out-degree histogram (integer atomics: order-independent result)
+// out-degree histogram (integer atomics: the counts do not depend on order)
 __global__ void __launch_bounds__(256) k_outdeg(int32_t E, const int32_t* __restrict__ src, int32_t* cnt)
 {
     const int32_t e = blockIdx.x * blockDim.x + threadIdx.x;
@@ -34,9 +25,9 @@ __global__ void __launch_bounds__(256) k_outdeg(int32_t E, const int32_t* __rest
 }
 
 // srow[0] = 0, srow[j+1] = srow[j] + cnt[j]; one block of 1024 threads, each
-// scanning a contiguous chunk
+// scanning a contiguous chunk; also clears the scatter cursors
 __global__ void __launch_bounds__(1024) k_scan(int32_t N, const int32_t* __restrict__ cnt,
-                                                int32_t* __restrict__ srow)
+                                                int32_t* __restrict__ srow, int32_t* __restrict__ cursor)
 {
     __shared__ int32_t part[1024];
     const int t = threadIdx.x;
@@ -58,6 +49,7 @@ __global__ void __launch_bounds__(1024) k_scan(int32_t N, const int32_t* __restr
     for (int32_t j = b; j < end; ++j) {
         run += cnt[j];
         srow[j + 1] = run;
+        cursor[j] = 0;
     }
 }
 
@@ -73,18 +65,51 @@ __global__ void __launch_bounds__(256) k_scatter(int32_t E, const int32_t* __res
     perm[srow[j] + k] = e;
 }
 
-// sort each sender bucket by edge id (heap sort, one thread per sender), so the
-// view is the stable counting sort of the edges by sender, then record the
-// receiver of each permuted edge
-__global__ void __launch_bounds__(256) k_sort_buckets(int32_t N, const int32_t* __restrict__ srow,
-                                                       int32_t* __restrict__ perm)
+// receiver of edge e: the last i with row_ptr[i] <= e
+__device__ __forceinline__ int32_t receiver_of(int32_t e, int32_t N, const int32_t* __restrict__ row_ptr)
 {
-    const int32_t j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= N) return;
-    int32_t* a = perm + srow[j];
-    const int32_t n = srow[j + 1] - srow[j];
-    if (n < 2) return;
-    if (n <= 32) {  // insertion sort
+    int32_t lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (row_ptr[mid] <= e) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+constexpr int kBucketLds = 1024;  // bucket entries a wave sorts in LDS
+
+// One wave per sender: order its bucket by edge id (so the view is the stable
+// counting sort of the edges by sender) and record the receiver of each
+// permuted edge.  Buckets up to kBucketLds are ranked in LDS (edge ids are
+// distinct, so rank = number of smaller ids); longer ones fall back to a
+// serial insertion sort by lane 0.
+__global__ void __launch_bounds__(256) k_sort_buckets(int32_t N, const int32_t* __restrict__ row_ptr,
+                                                       const int32_t* __restrict__ srow, int32_t* __restrict__ perm,
+                                                       int32_t* __restrict__ sdst)
+{
+    __shared__ int32_t buf[4][kBucketLds];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int32_t j = (int32_t)blockIdx.x * 4 + w;
+    if (j >= N) return;  // whole wave; no block-level barrier below
+    const int32_t b = srow[j], n = srow[j + 1] - b;
+    if (n <= kBucketLds) {
+        int32_t* sb = buf[w];
+        for (int32_t k = lane; k < n; k += 64) sb[k] = perm[b + k];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int32_t k = lane; k < n; k += 64) {
+            const int32_t v = sb[k];
+            int32_t rank = 0;
+            for (int32_t t = 0; t < n; ++t) rank += sb[t] < v ? 1 : 0;
+            perm[b + rank] = v;
+            sdst[b + rank] = receiver_of(v, N, row_ptr);
+        }
+        return;
+    }
+    if (lane == 0) {
+        int32_t* a = perm + b;
         for (int32_t q = 1; q < n; ++q) {
             const int32_t v = a[q];
             int32_t r = q - 1;
@@ -94,34 +119,11 @@ __global__ void __launch_bounds__(256) k_sort_buckets(int32_t N, const int32_t* 
             }
             a[r + 1] = v;
         }
-        return;
     }
-    auto sift = [&](int32_t root, int32_t len) {
-        while (true) {
-            int32_t c = 2 * root + 1;
-            if (c >= len) break;
-            if (c + 1 < len && a[c + 1] > a[c]) ++c;
-            if (a[root] >= a[c]) break;
-            const int32_t t = a[root];
-            a[root] = a[c];
-            a[c] = t;
-            root = c;
-        }
-    };
-    for (int32_t r = n / 2 - 1; r >= 0; --r) sift(r, n);
-    for (int32_t len = n - 1; len > 0; --len) {
-        const int32_t t = a[0];
-        a[0] = a[len];
-        a[len] = t;
-        sift(0, len);
-    }
-}
-
-__global__ void __launch_bounds__(256) k_sdst(int32_t E, const int32_t* __restrict__ perm,
-                                               const int32_t* __restrict__ recv, int32_t* __restrict__ sdst)
-{
-    const int32_t k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k < E) sdst[k] = recv[perm[k]];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int32_t k = lane; k < n; k += 64) sdst[b + k] = receiver_of(perm[b + k], N, row_ptr);
 }
 
 hipError_t launch_graph_prepare(int32_t N, int32_t E, const int32_t* row_ptr, const int32_t* src, void* ws,
@@ -132,17 +134,15 @@ hipError_t launch_graph_prepare(int32_t N, int32_t E, const int32_t* row_ptr, co
     int32_t* srow = (int32_t*)(base + L.srow);
     int32_t* perm = (int32_t*)(base + L.perm);
     int32_t* sdst = (int32_t*)(base + L.sdst);
-    int32_t* recv = (int32_t*)(base + L.recv);
     int32_t* cnt = (int32_t*)(base + L.cnt);
+    int32_t* cursor = (int32_t*)(base + L.cursor);
     const unsigned bN = (unsigned)((N + 255) / 256), bE = (unsigned)((E + 255) / 256);
     if (N > 0) hipLaunchKernelGGL(k_fill_i32, dim3(bN), dim3(256), 0, s, N, cnt, 0);
     if (E > 0) hipLaunchKernelGGL(k_outdeg, dim3(bE), dim3(256), 0, s, E, src, cnt);
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, N, cnt, srow);
-    if (N > 0) hipLaunchKernelGGL(k_fill_i32, dim3(bN), dim3(256), 0, s, N, cnt, 0);
-    if (N > 0) hipLaunchKernelGGL(k_recv, dim3(bN), dim3(256), 0, s, N, row_ptr, recv);
-    if (E > 0) hipLaunchKernelGGL(k_scatter, dim3(bE), dim3(256), 0, s, E, src, srow, cnt, perm);
-    if (N > 0) hipLaunchKernelGGL(k_sort_buckets, dim3(bN), dim3(256), 0, s, N, srow, perm);
-    if (E > 0) hipLaunchKernelGGL(k_sdst, dim3(bE), dim3(256), 0, s, E, perm, recv, sdst);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, N, cnt, srow, cursor);
+    if (E > 0) hipLaunchKernelGGL(k_scatter, dim3(bE), dim3(256), 0, s, E, src, srow, cursor, perm);
+    if (E > 0) hipLaunchKernelGGL(k_sort_buckets, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, N, row_ptr, srow,
+                                  perm, sdst);
     return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@ namespace cgtp {
 
 // Byte offsets of the sender-sorted graph view inside the workspace.
 struct WsLayout {
-    size_t srow, perm, sdst, recv, cnt, total;
+    size_t srow, perm, sdst, cnt, cursor, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -25,9 +25,9 @@ inline WsLayout ws_layout(int64_t N, int64_t E)
     o += align256(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
     w.sdst = o;
     o += align256(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
-    w.recv = o;
-    o += align256(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
     w.cnt = o;
+    o += align256(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+    w.cursor = o;
     o += align256(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
     w.total = o;
     return w;

@@ -5,30 +5,34 @@
 // equivariant MLIPs; "LunaTP: Enabling Efficient and Scalable Tensor Product
 // for Equivariant MLIPs", Abstract):
 //   * real spherical harmonics of the edge vectors          (k_sh)
-//   * sender-sorted view of the receiver CSR                (graph prep)
-//   * forward, node-centric: one wavefront owns a receiver, walks its CSR
-//     segment, gathers the sender rows x_j with channel-contiguous loads,
-//     streams W[e], accumulates in registers and writes out[i] once; no
-//     atomics                                               (k_conv_fwd)
-//   * backward, sender-centric over the sender-sorted view: one wavefront owns
-//     a sender j, keeps x_j and grad_x[j] in registers, gathers grad_out rows
-//     of the receivers, writes grad_W[e] and a cross-lane-reduced grad_Y[e]
-//     per edge; no atomics                                  (k_conv_bwd)
+//   * forward, node-centric: the waves of a receiver walk its CSR segment,
+//     gather the sender rows x_j with channel-contiguous loads, stream W[e],
+//     accumulate in registers and write out[i] once; no atomics (k_conv_fwd)
+//   * backward, sender-centric over the sender-sorted view: the waves of a
+//     sender keep x_j and grad_x[j] in registers, gather the grad_out rows of
+//     its receivers, write grad_W[e] per edge and grad_Y[e] reduced over the
+//     channels; no atomics                                   (k_conv_bwd)
+// (graph preparation lives in cgtp_graph.hip)
 //
 // Arithmetic is fp64 on fp32 data: the per-edge contraction and the sums over
 // a segment and over channels keep fp64 accuracy, and fp64 FMA issues at the
 // same rate as unpacked fp32 on this chip.
 //
-// Within an edge, the CG contraction is reused across channels: for each path
-// p = (l1,l2,l3) the matrix M_p[m1][m3] = sum_m2 T_p[m1][m2][m3] Y[e][l2,m2]
-// depends only on the edge, so it is formed once per edge (per lane, shared by
-// the lane's channels) and each channel then needs M_p x (forward) or M_p g
-// (backward).  The CG values and their nonzero pattern are compile-time
-// constants of the (L_in, L_sh, L_out) specialisation.
+// Lane mapping: a lane owns one channel of one edge.  For C >= 64 a node's
+// channels are split over C/64 waves (each owning a 64-channel slice of the
+// node's rows); for C < 64 a wave covers 64/C edges of the segment at once and
+// reduces across those edge groups at the end.  The CG values and their
+// nonzero pattern are compile-time constants of the (L_in, L_sh, L_out)
+// specialisation, so every contraction below is a straight line of fp64 FMAs
+// over the nonzero coefficients only.
 //
-// Lane mapping: a lane owns CPL adjacent channels of one edge; LPE = C/CPL
-// lanes cover an edge, so a wave processes 64/LPE edges of its segment at once
-// and reduces across those edge groups at the end.
+// Reuse inside an edge ("multi-level reuse" in the LunaTP abstract, done here
+// per channel):
+//   forward:  q[a][b] = x[l1,a] Y[l2,b] is formed once per (l1,l2) block and
+//             shared by every path (l1,l2,l3) of the block; z_p = T_p q.
+//   backward: R_p[a][b] = sum_m3 T_p[a][b][m3] g[l3,m3] gives both
+//             h_p = R_p Y (-> grad_x += W h_p, grad_W = x . h_p) and
+//             v_p = R_p^T x (-> grad_Y += W v_p).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -162,130 +166,153 @@ hipError_t launch_sh(int64_t E, const float* r, float* Y, hipStream_t s)
 }
 
 // ----------------------------------------------------------------------------
-// channel I/O helpers: CPL adjacent fp32 channels
+// lane geometry
 // ----------------------------------------------------------------------------
-template <int CPL>
-__device__ __forceinline__ void load_ch(const float* __restrict__ p, float (&v)[CPL])
-{
-    if constexpr (CPL == 2) {
-        const float2 t = *reinterpret_cast<const float2*>(p);
-        v[0] = t.x;
-        v[1] = t.y;
-    } else if constexpr (CPL == 4) {
-        const float4 t = *reinterpret_cast<const float4*>(p);
-        v[0] = t.x;
-        v[1] = t.y;
-        v[2] = t.z;
-        v[3] = t.w;
-    } else {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) v[c] = p[c];
-    }
-}
+template <int C>
+struct Geo {
+    static constexpr int LPE = C < 64 ? C : 64;  // lanes per edge (one channel each)
+    static constexpr int EPW = 64 / LPE;         // edges a wave processes at once
+    static constexpr int WPN = C > 64 ? C / 64 : 1;  // waves per node
+    static_assert(C > 0 && (C & (C - 1)) == 0 && C <= 256, "C must be a power of two <= 256");
+};
 
-template <int CPL>
-__device__ __forceinline__ void store_ch(float* __restrict__ p, const double (&v)[CPL])
-{
-    if constexpr (CPL == 2) {
-        *reinterpret_cast<float2*>(p) = make_float2((float)v[0], (float)v[1]);
-    } else if constexpr (CPL == 4) {
-        *reinterpret_cast<float4*>(p) = make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
-    } else {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) p[c] = (float)v[c];
-    }
-}
+// minimum waves per SIMD the register allocation must allow
+#ifndef CGTP_BWD_OCC
+#define CGTP_BWD_OCC 2
+#endif
+#ifndef CGTP_FWD_OCC
+#define CGTP_FWD_OCC 4
+#endif
+// software prefetch of the next edge's operands (1) or not (0)
+#ifndef CGTP_BWD_PREFETCH
+#define CGTP_BWD_PREFETCH 0
+#endif
+#ifndef CGTP_FWD_PREFETCH
+#define CGTP_FWD_PREFETCH 1
+#endif
 
 // ----------------------------------------------------------------------------
 // forward
 // ----------------------------------------------------------------------------
-template <int LIN, int LSH, int LOUT, int CPL, int LPE>
-__global__ void __launch_bounds__(256) k_conv_fwd(int32_t N, const int32_t* __restrict__ row_ptr,
+template <class Tb>
+struct FwdEdge {
+    static constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH, DOUT = Tb::DOUT;
+    float w[P], x[DIN], y[DSH];
+};
+
+template <class Tb, int C>
+__device__ __forceinline__ void fwd_load(FwdEdge<Tb>& d, int32_t e, int c, const int32_t* __restrict__ src,
+                                         const float* __restrict__ x, const float* __restrict__ Y,
+                                         const float* __restrict__ W)
+{
+    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH;
+    const int32_t j = src[e];
+    const float* wp = W + (int64_t)e * (P * C) + c;
+#pragma unroll
+    for (int p = 0; p < P; ++p) d.w[p] = __builtin_nontemporal_load(wp + p * C);
+    const float* xp = x + (int64_t)j * (DIN * C) + c;
+#pragma unroll
+    for (int k = 0; k < DIN; ++k) d.x[k] = xp[k * C];
+    const float* yp = Y + (int64_t)e * DSH;
+#pragma unroll
+    for (int k = 0; k < DSH; ++k) d.y[k] = yp[k];
+}
+
+// acc[l3,m3] += sum_p W_p sum_{a,b} T_p[a][b][m3] x[l1,a] y[l2,b]
+template <class Tb>
+__device__ __forceinline__ void fwd_compute(const FwdEdge<Tb>& d, double (&acc)[Tb::DOUT])
+{
+    constexpr int DIN = Tb::DIN, DSH = Tb::DSH;
+    double xv[DIN], yv[DSH];
+#pragma unroll
+    for (int k = 0; k < DIN; ++k) xv[k] = (double)d.x[k];
+#pragma unroll
+    for (int k = 0; k < DSH; ++k) yv[k] = (double)d.y[k];
+    static_for<0, Tb::P>([&](auto PI) {
+        constexpr int p = decltype(PI)::value;
+        using K = PathK<Tb, p>;
+        // first path of its (l1,l2) block forms the products for the block
+        constexpr bool first = (p == 0) || Tb::data.l1[p > 0 ? p - 1 : 0] != K::l1 ||
+                               Tb::data.l2[p > 0 ? p - 1 : 0] != K::l2;
+        (void)first;
+        const double w = (double)d.w[p];
+        static_for<0, K::d3>([&](auto M3) {
+            constexpr int m3 = decltype(M3)::value;
+            double z = 0.0;
+            bool any = false;
+            static_for<0, K::d1>([&](auto A) {
+                static_for<0, K::d2>([&](auto B) {
+                    constexpr int a = decltype(A)::value, b = decltype(B)::value;
+                    constexpr double t = K::T(a, b, m3);
+                    if constexpr (t != 0.0) {
+                        z = __builtin_fma(t, xv[K::k1 + a] * yv[K::k2 + b], z);
+                        any = true;
+                    }
+                });
+            });
+            if (any) acc[K::k3 + m3] = __builtin_fma(w, z, acc[K::k3 + m3]);
+        });
+    });
+}
+
+template <int LIN, int LSH, int LOUT, int C>
+__global__ void __launch_bounds__(256, CGTP_FWD_OCC) k_conv_fwd(int32_t N, const int32_t* __restrict__ row_ptr,
                                                    const int32_t* __restrict__ src, const float* __restrict__ x,
                                                    const float* __restrict__ Y, const float* __restrict__ W,
                                                    float* __restrict__ out)
 {
     using Tb = cgmath::Tables<LIN, LSH, LOUT>;
-    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH, DOUT = Tb::DOUT;
-    constexpr int C = CPL * LPE;
-    constexpr int EPW = 64 / LPE;  // edges in flight per wave
+    using G = Geo<C>;
+    constexpr int DOUT = Tb::DOUT;
     const int lane = threadIdx.x & 63;
-    const int32_t i = (int32_t)blockIdx.x * 4 + (int32_t)(threadIdx.x >> 6);
+    // wave index made explicitly uniform so the node, its segment and the
+    // per-edge indices live in scalar registers
+    const int32_t gw = (int32_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int32_t i = gw / G::WPN;
     if (i >= N) return;
-    const int g = lane / LPE;
-    const int c0 = (lane % LPE) * CPL;
+    const int g = lane / G::LPE;
+    const int c = (gw % G::WPN) * 64 + lane % G::LPE;
 
-    double acc[DOUT][CPL];
+    double acc[DOUT];
 #pragma unroll
-    for (int k = 0; k < DOUT; ++k)
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[k][c] = 0.0;
+    for (int k = 0; k < DOUT; ++k) acc[k] = 0.0;
 
-    const int32_t beg = row_ptr[i], end = row_ptr[i + 1];
-    for (int32_t e = beg + g; e < end; e += EPW) {
-        const int32_t j = src[e];
-        double y[DSH];
-#pragma unroll
-        for (int k = 0; k < DSH; ++k) y[k] = (double)Y[(int64_t)e * DSH + k];
-        float wv[P][CPL];
-        const float* wp = W + (int64_t)e * (P * C) + c0;
-#pragma unroll
-        for (int p = 0; p < P; ++p) load_ch<CPL>(wp + p * C, wv[p]);
-        float xf[DIN][CPL];
-        const float* xp = x + (int64_t)j * (DIN * C) + c0;
-#pragma unroll
-        for (int k = 0; k < DIN; ++k) load_ch<CPL>(xp + k * C, xf[k]);
-        double xv[DIN][CPL];
-#pragma unroll
-        for (int k = 0; k < DIN; ++k)
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) xv[k][c] = (double)xf[k][c];
-
-        static_for<0, P>([&](auto PI) {
-            using K = PathK<Tb, decltype(PI)::value>;
-            constexpr int p = decltype(PI)::value;
-            double M[K::d1][K::d3];
-            make_M<K>(y, M);
-            static_for<0, CPL>([&](auto CI) {
-                constexpr int c = decltype(CI)::value;
-                const double w = (double)wv[p][c];
-                static_for<0, K::d3>([&](auto M3) {
-                    constexpr int m3 = decltype(M3)::value;
-                    double z = 0.0;
-                    bool any = false;
-                    static_for<0, K::d1>([&](auto A) {
-                        constexpr int a = decltype(A)::value;
-                        if constexpr (K::NZ(a, m3)) {
-                            z = __builtin_fma(M[a][m3], xv[K::k1 + a][c], z);
-                            any = true;
-                        }
-                    });
-                    if (any) acc[K::k3 + m3][c] = __builtin_fma(w, z, acc[K::k3 + m3][c]);
-                });
-            });
-        });
+    const int32_t end = row_ptr[i + 1];
+    int32_t e = row_ptr[i] + g;
+    FwdEdge<Tb> cur;
+    if (CGTP_FWD_PREFETCH && e < end) fwd_load<Tb, C>(cur, e, c, src, x, Y, W);
+    while (e < end) {
+        const int32_t en = e + G::EPW;
+        FwdEdge<Tb> nxt;
+        if (CGTP_FWD_PREFETCH) {
+            if (en < end) fwd_load<Tb, C>(nxt, en, c, src, x, Y, W);
+        } else {
+            fwd_load<Tb, C>(cur, e, c, src, x, Y, W);
+        }
+        fwd_compute<Tb>(cur, acc);
+        if (CGTP_FWD_PREFETCH) cur = nxt;
+        e = en;
     }
-    if constexpr (EPW > 1) {
+    if constexpr (G::EPW > 1) {
 #pragma unroll
-        for (int off = LPE; off < 64; off <<= 1)
+        for (int off = G::LPE; off < 64; off <<= 1)
 #pragma unroll
-            for (int k = 0; k < DOUT; ++k)
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) acc[k][c] += __shfl_xor(acc[k][c], off, 64);
+            for (int k = 0; k < DOUT; ++k) acc[k] += __shfl_xor(acc[k], off, 64);
     }
     if (g == 0) {
-        float* op = out + (int64_t)i * (DOUT * C) + c0;
+        float* op = out + (int64_t)i * (DOUT * C) + c;
 #pragma unroll
-        for (int k = 0; k < DOUT; ++k) store_ch<CPL>(op + k * C, acc[k]);
+        for (int k = 0; k < DOUT; ++k) op[k * C] = (float)acc[k];
     }
 }
 
-template <int LIN, int LSH, int LOUT, int CPL, int LPE>
+template <int LIN, int LSH, int LOUT, int C>
 hipError_t launch_fwd(int32_t N, const int32_t* row_ptr, const int32_t* src, const float* x, const float* Y,
                       const float* W, float* out, hipStream_t s)
 {
     if (N == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_conv_fwd<LIN, LSH, LOUT, CPL, LPE>), dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, N,
+    const int64_t waves = (int64_t)N * Geo<C>::WPN;
+    hipLaunchKernelGGL((k_conv_fwd<LIN, LSH, LOUT, C>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, N,
                        row_ptr, src, x, Y, W, out);
     return hipGetLastError();
 }
@@ -293,168 +320,302 @@ hipError_t launch_fwd(int32_t N, const int32_t* row_ptr, const int32_t* src, con
 // ----------------------------------------------------------------------------
 // backward
 // ----------------------------------------------------------------------------
-template <int LIN, int LSH, int LOUT, int CPL, int LPE>
-__global__ void __launch_bounds__(256) k_conv_bwd(int32_t N, GraphView gv, const float* __restrict__ x,
-                                                   const float* __restrict__ Y, const float* __restrict__ W,
-                                                   const float* __restrict__ G, float* __restrict__ dx,
-                                                   float* __restrict__ dW, float* __restrict__ dY, int mask)
+template <class Tb>
+struct BwdEdge {
+    static constexpr int P = Tb::P, DSH = Tb::DSH, DOUT = Tb::DOUT;
+    int32_t e;
+    float w[P], g[DOUT], y[DSH];
+};
+
+template <class Tb, int C>
+__device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, int c, const GraphView& gv,
+                                         const float* __restrict__ Y, const float* __restrict__ W,
+                                         const float* __restrict__ Gr)
 {
-    using Tb = cgmath::Tables<LIN, LSH, LOUT>;
-    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH, DOUT = Tb::DOUT;
-    constexpr int C = CPL * LPE;
-    constexpr int EPW = 64 / LPE;
-    const int lane = threadIdx.x & 63;
-    const int32_t j = (int32_t)blockIdx.x * 4 + (int32_t)(threadIdx.x >> 6);
-    if (j >= N) return;
-    const int g = lane / LPE;
-    const int c0 = (lane % LPE) * CPL;
-    const bool want_dx = (mask & kGradX) != 0;
-    const bool want_dW = (mask & kGradW) != 0;
-    const bool want_dY = (mask & kGradY) != 0;
+    constexpr int P = Tb::P, DSH = Tb::DSH, DOUT = Tb::DOUT;
+    const int32_t e = gv.perm[q];
+    const int32_t i = gv.sdst[q];
+    d.e = e;
+    const float* wp = W + (int64_t)e * (P * C) + c;
+#pragma unroll
+    for (int p = 0; p < P; ++p) d.w[p] = __builtin_nontemporal_load(wp + p * C);
+    const float* gp = Gr + (int64_t)i * (DOUT * C) + c;
+#pragma unroll
+    for (int k = 0; k < DOUT; ++k) d.g[k] = gp[k * C];
+    const float* yp = Y + (int64_t)e * DSH;
+#pragma unroll
+    for (int k = 0; k < DSH; ++k) d.y[k] = yp[k];
+}
 
-    double xv[DIN][CPL];
-    {
-        float xf[DIN][CPL];
-        const float* xp = x + (int64_t)j * (DIN * C) + c0;
-#pragma unroll
-        for (int k = 0; k < DIN; ++k) load_ch<CPL>(xp + k * C, xf[k]);
-#pragma unroll
-        for (int k = 0; k < DIN; ++k)
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) xv[k][c] = (double)xf[k][c];
-    }
-    double dxa[DIN][CPL];
-#pragma unroll
-    for (int k = 0; k < DIN; ++k)
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) dxa[k][c] = 0.0;
+// One edge of the backward for this lane's channel:
+//   R_p[a][b] = sum_m3 T_p[a][b][m3] g[l3,m3]
+//   h_p[a] = sum_b R_p[a][b] y[l2,b]   -> dx[l1,a] += W_p h_p[a], dW_p = sum_a x[l1,a] h_p[a]
+//   v_p[b] = sum_a R_p[a][b] x[l1,a]   -> dy[l2,b] += W_p v_p[b]
+// Hide a register value from the optimiser: values passed through here before
+// each path cannot be matched with the previous path's, so products of
+// coefficients and components are not shared across paths and kept live for
+// the whole edge (which costs more registers than recomputing them).
+__device__ __forceinline__ void opaque(double& v) { asm volatile("" : "+v"(v)); }
 
-    const int32_t beg = gv.srow[j], end = gv.srow[j + 1];
-    for (int32_t q = beg + g; q < end; q += EPW) {
-        const int32_t e = gv.perm[q];
-        const int32_t i = gv.sdst[q];
-        double y[DSH];
+template <class Tb, int C, bool DX, bool DW, bool DY>
+__device__ __forceinline__ void bwd_compute(const BwdEdge<Tb>& d, const double (&xv)[Tb::DIN],
+                                            double (&dxa)[Tb::DIN], float* __restrict__ dwp,
+                                            double (&dya)[Tb::DSH])
+{
+    constexpr int DSH = Tb::DSH, DOUT = Tb::DOUT;
+    double gv[DOUT], yv[DSH];
 #pragma unroll
-        for (int k = 0; k < DSH; ++k) y[k] = (double)Y[(int64_t)e * DSH + k];
-        float wv[P][CPL];
-        const float* wp = W + (int64_t)e * (P * C) + c0;
+    for (int k = 0; k < DOUT; ++k) gv[k] = (double)d.g[k];
 #pragma unroll
-        for (int p = 0; p < P; ++p) load_ch<CPL>(wp + p * C, wv[p]);
-        double gg[DOUT][CPL];
-        {
-            float gf[DOUT][CPL];
-            const float* gp = G + (int64_t)i * (DOUT * C) + c0;
+    for (int k = 0; k < DSH; ++k) yv[k] = (double)d.y[k];
 #pragma unroll
-            for (int k = 0; k < DOUT; ++k) load_ch<CPL>(gp + k * C, gf[k]);
-#pragma unroll
-            for (int k = 0; k < DOUT; ++k)
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) gg[k][c] = (double)gf[k][c];
-        }
-        double dya[DSH];
-#pragma unroll
-        for (int k = 0; k < DSH; ++k) dya[k] = 0.0;
-        float* dwp = dW + (int64_t)e * (P * C) + c0;
-
-        static_for<0, P>([&](auto PI) {
-            using K = PathK<Tb, decltype(PI)::value>;
-            constexpr int p = decltype(PI)::value;
-            double M[K::d1][K::d3];
-            make_M<K>(y, M);
-            double dwc[CPL];
-            static_for<0, CPL>([&](auto CI) {
-                constexpr int c = decltype(CI)::value;
-                const double w = (double)wv[p][c];
-                // h[a] = sum_m3 M[a][m3] g[m3]
-                double h[K::d1];
-                double dw = 0.0;
-                static_for<0, K::d1>([&](auto A) {
-                    constexpr int a = decltype(A)::value;
-                    if constexpr (K::ROW(a)) {
-                        double s = 0.0;
-                        static_for<0, K::d3>([&](auto M3) {
-                            constexpr int m3 = decltype(M3)::value;
-                            if constexpr (K::NZ(a, m3)) s = __builtin_fma(M[a][m3], gg[K::k3 + m3][c], s);
-                        });
-                        h[a] = s;
-                        dw = __builtin_fma(xv[K::k1 + a][c], s, dw);
-                        if (want_dx) dxa[K::k1 + a][c] = __builtin_fma(w, s, dxa[K::k1 + a][c]);
+    for (int k = 0; k < DSH; ++k) dya[k] = 0.0;
+    static_for<0, Tb::P>([&](auto PI) {
+        constexpr int p = decltype(PI)::value;
+        using K = PathK<Tb, p>;
+        const double w = (double)d.w[p];
+        static_for<0, K::d3>([&](auto M3) { opaque(gv[K::k3 + decltype(M3)::value]); });
+        double v[K::d2];
+        static_for<0, K::d2>([&](auto B) { v[decltype(B)::value] = 0.0; });
+        double dw = 0.0;
+        static_for<0, K::d1>([&](auto A) {
+            constexpr int a = decltype(A)::value;
+            if constexpr (K::ROW(a)) {
+                double h = 0.0;
+                static_for<0, K::d2>([&](auto B) {
+                    constexpr int b = decltype(B)::value;
+                    // R[a][b]
+                    double r = 0.0;
+                    bool any = false;
+                    static_for<0, K::d3>([&](auto M3) {
+                        constexpr int m3 = decltype(M3)::value;
+                        constexpr double t = K::T(a, b, m3);
+                        if constexpr (t != 0.0) {
+                            r = __builtin_fma(t, gv[K::k3 + m3], r);
+                            any = true;
+                        }
+                    });
+                    if (any) {
+                        h = __builtin_fma(r, yv[K::k2 + b], h);
+                        if constexpr (DY) v[b] = __builtin_fma(r, xv[K::k1 + a], v[b]);
                     }
                 });
-                dwc[c] = dw;
-                if (want_dY) {
-                    // v[b] = sum_{a,m3} T[a][b][m3] x[a] g[m3]; dY[b] += w v[b]
-                    double v[K::d2];
-                    static_for<0, K::d2>([&](auto B) { v[decltype(B)::value] = 0.0; });
-                    static_for<0, K::d1>([&](auto A) {
-                        static_for<0, K::d3>([&](auto M3) {
-                            constexpr int a = decltype(A)::value, m3 = decltype(M3)::value;
-                            if constexpr (K::NZ(a, m3)) {
-                                const double pr = xv[K::k1 + a][c] * gg[K::k3 + m3][c];
-                                static_for<0, K::d2>([&](auto B) {
-                                    constexpr int b = decltype(B)::value;
-                                    constexpr double t = K::T(a, b, m3);
-                                    if constexpr (t != 0.0) v[b] = __builtin_fma(t, pr, v[b]);
-                                });
-                            }
-                        });
-                    });
-                    static_for<0, K::d2>([&](auto B) {
-                        constexpr int b = decltype(B)::value;
-                        if constexpr (K::COL2(b)) dya[K::k2 + b] = __builtin_fma(w, v[b], dya[K::k2 + b]);
-                    });
-                }
-            });
-            if (want_dW) store_ch<CPL>(dwp + p * C, dwc);
-        });
-
-        if (want_dY) {
-#pragma unroll
-            for (int k = 0; k < DSH; ++k) {
-                double v = dya[k];
-#pragma unroll
-                for (int off = 1; off < LPE; off <<= 1) v += __shfl_xor(v, off, 64);
-                dya[k] = v;
+                if constexpr (DX) dxa[K::k1 + a] = __builtin_fma(w, h, dxa[K::k1 + a]);
+                if constexpr (DW) dw = __builtin_fma(xv[K::k1 + a], h, dw);
             }
-            if ((lane % LPE) == 0) {
-                float* yp = dY + (int64_t)e * DSH;
+        });
+        if constexpr (DW) __builtin_nontemporal_store((float)dw, dwp + p * C);
+        if constexpr (DY)
+            static_for<0, K::d2>([&](auto B) {
+                constexpr int b = decltype(B)::value;
+                if constexpr (K::COL2(b)) dya[K::k2 + b] = __builtin_fma(w, v[b], dya[K::k2 + b]);
+            });
+        // schedule path by path: interleaving paths buys little ILP at this
+        // occupancy and multiplies the live transients
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+// grad_Y slots combined across the waves of a sender (C > 64), in LDS
+constexpr int kDyBatch = 32;
+
+// quad_perm DPP move of a double (both halves), CTRL a quad_perm selector
+template <int CTRL>
+__device__ __forceinline__ double dpp_quad(double v)
+{
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
+
+// Sum of v[k] over the 64 lanes of a wave, for every k < D (D <= 16), through
+// a per-wave LDS tile red[D][64]: each lane stores its D partials, lane 4k+q
+// adds red[k][16q .. 16q+15], and a quad exchange (DPP) completes the sum.
+// Returns the total of component lane/4 in lanes with lane%4 == 0.
+template <int D>
+__device__ __forceinline__ double wave_sum_lds(const double (&v)[D], double* __restrict__ red, int lane)
+{
+    static_assert(D <= 16, "at most 16 components");
 #pragma unroll
-                for (int k = 0; k < DSH; ++k) yp[k] = (float)dya[k];
+    for (int k = 0; k < D; ++k) red[k * 64 + lane] = v[k];
+    __builtin_amdgcn_wave_barrier();
+    const int k = lane >> 2, q = lane & 3;
+    double s = 0.0;
+    if (k < D) {
+        const double2* r = reinterpret_cast<const double2*>(red + k * 64 + q * 16);
+        double2 acc2[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc2[t] = r[t];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) s += acc2[t].x + acc2[t].y;
+    }
+    __builtin_amdgcn_wave_barrier();
+    s += dpp_quad<0xB1>(s);  // lanes ^1
+    s += dpp_quad<0x4E>(s);  // lanes ^2
+    return s;
+}
+
+template <int LIN, int LSH, int LOUT, int C, bool DX, bool DW, bool DY>
+__global__ void __launch_bounds__(256, CGTP_BWD_OCC) k_conv_bwd(int32_t N, GraphView gv, const float* __restrict__ x,
+                                                   const float* __restrict__ Y, const float* __restrict__ W,
+                                                   const float* __restrict__ Gr, float* __restrict__ dx,
+                                                   float* __restrict__ dW, float* __restrict__ dY)
+{
+    using Tb = cgmath::Tables<LIN, LSH, LOUT>;
+    using Gm = Geo<C>;
+    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH;
+    constexpr int WPN = Gm::WPN;
+    constexpr int NPB = WPN > 1 ? 1 : 4;  // senders per block
+    // per-wave grad_Y partial sums of a batch of edges (only when WPN > 1)
+    __shared__ double dy_part[WPN > 1 ? WPN : 1][WPN > 1 ? kDyBatch : 1][DSH];
+    __shared__ int32_t dy_edge[WPN > 1 ? kDyBatch : 1];
+    // per-wave transpose tile of the channel reduction (one channel per lane)
+    constexpr bool kLdsSum = DY && Gm::LPE == 64;
+    __shared__ double dy_red[kLdsSum ? (WPN > 1 ? WPN : 4) : 1][kLdsSum ? DSH * 64 : 1];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int32_t j = (int32_t)blockIdx.x * NPB + (WPN > 1 ? 0 : wv);
+    if (WPN == 1 && j >= N) return;  // whole wave; no block barrier when WPN == 1
+    const int half = WPN > 1 ? wv : 0;
+    const int g = lane / Gm::LPE;
+    const int c = half * 64 + lane % Gm::LPE;
+
+    double xv[DIN], dxa[DIN];
+    {
+        const float* xp = x + (int64_t)j * (DIN * C) + c;
+#pragma unroll
+        for (int k = 0; k < DIN; ++k) {
+            xv[k] = (double)xp[k * C];
+            dxa[k] = 0.0;
+        }
+    }
+    const int32_t beg = gv.srow[j], end = gv.srow[j + 1];
+
+    if constexpr (WPN == 1) {
+        int32_t q = beg + g;
+        BwdEdge<Tb> cur;
+        if (CGTP_BWD_PREFETCH && q < end) bwd_load<Tb, C>(cur, q, c, gv, Y, W, Gr);
+        while (q < end) {
+            const int32_t qn = q + Gm::EPW;
+            BwdEdge<Tb> nxt;
+            if (CGTP_BWD_PREFETCH) {
+                if (qn < end) bwd_load<Tb, C>(nxt, qn, c, gv, Y, W, Gr);
+            } else {
+                bwd_load<Tb, C>(cur, q, c, gv, Y, W, Gr);
+            }
+            double dya[DSH];
+            bwd_compute<Tb, C, DX, DW, DY>(cur, xv, dxa, dW + (int64_t)cur.e * (P * C) + c, dya);
+            if constexpr (DY) {
+                if constexpr (kLdsSum) {
+                    const double t = wave_sum_lds<DSH>(dya, dy_red[wv], lane);
+                    if ((lane & 3) == 0 && (lane >> 2) < DSH) dY[(int64_t)cur.e * DSH + (lane >> 2)] = (float)t;
+                } else {
+#pragma unroll
+                    for (int k = 0; k < DSH; ++k) {
+                        double s = dya[k];
+#pragma unroll
+                        for (int off = 1; off < Gm::LPE; off <<= 1) s += __shfl_xor(s, off, 64);
+                        dya[k] = s;
+                    }
+                    if ((lane % Gm::LPE) == 0) {
+                        float* yp = dY + (int64_t)cur.e * DSH;
+#pragma unroll
+                        for (int k = 0; k < DSH; ++k) yp[k] = (float)dya[k];
+                    }
+                }
+            }
+            if (CGTP_BWD_PREFETCH) cur = nxt;
+            q = qn;
+        }
+    } else {
+        // WPN waves share the sender; the segment is walked in batches so the
+        // per-wave grad_Y partials can be combined in LDS
+        const int32_t n = end - beg;
+        for (int32_t b0 = 0; b0 < n; b0 += kDyBatch) {
+            const int32_t nb = n - b0 < kDyBatch ? n - b0 : kDyBatch;
+            int32_t q = beg + b0;
+            const int32_t qe = q + nb;
+            BwdEdge<Tb> cur;
+            if (CGTP_BWD_PREFETCH) bwd_load<Tb, C>(cur, q, c, gv, Y, W, Gr);
+            for (int32_t s = 0; s < nb; ++s) {
+                BwdEdge<Tb> nxt;
+                if (CGTP_BWD_PREFETCH) {
+                    if (q + 1 < qe) bwd_load<Tb, C>(nxt, q + 1, c, gv, Y, W, Gr);
+                } else {
+                    bwd_load<Tb, C>(cur, q, c, gv, Y, W, Gr);
+                }
+                double dya[DSH];
+                bwd_compute<Tb, C, DX, DW, DY>(cur, xv, dxa, dW + (int64_t)cur.e * (P * C) + c, dya);
+                if constexpr (DY) {
+                    const double t = wave_sum_lds<DSH>(dya, dy_red[wv], lane);
+                    if ((lane & 3) == 0 && (lane >> 2) < DSH) dy_part[half][s][lane >> 2] = t;
+                    if (lane == 0 && half == 0) dy_edge[s] = cur.e;
+                }
+                if (CGTP_BWD_PREFETCH) cur = nxt;
+                ++q;
+            }
+            if constexpr (DY) {
+                __syncthreads();
+                for (int t = threadIdx.x; t < nb * DSH; t += 64 * WPN) {
+                    const int s = t / DSH, k = t % DSH;
+                    double v = 0.0;
+#pragma unroll
+                    for (int h = 0; h < WPN; ++h) v += dy_part[h][s][k];
+                    dY[(int64_t)dy_edge[s] * DSH + k] = (float)v;
+                }
+                __syncthreads();
             }
         }
     }
-    if (want_dx) {
-        if constexpr (EPW > 1) {
+    if constexpr (DX) {
+        if constexpr (Gm::EPW > 1) {
 #pragma unroll
-            for (int off = LPE; off < 64; off <<= 1)
+            for (int off = Gm::LPE; off < 64; off <<= 1)
 #pragma unroll
-                for (int k = 0; k < DIN; ++k)
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) dxa[k][c] += __shfl_xor(dxa[k][c], off, 64);
+                for (int k = 0; k < DIN; ++k) dxa[k] += __shfl_xor(dxa[k], off, 64);
         }
         if (g == 0) {
-            float* dp = dx + (int64_t)j * (DIN * C) + c0;
+            float* dp = dx + (int64_t)j * (DIN * C) + c;
 #pragma unroll
-            for (int k = 0; k < DIN; ++k) store_ch<CPL>(dp + k * C, dxa[k]);
+            for (int k = 0; k < DIN; ++k) dp[k * C] = (float)dxa[k];
         }
     }
 }
 
-template <int LIN, int LSH, int LOUT, int CPL, int LPE>
+template <int LIN, int LSH, int LOUT, int C, bool DX, bool DW, bool DY>
+hipError_t launch_bwd_t(int32_t N, GraphView g, const float* x, const float* Y, const float* W, const float* G,
+                        float* dx, float* dW, float* dY, hipStream_t s)
+{
+    using Gm = Geo<C>;
+    const unsigned blocks = Gm::WPN > 1 ? (unsigned)N : (unsigned)((N + 3) / 4);
+    const unsigned threads = Gm::WPN > 1 ? 64u * Gm::WPN : 256u;
+    hipLaunchKernelGGL((k_conv_bwd<LIN, LSH, LOUT, C, DX, DW, DY>), dim3(blocks), dim3(threads), 0, s, N, g, x, Y,
+                       W, G, dx, dW, dY);
+    return hipGetLastError();
+}
+
+template <int LIN, int LSH, int LOUT, int C>
 hipError_t launch_bwd(int32_t N, GraphView g, const float* x, const float* Y, const float* W, const float* G,
                       float* dx, float* dW, float* dY, int mask, hipStream_t s)
 {
     if (N == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_conv_bwd<LIN, LSH, LOUT, CPL, LPE>), dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, N,
-                       g, x, Y, W, G, dx, dW, dY, mask);
-    return hipGetLastError();
+    switch (mask) {
+        case 1: return launch_bwd_t<LIN, LSH, LOUT, C, true, false, false>(N, g, x, Y, W, G, dx, dW, dY, s);
+        case 2: return launch_bwd_t<LIN, LSH, LOUT, C, false, true, false>(N, g, x, Y, W, G, dx, dW, dY, s);
+        case 3: return launch_bwd_t<LIN, LSH, LOUT, C, true, true, false>(N, g, x, Y, W, G, dx, dW, dY, s);
+        case 4: return launch_bwd_t<LIN, LSH, LOUT, C, false, false, true>(N, g, x, Y, W, G, dx, dW, dY, s);
+        case 5: return launch_bwd_t<LIN, LSH, LOUT, C, true, false, true>(N, g, x, Y, W, G, dx, dW, dY, s);
+        case 6: return launch_bwd_t<LIN, LSH, LOUT, C, false, true, true>(N, g, x, Y, W, G, dx, dW, dY, s);
+        case 7: return launch_bwd_t<LIN, LSH, LOUT, C, true, true, true>(N, g, x, Y, W, G, dx, dW, dY, s);
+        default: return hipSuccess;
+    }
 }
 
-
-template <int L, int C, int CPL>
+template <int L, int C>
 constexpr KernelSet make_set()
 {
-    return KernelSet{L, L, L, C, &launch_sh<L>, &launch_fwd<L, L, L, CPL, C / CPL>, &launch_bwd<L, L, L, CPL, C / CPL>};
+    return KernelSet{L, L, L, C, &launch_sh<L>, &launch_fwd<L, L, L, C>, &launch_bwd<L, L, L, C>};
 }
 
 template <int LIN, int LSH, int LOUT>

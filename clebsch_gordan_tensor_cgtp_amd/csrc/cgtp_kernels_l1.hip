@@ -4,11 +4,11 @@
 namespace cgtp {
 
 static const KernelSet kSets[] = {
-    make_set<1, 8, 2>(),
-    make_set<1, 16, 2>(),
-    make_set<1, 32, 2>(),
-    make_set<1, 64, 2>(),
-    make_set<1, 128, 2>(),
+    make_set<1, 8>(),
+    make_set<1, 16>(),
+    make_set<1, 32>(),
+    make_set<1, 64>(),
+    make_set<1, 128>(),
 };
 
 const KernelSet* kernels_l1(int channels)

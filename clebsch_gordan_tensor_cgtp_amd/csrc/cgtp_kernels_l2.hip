@@ -4,11 +4,11 @@
 namespace cgtp {
 
 static const KernelSet kSets[] = {
-    make_set<2, 8, 2>(),
-    make_set<2, 16, 2>(),
-    make_set<2, 32, 2>(),
-    make_set<2, 64, 2>(),
-    make_set<2, 128, 2>(),
+    make_set<2, 8>(),
+    make_set<2, 16>(),
+    make_set<2, 32>(),
+    make_set<2, 64>(),
+    make_set<2, 128>(),
 };
 
 const KernelSet* kernels_l2(int channels)

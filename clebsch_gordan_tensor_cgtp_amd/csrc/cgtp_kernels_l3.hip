@@ -4,10 +4,10 @@
 namespace cgtp {
 
 static const KernelSet kSets[] = {
-    make_set<3, 8, 1>(),
-    make_set<3, 16, 1>(),
-    make_set<3, 32, 1>(),
-    make_set<3, 64, 1>(),
+    make_set<3, 8>(),
+    make_set<3, 16>(),
+    make_set<3, 32>(),
+    make_set<3, 64>(),
 };
 
 const KernelSet* kernels_l3(int channels)

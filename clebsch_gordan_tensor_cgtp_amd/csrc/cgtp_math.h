@@ -146,6 +146,33 @@ CGTP_HD constexpr Path path_at(int lin, int lsh, int lout, int p)
 
 CGTP_HD constexpr int path_size(Path p) { return (2 * p.l1 + 1) * (2 * p.l2 + 1) * (2 * p.l3 + 1); }
 
+// Every real-basis coefficient is +-sqrt(q) with q a small rational.  Snapping
+// to that form (continued fraction of v*v, then one square root) makes equal
+// coefficients bit-identical whatever route computed them, so a kernel needs
+// only one register constant per distinct magnitude.
+CGTP_HD constexpr double canonical(double v)
+{
+    const double x = v * v;
+    int64_t h0 = 0, h1 = 1, k0 = 1, k1 = 0;
+    double r = x;
+    for (int it = 0; it < 40; ++it) {
+        const int64_t a = (int64_t)r;
+        const int64_t h2 = a * h1 + h0, k2 = a * k1 + k0;
+        h0 = h1;
+        h1 = h2;
+        k0 = k1;
+        k1 = k2;
+        const double approx = (double)h1 / (double)k1;
+        const double err = approx > x ? approx - x : x - approx;
+        if (err <= 1e-13 * x || k1 > 100000000) break;
+        const double frac = r - (double)a;
+        if (frac < 1e-12) break;
+        r = 1.0 / frac;
+    }
+    const double q = csqrt((double)h1 / (double)k1);
+    return v < 0.0 ? -q : q;
+}
+
 // real-basis coefficient T_p[m1][m2][m3], computed by scattering every
 // complex coefficient <l1 mu1 l2 mu2 | l3 mu1+mu2> onto the real indices
 // m_i = +-|mu_i| that it feeds.
@@ -170,7 +197,7 @@ CGTP_HD constexpr double real_cg(int l1, int l2, int l3, int m1, int m2, int m3)
         }
     }
     const double v = ((l1 + l2 + l3) & 1) ? im : re;
-    return (v < 1e-14 && v > -1e-14) ? 0.0 : v;
+    return (v < 1e-14 && v > -1e-14) ? 0.0 : canonical(v);
 }
 
 // ---- compile-time tables ---------------------------------------------------
