@@ -158,7 +158,9 @@ cgtp_status_t cgtp_conv_fwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
     if (n_nodes == 0) return CGTP_OK;
     if (!out || !aligned8(out) || !x || !aligned8(x)) return CGTP_ERR_INVALID_ARG;
     if (n_edges > 0 && (!Y || !W || !aligned8(W) || ((uintptr_t)Y & 3u))) return CGTP_ERR_INVALID_ARG;
-    return hip_status(plan->ks->fwd((int32_t)n_nodes, row_ptr, src, x, Y, W, out, stream));
+    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges);
+    const int32_t* rorder = (const int32_t*)((const char*)ws + L.rorder);
+    return hip_status(plan->ks->fwd((int32_t)n_nodes, row_ptr, src, rorder, x, Y, W, out, stream));
 }
 
 cgtp_status_t cgtp_conv_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
@@ -180,7 +182,7 @@ cgtp_status_t cgtp_conv_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
     const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges);
     const char* base = (const char*)ws;
     cgtp::GraphView g{(const int32_t*)(base + L.srow), (const int32_t*)(base + L.perm),
-                      (const int32_t*)(base + L.sdst)};
+                      (const int32_t*)(base + L.sdst), (const int32_t*)(base + L.sorder), (int32_t)n_edges};
     return hip_status(
         plan->ks->bwd((int32_t)n_nodes, g, x, Y, W, grad_out, grad_x, grad_W, grad_Y, mask, stream));
 }

@@ -24,32 +24,60 @@ __global__ void __launch_bounds__(256) k_outdeg(int32_t E, const int32_t* __rest
     if (e < E) atomicAdd(&cnt[src[e]], 1);
 }
 
-// srow[0] = 0, srow[j+1] = srow[j] + cnt[j]; one block of 1024 threads, each
-// scanning a contiguous chunk; also clears the scatter cursors
-__global__ void __launch_bounds__(1024) k_scan(int32_t N, const int32_t* __restrict__ cnt,
-                                                int32_t* __restrict__ srow, int32_t* __restrict__ cursor)
+constexpr int kDegBins = 1024;  // degrees at or above kDegBins-1 share the first bin
+
+// One block of 1024 threads, each owning a contiguous chunk of nodes:
+//   srow[0] = 0, srow[j+1] = srow[j] + cnt[j]  (sender offsets), cursors cleared;
+//   rorder / sorder: nodes ordered by in-degree / out-degree, longest first, so
+//   the convolution kernels start the longest segments first (ties in any
+//   order: the order only schedules blocks, every output has a fixed sum order).
+__global__ void __launch_bounds__(1024) k_scan(int32_t N, const int32_t* __restrict__ row_ptr,
+                                                const int32_t* __restrict__ cnt, int32_t* __restrict__ srow,
+                                                int32_t* __restrict__ cursor, int32_t* __restrict__ rorder,
+                                                int32_t* __restrict__ sorder)
 {
     __shared__ int32_t part[1024];
+    __shared__ int32_t hin[kDegBins], hout[kDegBins];
     const int t = threadIdx.x;
     const int32_t chunk = (N + 1023) / 1024;
     const int32_t b = t * chunk;
     const int32_t end = b + chunk < N ? b + chunk : N;
+    auto bin = [](int32_t deg) { return kDegBins - 1 - (deg < kDegBins - 1 ? deg : kDegBins - 1); };
+    hin[t] = 0;
+    hout[t] = 0;
     int32_t s = 0;
     for (int32_t j = b; j < end; ++j) s += cnt[j];
     part[t] = s;
     __syncthreads();
+    for (int32_t j = b; j < end; ++j) {
+        atomicAdd(&hin[bin(row_ptr[j + 1] - row_ptr[j])], 1);
+        atomicAdd(&hout[bin(cnt[j])], 1);
+    }
+    __syncthreads();  // histograms complete before the scan reads them
     for (int off = 1; off < 1024; off <<= 1) {
         const int32_t v = t >= off ? part[t - off] : 0;
+        const int32_t vi = t >= off ? hin[t - off] : 0;
+        const int32_t vo = t >= off ? hout[t - off] : 0;
         __syncthreads();
         part[t] += v;
+        hin[t] += vi;
+        hout[t] += vo;
         __syncthreads();
     }
+    // exclusive bin starts
+    const int32_t hi_excl = t > 0 ? hin[t - 1] : 0, ho_excl = t > 0 ? hout[t - 1] : 0;
+    __syncthreads();
+    hin[t] = hi_excl;
+    hout[t] = ho_excl;
+    __syncthreads();
     int32_t run = part[t] - s;  // exclusive prefix of this chunk
     if (t == 0) srow[0] = 0;
     for (int32_t j = b; j < end; ++j) {
         run += cnt[j];
         srow[j + 1] = run;
         cursor[j] = 0;
+        rorder[atomicAdd(&hin[bin(row_ptr[j + 1] - row_ptr[j])], 1)] = j;
+        sorder[atomicAdd(&hout[bin(cnt[j])], 1)] = j;
     }
 }
 
@@ -136,10 +164,12 @@ hipError_t launch_graph_prepare(int32_t N, int32_t E, const int32_t* row_ptr, co
     int32_t* sdst = (int32_t*)(base + L.sdst);
     int32_t* cnt = (int32_t*)(base + L.cnt);
     int32_t* cursor = (int32_t*)(base + L.cursor);
+    int32_t* rorder = (int32_t*)(base + L.rorder);
+    int32_t* sorder = (int32_t*)(base + L.sorder);
     const unsigned bN = (unsigned)((N + 255) / 256), bE = (unsigned)((E + 255) / 256);
     if (N > 0) hipLaunchKernelGGL(k_fill_i32, dim3(bN), dim3(256), 0, s, N, cnt, 0);
     if (E > 0) hipLaunchKernelGGL(k_outdeg, dim3(bE), dim3(256), 0, s, E, src, cnt);
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, N, cnt, srow, cursor);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, N, row_ptr, cnt, srow, cursor, rorder, sorder);
     if (E > 0) hipLaunchKernelGGL(k_scatter, dim3(bE), dim3(256), 0, s, E, src, srow, cursor, perm);
     if (E > 0) hipLaunchKernelGGL(k_sort_buckets, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, N, row_ptr, srow,
                                   perm, sdst);

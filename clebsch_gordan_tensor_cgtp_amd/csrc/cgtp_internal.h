@@ -10,7 +10,7 @@ namespace cgtp {
 
 // Byte offsets of the sender-sorted graph view inside the workspace.
 struct WsLayout {
-    size_t srow, perm, sdst, cnt, cursor, total;
+    size_t srow, perm, sdst, cnt, cursor, rorder, sorder, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -29,21 +29,27 @@ inline WsLayout ws_layout(int64_t N, int64_t E)
     o += align256(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
     w.cursor = o;
     o += align256(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+    w.rorder = o;
+    o += align256(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+    w.sorder = o;
+    o += align256(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
     w.total = o;
     return w;
 }
 
 struct GraphView {
-    const int32_t* srow;  // [N+1] sender offsets
-    const int32_t* perm;  // [E]  edge ids grouped by sender
-    const int32_t* sdst;  // [E]  receiver of perm[k]
+    const int32_t* srow;    // [N+1] sender offsets
+    const int32_t* perm;    // [E]  edge ids grouped by sender
+    const int32_t* sdst;    // [E]  receiver of perm[k]
+    const int32_t* sorder;  // [N]  senders, longest out-edge list first
+    int32_t n_edges;        // E
 };
 
 enum GradMask : int { kGradX = 1, kGradW = 2, kGradY = 4 };
 
 using ShLaunch = hipError_t (*)(int64_t E, const float* r, float* Y, hipStream_t s);
-using FwdLaunch = hipError_t (*)(int32_t N, const int32_t* row_ptr, const int32_t* src, const float* x,
-                                 const float* Y, const float* W, float* out, hipStream_t s);
+using FwdLaunch = hipError_t (*)(int32_t N, const int32_t* row_ptr, const int32_t* src, const int32_t* rorder,
+                                 const float* x, const float* Y, const float* W, float* out, hipStream_t s);
 using BwdLaunch = hipError_t (*)(int32_t N, GraphView g, const float* x, const float* Y, const float* W,
                                  const float* G, float* dx, float* dW, float* dY, int mask, hipStream_t s);
 

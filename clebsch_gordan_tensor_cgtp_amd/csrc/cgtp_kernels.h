@@ -85,26 +85,6 @@ struct PathK {
     }
 };
 
-// M[a][c] = sum_b T[a][b][c] y[k2 + b] for the nonzero (a, c) pairs of path K.
-template <class K, int DSH>
-__device__ __forceinline__ void make_M(const double (&y)[DSH], double (&M)[K::d1][K::d3])
-{
-    static_for<0, K::d1>([&](auto A) {
-        static_for<0, K::d3>([&](auto Cc) {
-            constexpr int a = decltype(A)::value, c = decltype(Cc)::value;
-            if constexpr (K::NZ(a, c)) {
-                double s = 0.0;
-                static_for<0, K::d2>([&](auto B) {
-                    constexpr int b = decltype(B)::value;
-                    constexpr double t = K::T(a, b, c);
-                    if constexpr (t != 0.0) s = __builtin_fma(t, y[K::k2 + b], s);
-                });
-                M[a][c] = s;
-            }
-        });
-    });
-}
-
 // ----------------------------------------------------------------------------
 // real spherical harmonics (orthonormal, l <= 3), fp64 from fp32 vectors
 // ----------------------------------------------------------------------------
@@ -166,76 +146,93 @@ hipError_t launch_sh(int64_t E, const float* r, float* Y, hipStream_t s)
 }
 
 // ----------------------------------------------------------------------------
-// lane geometry
+// work decomposition
 // ----------------------------------------------------------------------------
+// One 256-thread block per node.  LPE = min(C, 64) lanes cover the channels
+// of one edge; a lane owns the channels cl, cl+64, ... (NH = max(1, C/64) of
+// them) and handles them one after the other, so only one slice's operands
+// are live at a time.  The block's S = 256/LPE edge streams take the node's
+// edges in turn (stream s: the node's edges s, s+S, s+2S, ...), which keeps a
+// long segment from serialising on one wave and gives the GPU four times more
+// work items than one wave per node; the streams' partial sums are combined
+// in LDS in a fixed order at the end (atomic-free, deterministic).
 template <int C>
 struct Geo {
-    static constexpr int LPE = C < 64 ? C : 64;  // lanes per edge (one channel each)
-    static constexpr int EPW = 64 / LPE;         // edges a wave processes at once
-    static constexpr int WPN = C > 64 ? C / 64 : 1;  // waves per node
     static_assert(C > 0 && (C & (C - 1)) == 0 && C <= 256, "C must be a power of two <= 256");
+    static constexpr int LPE = C < 64 ? C : 64;      // lanes per edge
+    static constexpr int NH = C > 64 ? C / 64 : 1;   // channel slices per lane
+    static constexpr int S = 256 / LPE;              // edge streams per block
 };
 
-// minimum waves per SIMD the register allocation must allow
-#ifndef CGTP_BWD_OCC
-#define CGTP_BWD_OCC 2
-#endif
-#ifndef CGTP_FWD_OCC
-#define CGTP_FWD_OCC 4
-#endif
-// software prefetch of the next edge's operands (1) or not (0)
-#ifndef CGTP_BWD_PREFETCH
-#define CGTP_BWD_PREFETCH 0
-#endif
-#ifndef CGTP_FWD_PREFETCH
-#define CGTP_FWD_PREFETCH 1
-#endif
+// Per-specialisation tuning: the minimum waves per SIMD the register
+// allocation must allow, and whether the next edge's operands are loaded
+// before the current edge is computed.  Chosen so that no specialisation
+// spills vector registers (a spill costs far more than the occupancy it buys).
+template <int L, int C>
+struct Tune {
+    static constexpr int fwd_occ = L <= 2 ? 3 : 2;
+    static constexpr int bwd_occ = 2;
+    static constexpr bool fwd_prefetch = false;
+    static constexpr bool bwd_prefetch = false;
+};
+
+// An empty asm that takes a register value and hands it back: the optimiser
+// must materialise the value at that point and cannot match it with values
+// computed before it.  Used to keep accumulations in path order (otherwise
+// they are sunk to the end of the edge and every path's intermediates stay
+// live) and to keep per-path products from being shared across paths.
+__device__ __forceinline__ void opaque(double& v) { asm volatile("" : "+v"(v)); }
+
+// stream index of this thread; wave-uniform (scalar) when a stream is a wave
+template <int LPE>
+__device__ __forceinline__ int stream_of(int tid)
+{
+    if constexpr (LPE == 64) return __builtin_amdgcn_readfirstlane(tid >> 6);
+    else return tid / LPE;
+}
 
 // ----------------------------------------------------------------------------
 // forward
 // ----------------------------------------------------------------------------
-template <class Tb>
+template <class Tb, int NH>
 struct FwdEdge {
-    static constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH, DOUT = Tb::DOUT;
-    float w[P], x[DIN], y[DSH];
+    static constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH;
+    float w[NH][P], x[NH][DIN], y[DSH];
 };
 
 template <class Tb, int C>
-__device__ __forceinline__ void fwd_load(FwdEdge<Tb>& d, int32_t e, int c, const int32_t* __restrict__ src,
-                                         const float* __restrict__ x, const float* __restrict__ Y,
-                                         const float* __restrict__ W)
+__device__ __forceinline__ void fwd_load(FwdEdge<Tb, Geo<C>::NH>& d, int32_t e, int cl,
+                                         const int32_t* __restrict__ src, const float* __restrict__ x,
+                                         const float* __restrict__ Y, const float* __restrict__ W)
 {
-    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH;
+    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH, NH = Geo<C>::NH, LPE = Geo<C>::LPE;
     const int32_t j = src[e];
-    const float* wp = W + (int64_t)e * (P * C) + c;
 #pragma unroll
-    for (int p = 0; p < P; ++p) d.w[p] = __builtin_nontemporal_load(wp + p * C);
-    const float* xp = x + (int64_t)j * (DIN * C) + c;
+    for (int h = 0; h < NH; ++h) {
+        const float* wp = W + (int64_t)e * (P * C) + h * LPE + cl;
 #pragma unroll
-    for (int k = 0; k < DIN; ++k) d.x[k] = xp[k * C];
+        for (int p = 0; p < P; ++p) d.w[h][p] = __builtin_nontemporal_load(wp + p * C);
+        const float* xp = x + (int64_t)j * (DIN * C) + h * LPE + cl;
+#pragma unroll
+        for (int k = 0; k < DIN; ++k) d.x[h][k] = xp[k * C];
+    }
     const float* yp = Y + (int64_t)e * DSH;
 #pragma unroll
     for (int k = 0; k < DSH; ++k) d.y[k] = yp[k];
 }
 
-// acc[l3,m3] += sum_p W_p sum_{a,b} T_p[a][b][m3] x[l1,a] y[l2,b]
+// acc[l3,m3] += sum_p W_p sum_{a,b} T_p[a][b][m3] x[l1,a] y[l2,b] for one channel
 template <class Tb>
-__device__ __forceinline__ void fwd_compute(const FwdEdge<Tb>& d, double (&acc)[Tb::DOUT])
+__device__ __forceinline__ void fwd_slice(const float (&w)[Tb::P], const float (&x)[Tb::DIN],
+                                          const double (&yv)[Tb::DSH], double (&acc)[Tb::DOUT])
 {
-    constexpr int DIN = Tb::DIN, DSH = Tb::DSH;
-    double xv[DIN], yv[DSH];
+    double xv[Tb::DIN];
 #pragma unroll
-    for (int k = 0; k < DIN; ++k) xv[k] = (double)d.x[k];
-#pragma unroll
-    for (int k = 0; k < DSH; ++k) yv[k] = (double)d.y[k];
+    for (int k = 0; k < Tb::DIN; ++k) xv[k] = (double)x[k];
     static_for<0, Tb::P>([&](auto PI) {
         constexpr int p = decltype(PI)::value;
         using K = PathK<Tb, p>;
-        // first path of its (l1,l2) block forms the products for the block
-        constexpr bool first = (p == 0) || Tb::data.l1[p > 0 ? p - 1 : 0] != K::l1 ||
-                               Tb::data.l2[p > 0 ? p - 1 : 0] != K::l2;
-        (void)first;
-        const double w = (double)d.w[p];
+        const double wd = (double)w[p];
         static_for<0, K::d3>([&](auto M3) {
             constexpr int m3 = decltype(M3)::value;
             double z = 0.0;
@@ -250,130 +247,134 @@ __device__ __forceinline__ void fwd_compute(const FwdEdge<Tb>& d, double (&acc)[
                     }
                 });
             });
-            if (any) acc[K::k3 + m3] = __builtin_fma(w, z, acc[K::k3 + m3]);
+            if (any) acc[K::k3 + m3] = __builtin_fma(wd, z, acc[K::k3 + m3]);
         });
+        // keep the accumulation in path order (see opaque)
+        static_for<0, K::d3>([&](auto M3) { opaque(acc[K::k3 + decltype(M3)::value]); });
     });
 }
 
 template <int LIN, int LSH, int LOUT, int C>
-__global__ void __launch_bounds__(256, CGTP_FWD_OCC) k_conv_fwd(int32_t N, const int32_t* __restrict__ row_ptr,
-                                                   const int32_t* __restrict__ src, const float* __restrict__ x,
-                                                   const float* __restrict__ Y, const float* __restrict__ W,
-                                                   float* __restrict__ out)
+__global__ void __launch_bounds__(256, (Tune<LIN, C>::fwd_occ)) k_conv_fwd(int32_t N, const int32_t* __restrict__ row_ptr,
+                                                               const int32_t* __restrict__ src,
+                                                               const int32_t* __restrict__ rorder,
+                                                               const float* __restrict__ x,
+                                                               const float* __restrict__ Y,
+                                                               const float* __restrict__ W, float* __restrict__ out)
 {
     using Tb = cgmath::Tables<LIN, LSH, LOUT>;
-    using G = Geo<C>;
-    constexpr int DOUT = Tb::DOUT;
-    const int lane = threadIdx.x & 63;
-    // wave index made explicitly uniform so the node, its segment and the
-    // per-edge indices live in scalar registers
-    const int32_t gw = (int32_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int32_t i = gw / G::WPN;
-    if (i >= N) return;
-    const int g = lane / G::LPE;
-    const int c = (gw % G::WPN) * 64 + lane % G::LPE;
+    using Gm = Geo<C>;
+    constexpr int DSH = Tb::DSH, DOUT = Tb::DOUT, NH = Gm::NH, S = Gm::S, LPE = Gm::LPE;
+    __shared__ double red[S * DOUT * C];  // [stream][k][channel]
 
-    double acc[DOUT];
-#pragma unroll
-    for (int k = 0; k < DOUT; ++k) acc[k] = 0.0;
-
+    const int tid = threadIdx.x;
+    const int cl = tid % LPE;
+    const int s = stream_of<LPE>(tid);
+    const int32_t i = rorder[blockIdx.x];
+    if ((uint32_t)i >= (uint32_t)N) return;  // unprepared workspace: never index with it
     const int32_t end = row_ptr[i + 1];
-    int32_t e = row_ptr[i] + g;
-    FwdEdge<Tb> cur;
-    if (CGTP_FWD_PREFETCH && e < end) fwd_load<Tb, C>(cur, e, c, src, x, Y, W);
+
+    double acc[NH][DOUT];
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int k = 0; k < DOUT; ++k) acc[h][k] = 0.0;
+
+    int32_t e = row_ptr[i] + s;
+    FwdEdge<Tb, NH> cur;
+    if (Tune<LIN, C>::fwd_prefetch && e < end) fwd_load<Tb, C>(cur, e, cl, src, x, Y, W);
     while (e < end) {
-        const int32_t en = e + G::EPW;
-        FwdEdge<Tb> nxt;
-        if (CGTP_FWD_PREFETCH) {
-            if (en < end) fwd_load<Tb, C>(nxt, en, c, src, x, Y, W);
+        const int32_t en = e + S;
+        FwdEdge<Tb, NH> nxt;
+        if (Tune<LIN, C>::fwd_prefetch) {
+            if (en < end) fwd_load<Tb, C>(nxt, en, cl, src, x, Y, W);
         } else {
-            fwd_load<Tb, C>(cur, e, c, src, x, Y, W);
+            fwd_load<Tb, C>(cur, e, cl, src, x, Y, W);
         }
-        fwd_compute<Tb>(cur, acc);
-        if (CGTP_FWD_PREFETCH) cur = nxt;
+        double yv[DSH];
+#pragma unroll
+        for (int k = 0; k < DSH; ++k) yv[k] = (double)cur.y[k];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) fwd_slice<Tb>(cur.w[h], cur.x[h], yv, acc[h]);
+        if (Tune<LIN, C>::fwd_prefetch) cur = nxt;
         e = en;
     }
-    if constexpr (G::EPW > 1) {
+
+    // combine the streams in a fixed order; out[i] has this block as its only writer
 #pragma unroll
-        for (int off = G::LPE; off < 64; off <<= 1)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
-            for (int k = 0; k < DOUT; ++k) acc[k] += __shfl_xor(acc[k], off, 64);
-    }
-    if (g == 0) {
-        float* op = out + (int64_t)i * (DOUT * C) + c;
+        for (int k = 0; k < DOUT; ++k) red[(s * DOUT + k) * C + h * LPE + cl] = acc[h][k];
+    __syncthreads();
+    float* op = out + (int64_t)i * (DOUT * C);
+    for (int t = tid; t < DOUT * C; t += 256) {
+        double v = 0.0;
 #pragma unroll
-        for (int k = 0; k < DOUT; ++k) op[k * C] = (float)acc[k];
+        for (int q = 0; q < S; ++q) v += red[q * DOUT * C + t];
+        op[t] = (float)v;
     }
 }
 
 template <int LIN, int LSH, int LOUT, int C>
-hipError_t launch_fwd(int32_t N, const int32_t* row_ptr, const int32_t* src, const float* x, const float* Y,
-                      const float* W, float* out, hipStream_t s)
+hipError_t launch_fwd(int32_t N, const int32_t* row_ptr, const int32_t* src, const int32_t* rorder, const float* x,
+                      const float* Y, const float* W, float* out, hipStream_t s)
 {
     if (N == 0) return hipSuccess;
-    const int64_t waves = (int64_t)N * Geo<C>::WPN;
-    hipLaunchKernelGGL((k_conv_fwd<LIN, LSH, LOUT, C>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, N,
-                       row_ptr, src, x, Y, W, out);
+    hipLaunchKernelGGL((k_conv_fwd<LIN, LSH, LOUT, C>), dim3((unsigned)N), dim3(256), 0, s, N, row_ptr, src, rorder,
+                       x, Y, W, out);
     return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------
 // backward
 // ----------------------------------------------------------------------------
-template <class Tb>
+template <class Tb, int NH>
 struct BwdEdge {
     static constexpr int P = Tb::P, DSH = Tb::DSH, DOUT = Tb::DOUT;
     int32_t e;
-    float w[P], g[DOUT], y[DSH];
+    float w[NH][P], g[NH][DOUT], y[DSH];
 };
 
 template <class Tb, int C>
-__device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, int c, const GraphView& gv,
+__device__ __forceinline__ void bwd_load(BwdEdge<Tb, Geo<C>::NH>& d, int32_t q, int cl, const GraphView& gv,
                                          const float* __restrict__ Y, const float* __restrict__ W,
                                          const float* __restrict__ Gr)
 {
-    constexpr int P = Tb::P, DSH = Tb::DSH, DOUT = Tb::DOUT;
+    constexpr int P = Tb::P, DSH = Tb::DSH, DOUT = Tb::DOUT, NH = Geo<C>::NH, LPE = Geo<C>::LPE;
     const int32_t e = gv.perm[q];
     const int32_t i = gv.sdst[q];
     d.e = e;
-    const float* wp = W + (int64_t)e * (P * C) + c;
 #pragma unroll
-    for (int p = 0; p < P; ++p) d.w[p] = __builtin_nontemporal_load(wp + p * C);
-    const float* gp = Gr + (int64_t)i * (DOUT * C) + c;
+    for (int h = 0; h < NH; ++h) {
+        const float* wp = W + (int64_t)e * (P * C) + h * LPE + cl;
 #pragma unroll
-    for (int k = 0; k < DOUT; ++k) d.g[k] = gp[k * C];
+        for (int p = 0; p < P; ++p) d.w[h][p] = __builtin_nontemporal_load(wp + p * C);
+        const float* gp = Gr + (int64_t)i * (DOUT * C) + h * LPE + cl;
+#pragma unroll
+        for (int k = 0; k < DOUT; ++k) d.g[h][k] = gp[k * C];
+    }
     const float* yp = Y + (int64_t)e * DSH;
 #pragma unroll
     for (int k = 0; k < DSH; ++k) d.y[k] = yp[k];
 }
 
-// One edge of the backward for this lane's channel:
+// One edge of the backward for one channel:
 //   R_p[a][b] = sum_m3 T_p[a][b][m3] g[l3,m3]
 //   h_p[a] = sum_b R_p[a][b] y[l2,b]   -> dx[l1,a] += W_p h_p[a], dW_p = sum_a x[l1,a] h_p[a]
 //   v_p[b] = sum_a R_p[a][b] x[l1,a]   -> dy[l2,b] += W_p v_p[b]
-// Hide a register value from the optimiser: values passed through here before
-// each path cannot be matched with the previous path's, so products of
-// coefficients and components are not shared across paths and kept live for
-// the whole edge (which costs more registers than recomputing them).
-__device__ __forceinline__ void opaque(double& v) { asm volatile("" : "+v"(v)); }
-
 template <class Tb, int C, bool DX, bool DW, bool DY>
-__device__ __forceinline__ void bwd_compute(const BwdEdge<Tb>& d, const double (&xv)[Tb::DIN],
-                                            double (&dxa)[Tb::DIN], float* __restrict__ dwp,
-                                            double (&dya)[Tb::DSH])
+__device__ __forceinline__ void bwd_slice(const float (&w)[Tb::P], const float (&g)[Tb::DOUT],
+                                          const double (&yv)[Tb::DSH], const double (&xv)[Tb::DIN],
+                                          double (&dxa)[Tb::DIN], float* __restrict__ dwp, double (&dya)[Tb::DSH])
 {
-    constexpr int DSH = Tb::DSH, DOUT = Tb::DOUT;
-    double gv[DOUT], yv[DSH];
+    constexpr int DOUT = Tb::DOUT;
+    double gv[DOUT];
 #pragma unroll
-    for (int k = 0; k < DOUT; ++k) gv[k] = (double)d.g[k];
-#pragma unroll
-    for (int k = 0; k < DSH; ++k) yv[k] = (double)d.y[k];
-#pragma unroll
-    for (int k = 0; k < DSH; ++k) dya[k] = 0.0;
+    for (int k = 0; k < DOUT; ++k) gv[k] = (double)g[k];
     static_for<0, Tb::P>([&](auto PI) {
         constexpr int p = decltype(PI)::value;
         using K = PathK<Tb, p>;
-        const double w = (double)d.w[p];
+        const double wd = (double)w[p];
         static_for<0, K::d3>([&](auto M3) { opaque(gv[K::k3 + decltype(M3)::value]); });
         double v[K::d2];
         static_for<0, K::d2>([&](auto B) { v[decltype(B)::value] = 0.0; });
@@ -384,7 +385,6 @@ __device__ __forceinline__ void bwd_compute(const BwdEdge<Tb>& d, const double (
                 double h = 0.0;
                 static_for<0, K::d2>([&](auto B) {
                     constexpr int b = decltype(B)::value;
-                    // R[a][b]
                     double r = 0.0;
                     bool any = false;
                     static_for<0, K::d3>([&](auto M3) {
@@ -400,7 +400,7 @@ __device__ __forceinline__ void bwd_compute(const BwdEdge<Tb>& d, const double (
                         if constexpr (DY) v[b] = __builtin_fma(r, xv[K::k1 + a], v[b]);
                     }
                 });
-                if constexpr (DX) dxa[K::k1 + a] = __builtin_fma(w, h, dxa[K::k1 + a]);
+                if constexpr (DX) dxa[K::k1 + a] = __builtin_fma(wd, h, dxa[K::k1 + a]);
                 if constexpr (DW) dw = __builtin_fma(xv[K::k1 + a], h, dw);
             }
         });
@@ -408,16 +408,22 @@ __device__ __forceinline__ void bwd_compute(const BwdEdge<Tb>& d, const double (
         if constexpr (DY)
             static_for<0, K::d2>([&](auto B) {
                 constexpr int b = decltype(B)::value;
-                if constexpr (K::COL2(b)) dya[K::k2 + b] = __builtin_fma(w, v[b], dya[K::k2 + b]);
+                if constexpr (K::COL2(b)) dya[K::k2 + b] = __builtin_fma(wd, v[b], dya[K::k2 + b]);
             });
-        // schedule path by path: interleaving paths buys little ILP at this
-        // occupancy and multiplies the live transients
+        // Pin this path's accumulator updates here: without it the compiler
+        // sinks every accumulation to the end of the edge and keeps all
+        // paths' h and v values live at once.
+        if constexpr (DX)
+            static_for<0, K::d1>([&](auto A) {
+                if constexpr (K::ROW(decltype(A)::value)) opaque(dxa[K::k1 + decltype(A)::value]);
+            });
+        if constexpr (DY)
+            static_for<0, K::d2>([&](auto B) {
+                if constexpr (K::COL2(decltype(B)::value)) opaque(dya[K::k2 + decltype(B)::value]);
+            });
         __builtin_amdgcn_sched_barrier(0);
     });
 }
-
-// grad_Y slots combined across the waves of a sender (C > 64), in LDS
-constexpr int kDyBatch = 32;
 
 // quad_perm DPP move of a double (both halves), CTRL a quad_perm selector
 template <int CTRL>
@@ -456,129 +462,102 @@ __device__ __forceinline__ double wave_sum_lds(const double (&v)[D], double* __r
 }
 
 template <int LIN, int LSH, int LOUT, int C, bool DX, bool DW, bool DY>
-__global__ void __launch_bounds__(256, CGTP_BWD_OCC) k_conv_bwd(int32_t N, GraphView gv, const float* __restrict__ x,
-                                                   const float* __restrict__ Y, const float* __restrict__ W,
-                                                   const float* __restrict__ Gr, float* __restrict__ dx,
-                                                   float* __restrict__ dW, float* __restrict__ dY)
+__global__ void __launch_bounds__(256, (Tune<LIN, C>::bwd_occ)) k_conv_bwd(int32_t N, GraphView gv, const float* __restrict__ x,
+                                                               const float* __restrict__ Y,
+                                                               const float* __restrict__ W,
+                                                               const float* __restrict__ Gr, float* __restrict__ dx,
+                                                               float* __restrict__ dW, float* __restrict__ dY)
 {
     using Tb = cgmath::Tables<LIN, LSH, LOUT>;
     using Gm = Geo<C>;
-    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH;
-    constexpr int WPN = Gm::WPN;
-    constexpr int NPB = WPN > 1 ? 1 : 4;  // senders per block
-    // per-wave grad_Y partial sums of a batch of edges (only when WPN > 1)
-    __shared__ double dy_part[WPN > 1 ? WPN : 1][WPN > 1 ? kDyBatch : 1][DSH];
-    __shared__ int32_t dy_edge[WPN > 1 ? kDyBatch : 1];
-    // per-wave transpose tile of the channel reduction (one channel per lane)
-    constexpr bool kLdsSum = DY && Gm::LPE == 64;
-    __shared__ double dy_red[kLdsSum ? (WPN > 1 ? WPN : 4) : 1][kLdsSum ? DSH * 64 : 1];
+    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH, NH = Gm::NH, S = Gm::S, LPE = Gm::LPE;
+    // LDS: per-wave grad_Y transpose tiles during the edge loop, then the
+    // streams' grad_x partials
+    constexpr bool kLdsSum = DY && LPE == 64;
+    constexpr int kTiles = kLdsSum ? 4 * DSH * 64 : 0;
+    constexpr int kDx = DX ? S * DIN * C : 0;
+    constexpr int kLds = (kTiles > kDx ? kTiles : kDx) > 0 ? (kTiles > kDx ? kTiles : kDx) : 1;
+    __shared__ double lds[kLds];
 
-    const int lane = threadIdx.x & 63;
-    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int32_t j = (int32_t)blockIdx.x * NPB + (WPN > 1 ? 0 : wv);
-    if (WPN == 1 && j >= N) return;  // whole wave; no block barrier when WPN == 1
-    const int half = WPN > 1 ? wv : 0;
-    const int g = lane / Gm::LPE;
-    const int c = half * 64 + lane % Gm::LPE;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int cl = tid % LPE;
+    const int s = stream_of<LPE>(tid);
+    const int32_t j = gv.sorder[blockIdx.x];
+    if ((uint32_t)j >= (uint32_t)N) return;  // unprepared workspace: never index with it
 
-    double xv[DIN], dxa[DIN];
-    {
-        const float* xp = x + (int64_t)j * (DIN * C) + c;
+    double xv[NH][DIN], dxa[NH][DIN];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const float* xp = x + (int64_t)j * (DIN * C) + h * LPE + cl;
 #pragma unroll
         for (int k = 0; k < DIN; ++k) {
-            xv[k] = (double)xp[k * C];
-            dxa[k] = 0.0;
+            xv[h][k] = (double)xp[k * C];
+            dxa[h][k] = 0.0;
         }
     }
-    const int32_t beg = gv.srow[j], end = gv.srow[j + 1];
-
-    if constexpr (WPN == 1) {
-        int32_t q = beg + g;
-        BwdEdge<Tb> cur;
-        if (CGTP_BWD_PREFETCH && q < end) bwd_load<Tb, C>(cur, q, c, gv, Y, W, Gr);
-        while (q < end) {
-            const int32_t qn = q + Gm::EPW;
-            BwdEdge<Tb> nxt;
-            if (CGTP_BWD_PREFETCH) {
-                if (qn < end) bwd_load<Tb, C>(nxt, qn, c, gv, Y, W, Gr);
+    const int32_t end = gv.srow[j + 1];
+    int32_t q = gv.srow[j] + s;
+    BwdEdge<Tb, NH> cur;
+    if (Tune<LIN, C>::bwd_prefetch && q < end) bwd_load<Tb, C>(cur, q, cl, gv, Y, W, Gr);
+    while (q < end) {
+        const int32_t qn = q + S;
+        if ((uint32_t)gv.perm[q] >= (uint32_t)gv.n_edges || (uint32_t)gv.sdst[q] >= (uint32_t)N) {
+            q = qn;  // corrupt view entry: skip rather than read out of bounds
+            continue;
+        }
+        BwdEdge<Tb, NH> nxt;
+        if (Tune<LIN, C>::bwd_prefetch) {
+            if (qn < end) bwd_load<Tb, C>(nxt, qn, cl, gv, Y, W, Gr);
+        } else {
+            bwd_load<Tb, C>(cur, q, cl, gv, Y, W, Gr);
+        }
+        double yv[DSH], dya[DSH];
+#pragma unroll
+        for (int k = 0; k < DSH; ++k) {
+            yv[k] = (double)cur.y[k];
+            dya[k] = 0.0;
+        }
+        float* dwp = dW + (int64_t)cur.e * (P * C) + cl;
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+            bwd_slice<Tb, C, DX, DW, DY>(cur.w[h], cur.g[h], yv, xv[h], dxa[h], dwp + h * LPE, dya);
+        if constexpr (DY) {
+            if constexpr (kLdsSum) {
+                const double t = wave_sum_lds<DSH>(dya, lds + (tid >> 6) * (DSH * 64), lane);
+                if ((lane & 3) == 0 && (lane >> 2) < DSH) dY[(int64_t)cur.e * DSH + (lane >> 2)] = (float)t;
             } else {
-                bwd_load<Tb, C>(cur, q, c, gv, Y, W, Gr);
-            }
-            double dya[DSH];
-            bwd_compute<Tb, C, DX, DW, DY>(cur, xv, dxa, dW + (int64_t)cur.e * (P * C) + c, dya);
-            if constexpr (DY) {
-                if constexpr (kLdsSum) {
-                    const double t = wave_sum_lds<DSH>(dya, dy_red[wv], lane);
-                    if ((lane & 3) == 0 && (lane >> 2) < DSH) dY[(int64_t)cur.e * DSH + (lane >> 2)] = (float)t;
-                } else {
 #pragma unroll
-                    for (int k = 0; k < DSH; ++k) {
-                        double s = dya[k];
+                for (int k = 0; k < DSH; ++k) {
+                    double v = dya[k];
 #pragma unroll
-                        for (int off = 1; off < Gm::LPE; off <<= 1) s += __shfl_xor(s, off, 64);
-                        dya[k] = s;
-                    }
-                    if ((lane % Gm::LPE) == 0) {
-                        float* yp = dY + (int64_t)cur.e * DSH;
+                    for (int off = 1; off < LPE; off <<= 1) v += __shfl_xor(v, off, 64);
+                    dya[k] = v;
+                }
+                if (cl == 0) {
+                    float* yp = dY + (int64_t)cur.e * DSH;
 #pragma unroll
-                        for (int k = 0; k < DSH; ++k) yp[k] = (float)dya[k];
-                    }
+                    for (int k = 0; k < DSH; ++k) yp[k] = (float)dya[k];
                 }
-            }
-            if (CGTP_BWD_PREFETCH) cur = nxt;
-            q = qn;
-        }
-    } else {
-        // WPN waves share the sender; the segment is walked in batches so the
-        // per-wave grad_Y partials can be combined in LDS
-        const int32_t n = end - beg;
-        for (int32_t b0 = 0; b0 < n; b0 += kDyBatch) {
-            const int32_t nb = n - b0 < kDyBatch ? n - b0 : kDyBatch;
-            int32_t q = beg + b0;
-            const int32_t qe = q + nb;
-            BwdEdge<Tb> cur;
-            if (CGTP_BWD_PREFETCH) bwd_load<Tb, C>(cur, q, c, gv, Y, W, Gr);
-            for (int32_t s = 0; s < nb; ++s) {
-                BwdEdge<Tb> nxt;
-                if (CGTP_BWD_PREFETCH) {
-                    if (q + 1 < qe) bwd_load<Tb, C>(nxt, q + 1, c, gv, Y, W, Gr);
-                } else {
-                    bwd_load<Tb, C>(cur, q, c, gv, Y, W, Gr);
-                }
-                double dya[DSH];
-                bwd_compute<Tb, C, DX, DW, DY>(cur, xv, dxa, dW + (int64_t)cur.e * (P * C) + c, dya);
-                if constexpr (DY) {
-                    const double t = wave_sum_lds<DSH>(dya, dy_red[wv], lane);
-                    if ((lane & 3) == 0 && (lane >> 2) < DSH) dy_part[half][s][lane >> 2] = t;
-                    if (lane == 0 && half == 0) dy_edge[s] = cur.e;
-                }
-                if (CGTP_BWD_PREFETCH) cur = nxt;
-                ++q;
-            }
-            if constexpr (DY) {
-                __syncthreads();
-                for (int t = threadIdx.x; t < nb * DSH; t += 64 * WPN) {
-                    const int s = t / DSH, k = t % DSH;
-                    double v = 0.0;
-#pragma unroll
-                    for (int h = 0; h < WPN; ++h) v += dy_part[h][s][k];
-                    dY[(int64_t)dy_edge[s] * DSH + k] = (float)v;
-                }
-                __syncthreads();
             }
         }
+        if (Tune<LIN, C>::bwd_prefetch) cur = nxt;
+        q = qn;
     }
     if constexpr (DX) {
-        if constexpr (Gm::EPW > 1) {
+        // combine the streams in a fixed order; dx[j] has this block as its only writer
+        if constexpr (kLdsSum) __syncthreads();  // every wave is done with its grad_Y tile
 #pragma unroll
-            for (int off = Gm::LPE; off < 64; off <<= 1)
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
-                for (int k = 0; k < DIN; ++k) dxa[k] += __shfl_xor(dxa[k], off, 64);
-        }
-        if (g == 0) {
-            float* dp = dx + (int64_t)j * (DIN * C) + c;
+            for (int k = 0; k < DIN; ++k) lds[(s * DIN + k) * C + h * LPE + cl] = dxa[h][k];
+        __syncthreads();
+        float* dp = dx + (int64_t)j * (DIN * C);
+        for (int t = tid; t < DIN * C; t += 256) {
+            double v = 0.0;
 #pragma unroll
-            for (int k = 0; k < DIN; ++k) dp[k * C] = (float)dxa[k];
+            for (int r = 0; r < S; ++r) v += lds[r * DIN * C + t];
+            dp[t] = (float)v;
         }
     }
 }
@@ -587,10 +566,7 @@ template <int LIN, int LSH, int LOUT, int C, bool DX, bool DW, bool DY>
 hipError_t launch_bwd_t(int32_t N, GraphView g, const float* x, const float* Y, const float* W, const float* G,
                         float* dx, float* dW, float* dY, hipStream_t s)
 {
-    using Gm = Geo<C>;
-    const unsigned blocks = Gm::WPN > 1 ? (unsigned)N : (unsigned)((N + 3) / 4);
-    const unsigned threads = Gm::WPN > 1 ? 64u * Gm::WPN : 256u;
-    hipLaunchKernelGGL((k_conv_bwd<LIN, LSH, LOUT, C, DX, DW, DY>), dim3(blocks), dim3(threads), 0, s, N, g, x, Y,
+    hipLaunchKernelGGL((k_conv_bwd<LIN, LSH, LOUT, C, DX, DW, DY>), dim3((unsigned)N), dim3(256), 0, s, N, g, x, Y,
                        W, G, dx, dW, dY);
     return hipGetLastError();
 }

@@ -142,6 +142,17 @@ def test_graph_prepare_is_the_stable_sender_sort(torch_dev, oracle, key):
     np.testing.assert_array_equal(srow, rs)
     np.testing.assert_array_equal(perm, rp)
     np.testing.assert_array_equal(sdst, rd)
+    # block schedules: permutations of the nodes, longest segment first (ties free)
+    o += a(4 * E)
+    o += 2 * a(4 * N)                                  # degree counters and cursors
+    rorder = ws[o:o + 4 * N].view(np.int32)
+    o += a(4 * N)
+    sorder = ws[o:o + 4 * N].view(np.int32)
+    indeg = np.minimum(np.diff(g.row_ptr), 1023)
+    outdeg = np.minimum(np.diff(rs), 1023)
+    for order, deg in ((rorder, indeg), (sorder, outdeg)):
+        np.testing.assert_array_equal(np.sort(order), np.arange(N))
+        assert np.all(np.diff(deg[order]) <= 0)
 
 
 # ---------------------------------------------------------------------------
