@@ -54,9 +54,9 @@ cgtp_status_t check_graph_args(const cgtp_plan_s* plan, int64_t N, int64_t E, co
     return CGTP_OK;
 }
 
-cgtp_status_t check_ws(int64_t N, int64_t E, const void* ws, size_t ws_bytes)
+cgtp_status_t check_ws(const cgtp_plan_s* plan, int64_t N, int64_t E, const void* ws, size_t ws_bytes)
 {
-    const cgtp::WsLayout L = cgtp::ws_layout(N, E);
+    const cgtp::WsLayout L = cgtp::ws_layout(N, E, plan->ks->dyp_per_edge);
     if (!ws || ws_bytes < L.total) return CGTP_ERR_WORKSPACE;
     if (((uintptr_t)ws & 255u) != 0) return CGTP_ERR_INVALID_ARG;
     return CGTP_OK;
@@ -125,7 +125,7 @@ cgtp_status_t cgtp_plan_export_cg(cgtp_plan_t plan, int path, double* dense)
 cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, size_t* bytes)
 {
     if (!plan || !bytes || n_nodes < 0 || n_edges < 0) return CGTP_ERR_INVALID_ARG;
-    *bytes = cgtp::ws_layout(n_nodes, n_edges).total;
+    *bytes = cgtp::ws_layout(n_nodes, n_edges, plan->ks->dyp_per_edge).total;
     return CGTP_OK;
 }
 
@@ -142,7 +142,7 @@ cgtp_status_t cgtp_graph_prepare(cgtp_plan_t plan, int64_t n_nodes, int64_t n_ed
 {
     cgtp_status_t st = check_graph_args(plan, n_nodes, n_edges, row_ptr, src);
     if (st != CGTP_OK) return st;
-    st = check_ws(n_nodes, n_edges, ws, ws_bytes);
+    st = check_ws(plan, n_nodes, n_edges, ws, ws_bytes);
     if (st != CGTP_OK) return st;
     return hip_status(cgtp::launch_graph_prepare((int32_t)n_nodes, (int32_t)n_edges, row_ptr, src, ws, stream));
 }
@@ -153,24 +153,24 @@ cgtp_status_t cgtp_conv_fwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
 {
     cgtp_status_t st = check_graph_args(plan, n_nodes, n_edges, row_ptr, src);
     if (st != CGTP_OK) return st;
-    st = check_ws(n_nodes, n_edges, ws, ws_bytes);
+    st = check_ws(plan, n_nodes, n_edges, ws, ws_bytes);
     if (st != CGTP_OK) return st;
     if (n_nodes == 0) return CGTP_OK;
     if (!out || !aligned8(out) || !x || !aligned8(x)) return CGTP_ERR_INVALID_ARG;
     if (n_edges > 0 && (!Y || !W || !aligned8(W) || ((uintptr_t)Y & 3u))) return CGTP_ERR_INVALID_ARG;
-    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges);
+    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges, plan->ks->dyp_per_edge);
     const int32_t* rorder = (const int32_t*)((const char*)ws + L.rorder);
     return hip_status(plan->ks->fwd((int32_t)n_nodes, row_ptr, src, rorder, x, Y, W, out, stream));
 }
 
 cgtp_status_t cgtp_conv_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
                             const int32_t* src, const float* x, const float* Y, const float* W,
-                            const float* grad_out, float* grad_x, float* grad_W, float* grad_Y, const void* ws,
+                            const float* grad_out, float* grad_x, float* grad_W, float* grad_Y, void* ws,
                             size_t ws_bytes, hipStream_t stream)
 {
     cgtp_status_t st = check_graph_args(plan, n_nodes, n_edges, row_ptr, src);
     if (st != CGTP_OK) return st;
-    st = check_ws(n_nodes, n_edges, ws, ws_bytes);
+    st = check_ws(plan, n_nodes, n_edges, ws, ws_bytes);
     if (st != CGTP_OK) return st;
     int mask = (grad_x ? cgtp::kGradX : 0) | (grad_W ? cgtp::kGradW : 0) | (grad_Y ? cgtp::kGradY : 0);
     if (mask == 0 || n_nodes == 0) return CGTP_OK;
@@ -179,10 +179,11 @@ cgtp_status_t cgtp_conv_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
     if (n_edges > 0 && (!Y || !W || !aligned8(W) || ((uintptr_t)Y & 3u))) return CGTP_ERR_INVALID_ARG;
     if (grad_W && !aligned8(grad_W)) return CGTP_ERR_INVALID_ARG;
     if (grad_Y && ((uintptr_t)grad_Y & 3u)) return CGTP_ERR_INVALID_ARG;
-    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges);
-    const char* base = (const char*)ws;
+    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges, plan->ks->dyp_per_edge);
+    char* base = (char*)ws;
     cgtp::GraphView g{(const int32_t*)(base + L.srow), (const int32_t*)(base + L.perm),
-                      (const int32_t*)(base + L.sdst), (const int32_t*)(base + L.sorder), (int32_t)n_edges};
+                      (const int32_t*)(base + L.sdst), (const int32_t*)(base + L.sorder),
+                      (double*)(base + L.dyp), (int32_t)n_edges};
     return hip_status(
         plan->ks->bwd((int32_t)n_nodes, g, x, Y, W, grad_out, grad_x, grad_W, grad_Y, mask, stream));
 }

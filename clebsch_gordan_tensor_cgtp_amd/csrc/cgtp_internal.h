@@ -10,12 +10,14 @@ namespace cgtp {
 
 // Byte offsets of the sender-sorted graph view inside the workspace.
 struct WsLayout {
-    size_t srow, perm, sdst, cnt, cursor, rorder, sorder, total;
+    size_t srow, perm, sdst, cnt, cursor, rorder, sorder, dyp, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-inline WsLayout ws_layout(int64_t N, int64_t E)
+// dyp_per_edge: fp64 values per edge of the grad_Y slice partials (0 when the
+// plan's channels fit one 64-lane slice)
+inline WsLayout ws_layout(int64_t N, int64_t E, int64_t dyp_per_edge = 0)
 {
     WsLayout w{};
     size_t o = 0;
@@ -33,6 +35,8 @@ inline WsLayout ws_layout(int64_t N, int64_t E)
     o += align256(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
     w.sorder = o;
     o += align256(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+    w.dyp = o;
+    o += align256(sizeof(double) * (size_t)(E > 0 ? E : 0) * (size_t)dyp_per_edge);
     w.total = o;
     return w;
 }
@@ -42,6 +46,7 @@ struct GraphView {
     const int32_t* perm;    // [E]  edge ids grouped by sender
     const int32_t* sdst;    // [E]  receiver of perm[k]
     const int32_t* sorder;  // [N]  senders, longest out-edge list first
+    double* dyp;            // [E][H][D_sh] grad_Y slice partials (C > 64 only)
     int32_t n_edges;        // E
 };
 
@@ -55,6 +60,7 @@ using BwdLaunch = hipError_t (*)(int32_t N, GraphView g, const float* x, const f
 
 struct KernelSet {
     int l_in, l_sh, l_out, channels;
+    int dyp_per_edge;  // workspace fp64 values per edge for grad_Y slice partials
     ShLaunch sh;
     FwdLaunch fwd;
     BwdLaunch bwd;

@@ -148,20 +148,37 @@ hipError_t launch_sh(int64_t E, const float* r, float* Y, hipStream_t s)
 // ----------------------------------------------------------------------------
 // work decomposition
 // ----------------------------------------------------------------------------
-// One 256-thread block per node.  LPE = min(C, 64) lanes cover the channels
-// of one edge; a lane owns the channels cl, cl+64, ... (NH = max(1, C/64) of
-// them) and handles them one after the other, so only one slice's operands
-// are live at a time.  The block's S = 256/LPE edge streams take the node's
-// edges in turn (stream s: the node's edges s, s+S, s+2S, ...), which keeps a
-// long segment from serialising on one wave and gives the GPU four times more
-// work items than one wave per node; the streams' partial sums are combined
-// in LDS in a fixed order at the end (atomic-free, deterministic).
+// One 256-thread block (four waves) per node.  A lane owns one channel of an
+// edge: LPE = min(C, 64) lanes cover a 64-channel slice, and for C > 64 the
+// H = C/64 slices of a node go to different waves, so every wave carries the
+// state of a single slice (the register budget decides occupancy here).  The
+// node's edges are interleaved over the block's S edge streams (stream s takes
+// the node's edges s, s+S, s+2S, ...), which keeps a long segment from
+// serialising on one wave; the streams' partial sums are combined in LDS in a
+// fixed order at the end (atomic-free, deterministic).
 template <int C>
 struct Geo {
     static_assert(C > 0 && (C & (C - 1)) == 0 && C <= 256, "C must be a power of two <= 256");
-    static constexpr int LPE = C < 64 ? C : 64;      // lanes per edge
-    static constexpr int NH = C > 64 ? C / 64 : 1;   // channel slices per lane
-    static constexpr int S = 256 / LPE;              // edge streams per block
+    static constexpr int LPE = C < 64 ? C : 64;      // lanes per edge slice
+    static constexpr int H = C / LPE;                // channel slices (waves) per edge
+    static_assert(H <= 4, "at most four slices per block");
+    static constexpr int S = (4 / H) * (64 / LPE);   // edge streams per block
+};
+
+// position of this thread: channel slice, channel within the slice, stream
+template <int C>
+struct Pos {
+    int h, cl, s;
+    __device__ __forceinline__ explicit Pos(int tid)
+    {
+        using G = Geo<C>;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        h = wave % G::H;
+        cl = (tid & 63) % G::LPE;
+        if constexpr (G::LPE == 64) s = wave / G::H;  // wave-uniform
+        else s = (wave / G::H) * (64 / G::LPE) + (tid & 63) / G::LPE;
+    }
+    __device__ __forceinline__ int channel() const { return h * Geo<C>::LPE + cl; }
 };
 
 // Per-specialisation tuning: the minimum waves per SIMD the register
@@ -170,9 +187,9 @@ struct Geo {
 // spills vector registers (a spill costs far more than the occupancy it buys).
 template <int L, int C>
 struct Tune {
-    static constexpr int fwd_occ = L <= 2 ? 3 : 2;
-    static constexpr int bwd_occ = 2;
-    static constexpr bool fwd_prefetch = false;
+    static constexpr int fwd_occ = L <= 2 ? 4 : 2;
+    static constexpr int bwd_occ = L <= 2 ? 3 : 2;
+    static constexpr bool fwd_prefetch = L <= 2;
     static constexpr bool bwd_prefetch = false;
 };
 
@@ -183,39 +200,49 @@ struct Tune {
 // live) and to keep per-path products from being shared across paths.
 __device__ __forceinline__ void opaque(double& v) { asm volatile("" : "+v"(v)); }
 
-// stream index of this thread; wave-uniform (scalar) when a stream is a wave
-template <int LPE>
-__device__ __forceinline__ int stream_of(int tid)
+// fp64 value known to be equal in every lane, moved to a scalar register pair
+__device__ __forceinline__ double uniform(double v)
 {
-    if constexpr (LPE == 64) return __builtin_amdgcn_readfirstlane(tid >> 6);
-    else return tid / LPE;
+    const int lo = __builtin_amdgcn_readfirstlane(__double2loint(v));
+    const int hi = __builtin_amdgcn_readfirstlane(__double2hiint(v));
+    return __hiloint2double(hi, lo);
+}
+
+// the edge's spherical harmonics in fp64; held in scalar registers when the
+// whole wave works on one edge (they are then the same in every lane)
+template <int DSH, int LPE>
+__device__ __forceinline__ void edge_sh(const float (&y)[DSH], double (&yv)[DSH])
+{
+#pragma unroll
+    for (int k = 0; k < DSH; ++k) {
+        yv[k] = (double)y[k];
+        if constexpr (LPE == 64) yv[k] = uniform(yv[k]);
+    }
 }
 
 // ----------------------------------------------------------------------------
 // forward
 // ----------------------------------------------------------------------------
-template <class Tb, int NH>
+template <class Tb>
 struct FwdEdge {
     static constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH;
-    float w[NH][P], x[NH][DIN], y[DSH];
+    float w[P], x[DIN], y[DSH];
 };
 
+// operands of edge e for channel ch
 template <class Tb, int C>
-__device__ __forceinline__ void fwd_load(FwdEdge<Tb, Geo<C>::NH>& d, int32_t e, int cl,
-                                         const int32_t* __restrict__ src, const float* __restrict__ x,
-                                         const float* __restrict__ Y, const float* __restrict__ W)
+__device__ __forceinline__ void fwd_load(FwdEdge<Tb>& d, int32_t e, int ch, const int32_t* __restrict__ src,
+                                         const float* __restrict__ x, const float* __restrict__ Y,
+                                         const float* __restrict__ W)
 {
-    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH, NH = Geo<C>::NH, LPE = Geo<C>::LPE;
+    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH;
     const int32_t j = src[e];
+    const float* wp = W + (int64_t)e * (P * C) + ch;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        const float* wp = W + (int64_t)e * (P * C) + h * LPE + cl;
+    for (int p = 0; p < P; ++p) d.w[p] = __builtin_nontemporal_load(wp + p * C);
+    const float* xp = x + (int64_t)j * (DIN * C) + ch;
 #pragma unroll
-        for (int p = 0; p < P; ++p) d.w[h][p] = __builtin_nontemporal_load(wp + p * C);
-        const float* xp = x + (int64_t)j * (DIN * C) + h * LPE + cl;
-#pragma unroll
-        for (int k = 0; k < DIN; ++k) d.x[h][k] = xp[k * C];
-    }
+    for (int k = 0; k < DIN; ++k) d.x[k] = xp[k * C];
     const float* yp = Y + (int64_t)e * DSH;
 #pragma unroll
     for (int k = 0; k < DSH; ++k) d.y[k] = yp[k];
@@ -256,55 +283,51 @@ __device__ __forceinline__ void fwd_slice(const float (&w)[Tb::P], const float (
 
 template <int LIN, int LSH, int LOUT, int C>
 __global__ void __launch_bounds__(256, (Tune<LIN, C>::fwd_occ)) k_conv_fwd(int32_t N, const int32_t* __restrict__ row_ptr,
-                                                               const int32_t* __restrict__ src,
-                                                               const int32_t* __restrict__ rorder,
-                                                               const float* __restrict__ x,
-                                                               const float* __restrict__ Y,
-                                                               const float* __restrict__ W, float* __restrict__ out)
+                                                                         const int32_t* __restrict__ src,
+                                                                         const int32_t* __restrict__ rorder,
+                                                                         const float* __restrict__ x,
+                                                                         const float* __restrict__ Y,
+                                                                         const float* __restrict__ W,
+                                                                         float* __restrict__ out)
 {
     using Tb = cgmath::Tables<LIN, LSH, LOUT>;
     using Gm = Geo<C>;
-    constexpr int DSH = Tb::DSH, DOUT = Tb::DOUT, NH = Gm::NH, S = Gm::S, LPE = Gm::LPE;
+    constexpr int DSH = Tb::DSH, DOUT = Tb::DOUT, S = Gm::S;
+    constexpr bool kPf = Tune<LIN, C>::fwd_prefetch;
     __shared__ double red[S * DOUT * C];  // [stream][k][channel]
 
     const int tid = threadIdx.x;
-    const int cl = tid % LPE;
-    const int s = stream_of<LPE>(tid);
+    const Pos<C> ps(tid);
+    const int ch = ps.channel();
     const int32_t i = rorder[blockIdx.x];
     if ((uint32_t)i >= (uint32_t)N) return;  // unprepared workspace: never index with it
     const int32_t end = row_ptr[i + 1];
 
-    double acc[NH][DOUT];
+    double acc[DOUT];
 #pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-        for (int k = 0; k < DOUT; ++k) acc[h][k] = 0.0;
+    for (int k = 0; k < DOUT; ++k) acc[k] = 0.0;
 
-    int32_t e = row_ptr[i] + s;
-    FwdEdge<Tb, NH> cur;
-    if (Tune<LIN, C>::fwd_prefetch && e < end) fwd_load<Tb, C>(cur, e, cl, src, x, Y, W);
+    int32_t e = row_ptr[i] + ps.s;
+    FwdEdge<Tb> cur;
+    if (kPf && e < end) fwd_load<Tb, C>(cur, e, ch, src, x, Y, W);
     while (e < end) {
         const int32_t en = e + S;
-        FwdEdge<Tb, NH> nxt;
-        if (Tune<LIN, C>::fwd_prefetch) {
-            if (en < end) fwd_load<Tb, C>(nxt, en, cl, src, x, Y, W);
+        FwdEdge<Tb> nxt;
+        if (kPf) {
+            if (en < end) fwd_load<Tb, C>(nxt, en, ch, src, x, Y, W);
         } else {
-            fwd_load<Tb, C>(cur, e, cl, src, x, Y, W);
+            fwd_load<Tb, C>(cur, e, ch, src, x, Y, W);
         }
         double yv[DSH];
-#pragma unroll
-        for (int k = 0; k < DSH; ++k) yv[k] = (double)cur.y[k];
-#pragma unroll
-        for (int h = 0; h < NH; ++h) fwd_slice<Tb>(cur.w[h], cur.x[h], yv, acc[h]);
-        if (Tune<LIN, C>::fwd_prefetch) cur = nxt;
+        edge_sh<DSH, Gm::LPE>(cur.y, yv);
+        fwd_slice<Tb>(cur.w, cur.x, yv, acc);
+        if (kPf) cur = nxt;
         e = en;
     }
 
     // combine the streams in a fixed order; out[i] has this block as its only writer
 #pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-        for (int k = 0; k < DOUT; ++k) red[(s * DOUT + k) * C + h * LPE + cl] = acc[h][k];
+    for (int k = 0; k < DOUT; ++k) red[(ps.s * DOUT + k) * C + ch] = acc[k];
     __syncthreads();
     float* op = out + (int64_t)i * (DOUT * C);
     for (int t = tid; t < DOUT * C; t += 256) {
@@ -328,31 +351,29 @@ hipError_t launch_fwd(int32_t N, const int32_t* row_ptr, const int32_t* src, con
 // ----------------------------------------------------------------------------
 // backward
 // ----------------------------------------------------------------------------
-template <class Tb, int NH>
+template <class Tb>
 struct BwdEdge {
     static constexpr int P = Tb::P, DSH = Tb::DSH, DOUT = Tb::DOUT;
     int32_t e;
-    float w[NH][P], g[NH][DOUT], y[DSH];
+    float w[P], g[DOUT], y[DSH];
 };
 
+// operands of the q-th edge of the sender-sorted view for channel ch
 template <class Tb, int C>
-__device__ __forceinline__ void bwd_load(BwdEdge<Tb, Geo<C>::NH>& d, int32_t q, int cl, const GraphView& gv,
+__device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, int ch, const GraphView& gv,
                                          const float* __restrict__ Y, const float* __restrict__ W,
                                          const float* __restrict__ Gr)
 {
-    constexpr int P = Tb::P, DSH = Tb::DSH, DOUT = Tb::DOUT, NH = Geo<C>::NH, LPE = Geo<C>::LPE;
+    constexpr int P = Tb::P, DSH = Tb::DSH, DOUT = Tb::DOUT;
     const int32_t e = gv.perm[q];
     const int32_t i = gv.sdst[q];
     d.e = e;
+    const float* wp = W + (int64_t)e * (P * C) + ch;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        const float* wp = W + (int64_t)e * (P * C) + h * LPE + cl;
+    for (int p = 0; p < P; ++p) d.w[p] = __builtin_nontemporal_load(wp + p * C);
+    const float* gp = Gr + (int64_t)i * (DOUT * C) + ch;
 #pragma unroll
-        for (int p = 0; p < P; ++p) d.w[h][p] = __builtin_nontemporal_load(wp + p * C);
-        const float* gp = Gr + (int64_t)i * (DOUT * C) + h * LPE + cl;
-#pragma unroll
-        for (int k = 0; k < DOUT; ++k) d.g[h][k] = gp[k * C];
-    }
+    for (int k = 0; k < DOUT; ++k) d.g[k] = gp[k * C];
     const float* yp = Y + (int64_t)e * DSH;
 #pragma unroll
     for (int k = 0; k < DSH; ++k) d.y[k] = yp[k];
@@ -462,15 +483,19 @@ __device__ __forceinline__ double wave_sum_lds(const double (&v)[D], double* __r
 }
 
 template <int LIN, int LSH, int LOUT, int C, bool DX, bool DW, bool DY>
-__global__ void __launch_bounds__(256, (Tune<LIN, C>::bwd_occ)) k_conv_bwd(int32_t N, GraphView gv, const float* __restrict__ x,
-                                                               const float* __restrict__ Y,
-                                                               const float* __restrict__ W,
-                                                               const float* __restrict__ Gr, float* __restrict__ dx,
-                                                               float* __restrict__ dW, float* __restrict__ dY)
+__global__ void __launch_bounds__(256, (Tune<LIN, C>::bwd_occ)) k_conv_bwd(int32_t N, GraphView gv,
+                                                                         const float* __restrict__ x,
+                                                                         const float* __restrict__ Y,
+                                                                         const float* __restrict__ W,
+                                                                         const float* __restrict__ Gr,
+                                                                         float* __restrict__ dx,
+                                                                         float* __restrict__ dW,
+                                                                         float* __restrict__ dY)
 {
     using Tb = cgmath::Tables<LIN, LSH, LOUT>;
     using Gm = Geo<C>;
-    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH, NH = Gm::NH, S = Gm::S, LPE = Gm::LPE;
+    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH, S = Gm::S, LPE = Gm::LPE, H = Gm::H;
+    constexpr bool kPf = Tune<LIN, C>::bwd_prefetch;
     // LDS: per-wave grad_Y transpose tiles during the edge loop, then the
     // streams' grad_x partials
     constexpr bool kLdsSum = DY && LPE == 64;
@@ -481,51 +506,48 @@ __global__ void __launch_bounds__(256, (Tune<LIN, C>::bwd_occ)) k_conv_bwd(int32
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int cl = tid % LPE;
-    const int s = stream_of<LPE>(tid);
+    const Pos<C> ps(tid);
+    const int ch = ps.channel();
     const int32_t j = gv.sorder[blockIdx.x];
     if ((uint32_t)j >= (uint32_t)N) return;  // unprepared workspace: never index with it
 
-    double xv[NH][DIN], dxa[NH][DIN];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        const float* xp = x + (int64_t)j * (DIN * C) + h * LPE + cl;
+    double xv[DIN], dxa[DIN];
+    {
+        const float* xp = x + (int64_t)j * (DIN * C) + ch;
 #pragma unroll
         for (int k = 0; k < DIN; ++k) {
-            xv[h][k] = (double)xp[k * C];
-            dxa[h][k] = 0.0;
+            xv[k] = (double)xp[k * C];
+            dxa[k] = 0.0;
         }
     }
     const int32_t end = gv.srow[j + 1];
-    int32_t q = gv.srow[j] + s;
-    BwdEdge<Tb, NH> cur;
-    if (Tune<LIN, C>::bwd_prefetch && q < end) bwd_load<Tb, C>(cur, q, cl, gv, Y, W, Gr);
+    int32_t q = gv.srow[j] + ps.s;
+    BwdEdge<Tb> cur;
+    if (kPf && q < end) bwd_load<Tb, C>(cur, q, ch, gv, Y, W, Gr);
     while (q < end) {
         const int32_t qn = q + S;
         if ((uint32_t)gv.perm[q] >= (uint32_t)gv.n_edges || (uint32_t)gv.sdst[q] >= (uint32_t)N) {
             q = qn;  // corrupt view entry: skip rather than read out of bounds
             continue;
         }
-        BwdEdge<Tb, NH> nxt;
-        if (Tune<LIN, C>::bwd_prefetch) {
-            if (qn < end) bwd_load<Tb, C>(nxt, qn, cl, gv, Y, W, Gr);
+        BwdEdge<Tb> nxt;
+        if (kPf) {
+            if (qn < end) bwd_load<Tb, C>(nxt, qn, ch, gv, Y, W, Gr);
         } else {
-            bwd_load<Tb, C>(cur, q, cl, gv, Y, W, Gr);
+            bwd_load<Tb, C>(cur, q, ch, gv, Y, W, Gr);
         }
         double yv[DSH], dya[DSH];
+        edge_sh<DSH, LPE>(cur.y, yv);
 #pragma unroll
-        for (int k = 0; k < DSH; ++k) {
-            yv[k] = (double)cur.y[k];
-            dya[k] = 0.0;
-        }
-        float* dwp = dW + (int64_t)cur.e * (P * C) + cl;
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-            bwd_slice<Tb, C, DX, DW, DY>(cur.w[h], cur.g[h], yv, xv[h], dxa[h], dwp + h * LPE, dya);
+        for (int k = 0; k < DSH; ++k) dya[k] = 0.0;
+        bwd_slice<Tb, C, DX, DW, DY>(cur.w, cur.g, yv, xv, dxa, dW + (int64_t)cur.e * (P * C) + ch, dya);
         if constexpr (DY) {
             if constexpr (kLdsSum) {
                 const double t = wave_sum_lds<DSH>(dya, lds + (tid >> 6) * (DSH * 64), lane);
-                if ((lane & 3) == 0 && (lane >> 2) < DSH) dY[(int64_t)cur.e * DSH + (lane >> 2)] = (float)t;
+                if ((lane & 3) == 0 && (lane >> 2) < DSH) {
+                    if constexpr (H == 1) dY[(int64_t)cur.e * DSH + (lane >> 2)] = (float)t;
+                    else gv.dyp[((int64_t)cur.e * H + ps.h) * DSH + (lane >> 2)] = t;
+                }
             } else {
 #pragma unroll
                 for (int k = 0; k < DSH; ++k) {
@@ -534,23 +556,21 @@ __global__ void __launch_bounds__(256, (Tune<LIN, C>::bwd_occ)) k_conv_bwd(int32
                     for (int off = 1; off < LPE; off <<= 1) v += __shfl_xor(v, off, 64);
                     dya[k] = v;
                 }
-                if (cl == 0) {
+                if (ps.cl == 0) {
                     float* yp = dY + (int64_t)cur.e * DSH;
 #pragma unroll
                     for (int k = 0; k < DSH; ++k) yp[k] = (float)dya[k];
                 }
             }
         }
-        if (Tune<LIN, C>::bwd_prefetch) cur = nxt;
+        if (kPf) cur = nxt;
         q = qn;
     }
     if constexpr (DX) {
         // combine the streams in a fixed order; dx[j] has this block as its only writer
         if constexpr (kLdsSum) __syncthreads();  // every wave is done with its grad_Y tile
 #pragma unroll
-        for (int h = 0; h < NH; ++h)
-#pragma unroll
-            for (int k = 0; k < DIN; ++k) lds[(s * DIN + k) * C + h * LPE + cl] = dxa[h][k];
+        for (int k = 0; k < DIN; ++k) lds[(ps.s * DIN + k) * C + ch] = dxa[k];
         __syncthreads();
         float* dp = dx + (int64_t)j * (DIN * C);
         for (int t = tid; t < DIN * C; t += 256) {
@@ -562,12 +582,33 @@ __global__ void __launch_bounds__(256, (Tune<LIN, C>::bwd_occ)) k_conv_bwd(int32
     }
 }
 
+// grad_Y of an edge = the sum of its H slice partials (fixed order)
+template <int DSH, int H>
+__global__ void __launch_bounds__(256) k_dy_combine(int32_t E, const double* __restrict__ dyp, float* __restrict__ dY)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (int64_t)E * DSH) return;
+    const int64_t e = t / DSH;
+    const int k = (int)(t % DSH);
+    double v = 0.0;
+#pragma unroll
+    for (int h = 0; h < H; ++h) v += dyp[(e * H + h) * DSH + k];
+    dY[t] = (float)v;
+}
+
 template <int LIN, int LSH, int LOUT, int C, bool DX, bool DW, bool DY>
 hipError_t launch_bwd_t(int32_t N, GraphView g, const float* x, const float* Y, const float* W, const float* G,
                         float* dx, float* dW, float* dY, hipStream_t s)
 {
     hipLaunchKernelGGL((k_conv_bwd<LIN, LSH, LOUT, C, DX, DW, DY>), dim3((unsigned)N), dim3(256), 0, s, N, g, x, Y,
                        W, G, dx, dW, dY);
+    if constexpr (DY && Geo<C>::H > 1) {
+        constexpr int DSH = (LSH + 1) * (LSH + 1);
+        const int64_t n = (int64_t)g.n_edges * DSH;
+        if (n > 0)
+            hipLaunchKernelGGL((k_dy_combine<DSH, Geo<C>::H>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                               g.n_edges, g.dyp, dY);
+    }
     return hipGetLastError();
 }
 
@@ -591,7 +632,8 @@ hipError_t launch_bwd(int32_t N, GraphView g, const float* x, const float* Y, co
 template <int L, int C>
 constexpr KernelSet make_set()
 {
-    return KernelSet{L, L, L, C, &launch_sh<L>, &launch_fwd<L, L, L, C>, &launch_bwd<L, L, L, C>};
+    return KernelSet{L, L, L, C, Geo<C>::H > 1 ? Geo<C>::H * (L + 1) * (L + 1) : 0, &launch_sh<L>,
+                     &launch_fwd<L, L, L, C>, &launch_bwd<L, L, L, C>};
 }
 
 template <int LIN, int LSH, int LOUT>

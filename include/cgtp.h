@@ -92,8 +92,9 @@ cgtp_status_t cgtp_plan_info(cgtp_plan_t plan, int* num_paths, int* paths_l1l2l3
  * dense [(2l1+1)][(2l2+1)][(2l3+1)] fp64 into host memory `dense`. */
 cgtp_status_t cgtp_plan_export_cg(cgtp_plan_t plan, int path, double* dense);
 
-/* Bytes of device workspace the graph preparation needs for N nodes and E
- * edges (sender-sorted view of the CSR and its temporaries). */
+/* Bytes of device workspace for N nodes and E edges: the sender-sorted view
+ * of the CSR and its temporaries, degree-ordered block schedules, and for
+ * C > 64 a scratch section of 8*E*(C/64)*(l_sh+1)^2 bytes for the backward. */
 cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, size_t* bytes);
 
 /* Real spherical harmonics, degrees 0..l_sh, of r[e]/|r[e]|: Y[E][(l_sh+1)^2].
@@ -118,11 +119,14 @@ cgtp_status_t cgtp_conv_fwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
 
 /* Backward of L = <grad_out, out>: grad_x [N][(l_in+1)^2][C],
  * grad_W [E][P][C], grad_Y [E][(l_sh+1)^2]; each may be NULL to skip it.
- * Sender-centric and atomic-free over the prepared workspace `ws`. */
+ * Sender-centric and atomic-free over the prepared workspace `ws`.  For
+ * C > 64 the backward also writes per-slice grad_Y partial sums into the
+ * workspace's scratch section, so two backward calls in flight at the same
+ * time must not share one workspace (the graph view itself is only read). */
 cgtp_status_t cgtp_conv_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
                             const int32_t* src, const float* x, const float* Y, const float* W,
                             const float* grad_out, float* grad_x, float* grad_W, float* grad_Y,
-                            const void* ws, size_t ws_bytes, hipStream_t stream);
+                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* cgtp_status_string(cgtp_status_t status);
