@@ -11,17 +11,18 @@ namespace cgtp {
 // ----------------------------------------------------------------------------
 // graph preparation: sender-sorted view of the receiver CSR
 // ----------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) k_fill_i32(int32_t n, int32_t* __restrict__ p, int32_t v)
+// zero the padded per-sender counters
+__global__ void __launch_bounds__(256) k_zero_counters(int32_t n, int32_t* __restrict__ p)
 {
     const int32_t t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (t < n) p[t] = v;
+    if (t < n) p[(int64_t)t * kCounterStride] = 0;
 }
 
 // out-degree histogram (integer atomics: the counts do not depend on order)
 __global__ void __launch_bounds__(256) k_outdeg(int32_t E, const int32_t* __restrict__ src, int32_t* cnt)
 {
     const int32_t e = blockIdx.x * blockDim.x + threadIdx.x;
-    if (e < E) atomicAdd(&cnt[src[e]], 1);
+    if (e < E) atomicAdd(&cnt[(int64_t)src[e] * kCounterStride], 1);
 }
 
 constexpr int kDegBins = 1024;  // degrees at or above kDegBins-1 share the first bin
@@ -46,12 +47,12 @@ __global__ void __launch_bounds__(1024) k_scan(int32_t N, const int32_t* __restr
     hin[t] = 0;
     hout[t] = 0;
     int32_t s = 0;
-    for (int32_t j = b; j < end; ++j) s += cnt[j];
+    for (int32_t j = b; j < end; ++j) s += cnt[(int64_t)j * kCounterStride];
     part[t] = s;
     __syncthreads();
     for (int32_t j = b; j < end; ++j) {
         atomicAdd(&hin[bin(row_ptr[j + 1] - row_ptr[j])], 1);
-        atomicAdd(&hout[bin(cnt[j])], 1);
+        atomicAdd(&hout[bin(cnt[(int64_t)j * kCounterStride])], 1);
     }
     __syncthreads();  // histograms complete before the scan reads them
     for (int off = 1; off < 1024; off <<= 1) {
@@ -73,11 +74,12 @@ __global__ void __launch_bounds__(1024) k_scan(int32_t N, const int32_t* __restr
     int32_t run = part[t] - s;  // exclusive prefix of this chunk
     if (t == 0) srow[0] = 0;
     for (int32_t j = b; j < end; ++j) {
-        run += cnt[j];
+        const int32_t c = cnt[(int64_t)j * kCounterStride];
+        run += c;
         srow[j + 1] = run;
-        cursor[j] = 0;
+        cursor[(int64_t)j * kCounterStride] = 0;
         rorder[atomicAdd(&hin[bin(row_ptr[j + 1] - row_ptr[j])], 1)] = j;
-        sorder[atomicAdd(&hout[bin(cnt[j])], 1)] = j;
+        sorder[atomicAdd(&hout[bin(c)], 1)] = j;
     }
 }
 
@@ -89,7 +91,7 @@ __global__ void __launch_bounds__(256) k_scatter(int32_t E, const int32_t* __res
     const int32_t e = blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= E) return;
     const int32_t j = src[e];
-    const int32_t k = atomicAdd(&cursor[j], 1);
+    const int32_t k = atomicAdd(&cursor[(int64_t)j * kCounterStride], 1);
     perm[srow[j] + k] = e;
 }
 
@@ -167,7 +169,7 @@ hipError_t launch_graph_prepare(int32_t N, int32_t E, const int32_t* row_ptr, co
     int32_t* rorder = (int32_t*)(base + L.rorder);
     int32_t* sorder = (int32_t*)(base + L.sorder);
     const unsigned bN = (unsigned)((N + 255) / 256), bE = (unsigned)((E + 255) / 256);
-    if (N > 0) hipLaunchKernelGGL(k_fill_i32, dim3(bN), dim3(256), 0, s, N, cnt, 0);
+    if (N > 0) hipLaunchKernelGGL(k_zero_counters, dim3(bN), dim3(256), 0, s, N, cnt);
     if (E > 0) hipLaunchKernelGGL(k_outdeg, dim3(bE), dim3(256), 0, s, E, src, cnt);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, N, row_ptr, cnt, srow, cursor, rorder, sorder);
     if (E > 0) hipLaunchKernelGGL(k_scatter, dim3(bE), dim3(256), 0, s, E, src, srow, cursor, perm);

@@ -15,6 +15,11 @@ struct WsLayout {
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// the per-sender counters and cursors of the graph preparation are spaced one
+// 128-byte cache line apart, so their atomic updates do not serialise on
+// shared lines
+constexpr int kCounterStride = 32;
+
 // dyp_per_edge: fp64 values per edge of the grad_Y slice partials (0 when the
 // plan's channels fit one 64-lane slice)
 inline WsLayout ws_layout(int64_t N, int64_t E, int64_t dyp_per_edge = 0)
@@ -28,9 +33,9 @@ inline WsLayout ws_layout(int64_t N, int64_t E, int64_t dyp_per_edge = 0)
     w.sdst = o;
     o += align256(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
     w.cnt = o;
-    o += align256(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+    o += align256(sizeof(int32_t) * kCounterStride * (size_t)(N > 0 ? N : 1));
     w.cursor = o;
-    o += align256(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+    o += align256(sizeof(int32_t) * kCounterStride * (size_t)(N > 0 ? N : 1));
     w.rorder = o;
     o += align256(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
     w.sorder = o;

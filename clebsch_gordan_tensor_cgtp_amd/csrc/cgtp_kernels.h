@@ -292,9 +292,10 @@ __global__ void __launch_bounds__(256, (Tune<LIN, C>::fwd_occ)) k_conv_fwd(int32
 {
     using Tb = cgmath::Tables<LIN, LSH, LOUT>;
     using Gm = Geo<C>;
-    constexpr int DSH = Tb::DSH, DOUT = Tb::DOUT, S = Gm::S;
+    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH, DOUT = Tb::DOUT, S = Gm::S;
     constexpr bool kPf = Tune<LIN, C>::fwd_prefetch;
-    __shared__ double red[S * DOUT * C];  // [stream][k][channel]
+    // LDS: the streams' partial sums [stream][k][channel]
+    __shared__ double red[S * DOUT * C];
 
     const int tid = threadIdx.x;
     const Pos<C> ps(tid);
@@ -307,13 +308,16 @@ __global__ void __launch_bounds__(256, (Tune<LIN, C>::fwd_occ)) k_conv_fwd(int32
 #pragma unroll
     for (int k = 0; k < DOUT; ++k) acc[k] = 0.0;
 
+    // with prefetch, the stream's next edge is loaded before the current one
+    // is computed (the copy `cur = nxt` costs fewer registers than
+    // alternating two named buffers, which would spill at this occupancy)
     int32_t e = row_ptr[i] + ps.s;
     FwdEdge<Tb> cur;
     if (kPf && e < end) fwd_load<Tb, C>(cur, e, ch, src, x, Y, W);
     while (e < end) {
         const int32_t en = e + S;
         FwdEdge<Tb> nxt;
-        if (kPf) {
+        if constexpr (kPf) {
             if (en < end) fwd_load<Tb, C>(nxt, en, ch, src, x, Y, W);
         } else {
             fwd_load<Tb, C>(cur, e, ch, src, x, Y, W);
@@ -321,7 +325,7 @@ __global__ void __launch_bounds__(256, (Tune<LIN, C>::fwd_occ)) k_conv_fwd(int32
         double yv[DSH];
         edge_sh<DSH, Gm::LPE>(cur.y, yv);
         fwd_slice<Tb>(cur.w, cur.x, yv, acc);
-        if (kPf) cur = nxt;
+        if constexpr (kPf) cur = nxt;
         e = en;
     }
 
@@ -355,18 +359,23 @@ template <class Tb>
 struct BwdEdge {
     static constexpr int P = Tb::P, DSH = Tb::DSH, DOUT = Tb::DOUT;
     int32_t e;
+    bool ok;  // the view entry names a valid edge and receiver
     float w[P], g[DOUT], y[DSH];
 };
 
-// operands of the q-th edge of the sender-sorted view for channel ch
+// operands of the q-th edge of the sender-sorted view for channel ch; a
+// corrupt entry (possible only if the view was not prepared for this graph)
+// is read as edge 0 / receiver 0 and flagged, never used out of bounds
 template <class Tb, int C>
-__device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, int ch, const GraphView& gv,
+__device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, int ch, int32_t N, const GraphView& gv,
                                          const float* __restrict__ Y, const float* __restrict__ W,
                                          const float* __restrict__ Gr)
 {
     constexpr int P = Tb::P, DSH = Tb::DSH, DOUT = Tb::DOUT;
-    const int32_t e = gv.perm[q];
-    const int32_t i = gv.sdst[q];
+    int32_t e = gv.perm[q];
+    int32_t i = gv.sdst[q];
+    d.ok = (uint32_t)e < (uint32_t)gv.n_edges && (uint32_t)i < (uint32_t)N;
+    if (!d.ok) e = i = 0;
     d.e = e;
     const float* wp = W + (int64_t)e * (P * C) + ch;
 #pragma unroll
@@ -498,6 +507,7 @@ __global__ void __launch_bounds__(256, (Tune<LIN, C>::bwd_occ)) k_conv_bwd(int32
     constexpr bool kPf = Tune<LIN, C>::bwd_prefetch;
     // LDS: per-wave grad_Y transpose tiles during the edge loop, then the
     // streams' grad_x partials
+    constexpr int DOUT = Tb::DOUT;
     constexpr bool kLdsSum = DY && LPE == 64;
     constexpr int kTiles = kLdsSum ? 4 * DSH * 64 : 0;
     constexpr int kDx = DX ? S * DIN * C : 0;
@@ -522,20 +532,17 @@ __global__ void __launch_bounds__(256, (Tune<LIN, C>::bwd_occ)) k_conv_bwd(int32
     }
     const int32_t end = gv.srow[j + 1];
     int32_t q = gv.srow[j] + ps.s;
-    BwdEdge<Tb> cur;
-    if (kPf && q < end) bwd_load<Tb, C>(cur, q, ch, gv, Y, W, Gr);
-    while (q < end) {
+    // One edge: with prefetch, load the stream's next edge into `nxt` before
+    // computing `cur`.  The loop alternates the two buffers (no copies).
+    auto step = [&](BwdEdge<Tb>& cur, BwdEdge<Tb>& nxt) {
         const int32_t qn = q + S;
-        if ((uint32_t)gv.perm[q] >= (uint32_t)gv.n_edges || (uint32_t)gv.sdst[q] >= (uint32_t)N) {
-            q = qn;  // corrupt view entry: skip rather than read out of bounds
-            continue;
-        }
-        BwdEdge<Tb> nxt;
-        if (kPf) {
-            if (qn < end) bwd_load<Tb, C>(nxt, qn, ch, gv, Y, W, Gr);
+        if constexpr (kPf) {
+            if (qn < end) bwd_load<Tb, C>(nxt, qn, ch, N, gv, Y, W, Gr);
         } else {
-            bwd_load<Tb, C>(cur, q, ch, gv, Y, W, Gr);
+            bwd_load<Tb, C>(cur, q, ch, N, gv, Y, W, Gr);
         }
+        q = qn;
+        if (!cur.ok) return;
         double yv[DSH], dya[DSH];
         edge_sh<DSH, LPE>(cur.y, yv);
 #pragma unroll
@@ -563,8 +570,13 @@ __global__ void __launch_bounds__(256, (Tune<LIN, C>::bwd_occ)) k_conv_bwd(int32
                 }
             }
         }
-        if (kPf) cur = nxt;
-        q = qn;
+    };
+    BwdEdge<Tb> ea, eb;
+    if (kPf && q < end) bwd_load<Tb, C>(ea, q, ch, N, gv, Y, W, Gr);
+    while (q < end) {
+        step(ea, eb);
+        if (q >= end) break;
+        step(eb, ea);
     }
     if constexpr (DX) {
         // combine the streams in a fixed order; dx[j] has this block as its only writer

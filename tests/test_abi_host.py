@@ -86,7 +86,7 @@ def test_workspace_size(L):
     b = ctypes.c_size_t()
     assert L.lib().cgtp_workspace_size(h, 2000, 105730, ctypes.byref(b)) == L.CGTP_OK
     a = lambda v: (v + 255) // 256 * 256
-    assert b.value == a(4 * 2001) + 2 * a(4 * 105730) + 4 * a(4 * 2000) + a(8 * 105730 * 2 * 9)
+    assert b.value == a(4 * 2001) + 2 * a(4 * 105730) + 2 * a(4 * 32 * 2000) + 2 * a(4 * 2000) + a(8 * 105730 * 2 * 9)
     assert L.lib().cgtp_workspace_size(h, -1, 5, ctypes.byref(b)) == L.CGTP_ERR_INVALID_ARG
     assert L.lib().cgtp_workspace_size(h, 5, 5, None) == L.CGTP_ERR_INVALID_ARG
     L.lib().cgtp_plan_destroy(h)

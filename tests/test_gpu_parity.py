@@ -144,7 +144,7 @@ def test_graph_prepare_is_the_stable_sender_sort(torch_dev, oracle, key):
     np.testing.assert_array_equal(sdst, rd)
     # block schedules: permutations of the nodes, longest segment first (ties free)
     o += a(4 * E)
-    o += 2 * a(4 * N)                                  # degree counters and cursors
+    o += 2 * a(4 * 32 * N)                             # padded degree counters and cursors
     rorder = ws[o:o + 4 * N].view(np.int32)
     o += a(4 * N)
     sorder = ws[o:o + 4 * N].view(np.int32)
