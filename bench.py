@@ -82,23 +82,50 @@ def make_inputs(torch, dev, key, seed=0):
     return w, g, T(g.row_ptr), T(g.src), T(g.r), x, W, G
 
 
-def cpu_baseline(w, g, x, W, G):
-    """The fp64 oracle on one full step of the same workload (host cores)."""
+def cpu_baseline(w, g, x, W, G, min_seconds=10.0):
+    """The fp64 oracle on full steps of the same workload (host cores),
+    repeated until about `min_seconds` of CPU work has been timed."""
     import numpy as np
 
     import oracle
 
     L = w.l_max
     xh, Wh, Gh = (t.cpu().numpy() for t in (x, W, G))
+    steps = 0
     t0 = time.perf_counter()
-    Y = oracle.sh(L, g.r)
-    oracle.graph_transpose(g.row_ptr, g.src)
-    Yf = Y.astype(np.float32)
-    oracle.conv_fwd(L, L, L, g.row_ptr, g.src, xh, Yf, Wh)
-    oracle.conv_bwd(L, L, L, g.row_ptr, g.src, xh, Yf, Wh, Gh)
-    dt = time.perf_counter() - t0
-    return {"value": g.n_edges / dt, "unit": "edges/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"one full step (SH, transpose, fwd, bwd) of the {w.key} workload, {dt:.1f} s"}
+    while True:
+        Y = oracle.sh(L, g.r)
+        oracle.graph_transpose(g.row_ptr, g.src)
+        Yf = Y.astype(np.float32)
+        oracle.conv_fwd(L, L, L, g.row_ptr, g.src, xh, Yf, Wh)
+        oracle.conv_bwd(L, L, L, g.row_ptr, g.src, xh, Yf, Wh, Gh)
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": steps * g.n_edges / dt, "unit": "edges/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{steps} full steps (SH, transpose, fwd, bwd) of the {w.key} workload "
+                      f"({g.n_edges} edges each), {dt:.1f} s"}
+
+
+def copy_ceiling(torch, dev, nbytes=2 << 30, reps=5):
+    """Best-of-`reps` rates of plain device copies of `nbytes`: the runtime's
+    device-to-device copy and an elementwise kernel, read + write bytes."""
+    a = torch.randn(nbytes // 4, device=dev)
+    b = torch.empty_like(a)
+    res = {}
+    for name, fn in (("memcpy_d2d", lambda: b.copy_(a)), ("elementwise_neg", lambda: torch.neg(a, out=b))):
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        res[name + "_gbs"] = 2 * nbytes / best / 1e6
+    res["bytes_each_way"] = nbytes
+    return res
 
 
 def main():
@@ -110,6 +137,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy kernel (PMC byte calibration)")
+    ap.add_argument("--copy-ceiling", action="store_true",
+                    help="measure only the device-to-device copy rate (the practical HBM ceiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU sharding is "
@@ -127,6 +156,9 @@ def main():
             torch.neg(a, out=b)
         torch.cuda.synchronize()
         log(f"copy calibration: 3 launches of neg(), {4 * n} bytes read and {4 * n} written per launch")
+        return
+    if args.copy_ceiling:
+        print(json.dumps(copy_ceiling(torch, dev)), flush=True)
         return
 
     from clebsch_gordan_tensor_cgtp_amd.ops import Plan
