@@ -188,7 +188,7 @@ struct Pos {
 template <int L, int C>
 struct Tune {
     static constexpr int fwd_occ = L <= 2 ? 4 : 2;
-    static constexpr int bwd_occ = L <= 2 ? 3 : 2;
+    static constexpr int bwd_occ = L == 1 || (L == 2 && C >= 64) ? 4 : (L == 2 ? 3 : 2);
     static constexpr bool fwd_prefetch = L <= 2;
     static constexpr bool bwd_prefetch = false;
 };
@@ -392,66 +392,81 @@ __device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, int ch, int3
 //   R_p[a][b] = sum_m3 T_p[a][b][m3] g[l3,m3]
 //   h_p[a] = sum_b R_p[a][b] y[l2,b]   -> dx[l1,a] += W_p h_p[a], dW_p = sum_a x[l1,a] h_p[a]
 //   v_p[b] = sum_a R_p[a][b] x[l1,a]   -> dy[l2,b] += W_p v_p[b]
-template <class Tb, int C, bool DX, bool DW, bool DY>
+// The paths are taken grouped by l2, so only one degree's grad_Y partials
+// are live at a time; flush_y(k2, dy) receives each degree's partials
+// (components k2 .. k2+2*l2) as soon as its last path is done.
+template <class Tb, int C, bool DX, bool DW, bool DY, class FlushY>
 __device__ __forceinline__ void bwd_slice(const float (&w)[Tb::P], const float (&g)[Tb::DOUT],
                                           const double (&yv)[Tb::DSH], const double (&xv)[Tb::DIN],
-                                          double (&dxa)[Tb::DIN], float* __restrict__ dwp, double (&dya)[Tb::DSH])
+                                          double (&dxa)[Tb::DIN], float* __restrict__ dwp, FlushY&& flush_y)
 {
     constexpr int DOUT = Tb::DOUT;
     double gv[DOUT];
 #pragma unroll
     for (int k = 0; k < DOUT; ++k) gv[k] = (double)g[k];
-    static_for<0, Tb::P>([&](auto PI) {
-        constexpr int p = decltype(PI)::value;
-        using K = PathK<Tb, p>;
-        const double wd = (double)w[p];
-        static_for<0, K::d3>([&](auto M3) { opaque(gv[K::k3 + decltype(M3)::value]); });
-        double v[K::d2];
-        static_for<0, K::d2>([&](auto B) { v[decltype(B)::value] = 0.0; });
-        double dw = 0.0;
-        static_for<0, K::d1>([&](auto A) {
-            constexpr int a = decltype(A)::value;
-            if constexpr (K::ROW(a)) {
-                double h = 0.0;
-                static_for<0, K::d2>([&](auto B) {
-                    constexpr int b = decltype(B)::value;
-                    double r = 0.0;
-                    bool any = false;
-                    static_for<0, K::d3>([&](auto M3) {
-                        constexpr int m3 = decltype(M3)::value;
-                        constexpr double t = K::T(a, b, m3);
-                        if constexpr (t != 0.0) {
-                            r = __builtin_fma(t, gv[K::k3 + m3], r);
-                            any = true;
+    static_for<0, 4>([&](auto L2I) {
+        constexpr int l2 = decltype(L2I)::value;
+        constexpr int d2 = 2 * l2 + 1, k2 = l2 * l2;
+        if constexpr ((l2 + 1) * (l2 + 1) <= Tb::DSH) {
+            double dyb[d2];
+#pragma unroll
+            for (int b = 0; b < d2; ++b) dyb[b] = 0.0;
+            static_for<0, Tb::P>([&](auto PI) {
+                constexpr int p = decltype(PI)::value;
+                using K = PathK<Tb, p>;
+                if constexpr (K::l2 == l2) {
+                    const double wd = (double)w[p];
+                    static_for<0, K::d3>([&](auto M3) { opaque(gv[K::k3 + decltype(M3)::value]); });
+                    double v[d2];
+                    static_for<0, d2>([&](auto B) { v[decltype(B)::value] = 0.0; });
+                    double dw = 0.0;
+                    static_for<0, K::d1>([&](auto A) {
+                        constexpr int a = decltype(A)::value;
+                        if constexpr (K::ROW(a)) {
+                            double h = 0.0;
+                            static_for<0, d2>([&](auto B) {
+                                constexpr int b = decltype(B)::value;
+                                double r = 0.0;
+                                bool any = false;
+                                static_for<0, K::d3>([&](auto M3) {
+                                    constexpr int m3 = decltype(M3)::value;
+                                    constexpr double t = K::T(a, b, m3);
+                                    if constexpr (t != 0.0) {
+                                        r = __builtin_fma(t, gv[K::k3 + m3], r);
+                                        any = true;
+                                    }
+                                });
+                                if (any) {
+                                    h = __builtin_fma(r, yv[k2 + b], h);
+                                    if constexpr (DY) v[b] = __builtin_fma(r, xv[K::k1 + a], v[b]);
+                                }
+                            });
+                            if constexpr (DX) dxa[K::k1 + a] = __builtin_fma(wd, h, dxa[K::k1 + a]);
+                            if constexpr (DW) dw = __builtin_fma(xv[K::k1 + a], h, dw);
                         }
                     });
-                    if (any) {
-                        h = __builtin_fma(r, yv[K::k2 + b], h);
-                        if constexpr (DY) v[b] = __builtin_fma(r, xv[K::k1 + a], v[b]);
-                    }
-                });
-                if constexpr (DX) dxa[K::k1 + a] = __builtin_fma(wd, h, dxa[K::k1 + a]);
-                if constexpr (DW) dw = __builtin_fma(xv[K::k1 + a], h, dw);
-            }
-        });
-        if constexpr (DW) __builtin_nontemporal_store((float)dw, dwp + p * C);
-        if constexpr (DY)
-            static_for<0, K::d2>([&](auto B) {
-                constexpr int b = decltype(B)::value;
-                if constexpr (K::COL2(b)) dya[K::k2 + b] = __builtin_fma(wd, v[b], dya[K::k2 + b]);
+                    if constexpr (DW) __builtin_nontemporal_store((float)dw, dwp + p * C);
+                    if constexpr (DY)
+                        static_for<0, d2>([&](auto B) {
+                            constexpr int b = decltype(B)::value;
+                            if constexpr (K::COL2(b)) dyb[b] = __builtin_fma(wd, v[b], dyb[b]);
+                        });
+                    // Pin this path's accumulator updates here: without it the
+                    // compiler sinks every accumulation to the end of the edge
+                    // and keeps all paths' h and v values live at once.
+                    if constexpr (DX)
+                        static_for<0, K::d1>([&](auto A) {
+                            if constexpr (K::ROW(decltype(A)::value)) opaque(dxa[K::k1 + decltype(A)::value]);
+                        });
+                    if constexpr (DY)
+                        static_for<0, d2>([&](auto B) {
+                            if constexpr (K::COL2(decltype(B)::value)) opaque(dyb[decltype(B)::value]);
+                        });
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             });
-        // Pin this path's accumulator updates here: without it the compiler
-        // sinks every accumulation to the end of the edge and keeps all
-        // paths' h and v values live at once.
-        if constexpr (DX)
-            static_for<0, K::d1>([&](auto A) {
-                if constexpr (K::ROW(decltype(A)::value)) opaque(dxa[K::k1 + decltype(A)::value]);
-            });
-        if constexpr (DY)
-            static_for<0, K::d2>([&](auto B) {
-                if constexpr (K::COL2(decltype(B)::value)) opaque(dya[K::k2 + decltype(B)::value]);
-            });
-        __builtin_amdgcn_sched_barrier(0);
+            if constexpr (DY) flush_y(std::integral_constant<int, k2>{}, dyb);
+        }
     });
 }
 
@@ -464,16 +479,15 @@ __device__ __forceinline__ double dpp_quad(double v)
     return __hiloint2double(hi, lo);
 }
 
-// Sum of v[k] over the 64 lanes of a wave, for every k < D (D <= 16), through
-// a per-wave LDS tile red[D][64]: each lane stores its D partials, lane 4k+q
-// adds red[k][16q .. 16q+15], and a quad exchange (DPP) completes the sum.
-// Returns the total of component lane/4 in lanes with lane%4 == 0.
+// Sum over the 64 lanes of a wave of the per-wave LDS tile red[D][64]
+// (D <= 16; row k holds every lane's partial of component k, written by the
+// caller): lane 4k+q adds red[k][16q .. 16q+15], and a quad exchange (DPP)
+// completes the sum.  Returns the total of component lane/4 in lanes with
+// lane%4 == 0.
 template <int D>
-__device__ __forceinline__ double wave_sum_lds(const double (&v)[D], double* __restrict__ red, int lane)
+__device__ __forceinline__ double wave_sum_tile(const double* __restrict__ red, int lane)
 {
     static_assert(D <= 16, "at most 16 components");
-#pragma unroll
-    for (int k = 0; k < D; ++k) red[k * 64 + lane] = v[k];
     __builtin_amdgcn_wave_barrier();
     const int k = lane >> 2, q = lane & 3;
     double s = 0.0;
@@ -543,32 +557,35 @@ __global__ void __launch_bounds__(256, (Tune<LIN, C>::bwd_occ)) k_conv_bwd(int32
         }
         q = qn;
         if (!cur.ok) return;
-        double yv[DSH], dya[DSH];
+        double yv[DSH];
         edge_sh<DSH, LPE>(cur.y, yv);
+        float* dwp = dW + (int64_t)cur.e * (P * C) + ch;
+        if constexpr (kLdsSum) {
+            // grad_Y partials go to this wave's LDS tile degree by degree
+            double* tile = lds + (tid >> 6) * (DSH * 64);
+            bwd_slice<Tb, C, DX, DW, DY>(cur.w, cur.g, yv, xv, dxa, dwp, [&](auto K2, const auto& dyb) {
+                constexpr int k2 = decltype(K2)::value;
 #pragma unroll
-        for (int k = 0; k < DSH; ++k) dya[k] = 0.0;
-        bwd_slice<Tb, C, DX, DW, DY>(cur.w, cur.g, yv, xv, dxa, dW + (int64_t)cur.e * (P * C) + ch, dya);
-        if constexpr (DY) {
-            if constexpr (kLdsSum) {
-                const double t = wave_sum_lds<DSH>(dya, lds + (tid >> 6) * (DSH * 64), lane);
-                if ((lane & 3) == 0 && (lane >> 2) < DSH) {
-                    if constexpr (H == 1) dY[(int64_t)cur.e * DSH + (lane >> 2)] = (float)t;
-                    else gv.dyp[((int64_t)cur.e * H + ps.h) * DSH + (lane >> 2)] = t;
-                }
-            } else {
+                for (int b = 0; b < (int)(sizeof(dyb) / sizeof(double)); ++b) tile[(k2 + b) * 64 + lane] = dyb[b];
+            });
+            const double t = wave_sum_tile<DSH>(tile, lane);
+            if ((lane & 3) == 0 && (lane >> 2) < DSH) {
+                if constexpr (H == 1) dY[(int64_t)cur.e * DSH + (lane >> 2)] = (float)t;
+                else gv.dyp[((int64_t)cur.e * H + ps.h) * DSH + (lane >> 2)] = t;
+            }
+        } else {
+            // an edge spans LPE < 64 lanes: reduce each degree's partials over them
+            float* yp = dY + (int64_t)cur.e * DSH;
+            bwd_slice<Tb, C, DX, DW, DY>(cur.w, cur.g, yv, xv, dxa, dwp, [&](auto K2, const auto& dyb) {
+                constexpr int k2 = decltype(K2)::value;
 #pragma unroll
-                for (int k = 0; k < DSH; ++k) {
-                    double v = dya[k];
+                for (int b = 0; b < (int)(sizeof(dyb) / sizeof(double)); ++b) {
+                    double v = dyb[b];
 #pragma unroll
                     for (int off = 1; off < LPE; off <<= 1) v += __shfl_xor(v, off, 64);
-                    dya[k] = v;
+                    if (ps.cl == 0) yp[k2 + b] = (float)v;
                 }
-                if (ps.cl == 0) {
-                    float* yp = dY + (int64_t)cur.e * DSH;
-#pragma unroll
-                    for (int k = 0; k < DSH; ++k) yp[k] = (float)dya[k];
-                }
-            }
+            });
         }
     };
     BwdEdge<Tb> ea, eb;
