@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="extra untimed warm-up, in seconds of sustained load, after the --warmup steps")
     ap.add_argument("--workload", default="layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -191,6 +193,16 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # The GPU raises its clocks only after ~0.1-0.2 s of sustained load; keep
+    # warming up (untimed) until the load has lasted `--settle` seconds so the
+    # timed steps see the loaded clock state a continuous training loop runs in.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(10):
+            step()
+        settle_steps += 10
+        torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -231,6 +243,7 @@ def main():
         "config": {
             "workload": w.name, "n_atoms": N, "n_edges": E, "l_max": L, "channels": C, "paths": P,
             "storage": "f32", "step": "sh + graph_prepare + conv_fwd + conv_bwd(dx, dW, dY)",
+            "settle_s": args.settle, "settle_steps": settle_steps,
             "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
             "fwd_bwd_edges_per_s": E / ((fwd_ms + bwd_ms) * 1e-3),
             "step_alg_gbs": step_bytes / (ms_step * 1e-3) / 1e9,

@@ -296,6 +296,27 @@ def test_conv_ragged_small(torch_dev, oracle, L, C):
     assert np.all(dx[no_out] == 0)
 
 
+@pytest.mark.parametrize("L,C", [(1, 8), (1, 128), (2, 16), (2, 64), (2, 128)])
+def test_conv_forward_many_nodes(torch_dev, oracle, L, C):
+    """A grid many rounds of resident blocks deep, with short ragged segments
+    and receivers without in-edges, for every lane mapping (C < 64, = 64, > 64)."""
+    torch, dev = torch_dev
+    from clebsch_gordan_tensor_cgtp_amd.ops import Plan
+    rng = np.random.default_rng(L * 77 + C)
+    N = 5000
+    degs = rng.integers(0, 7, size=N)
+    g = synth.random_graph(N, degs, seed=L * 31 + C)
+    x, W, G = synth.make_tensors_numpy(N, g.n_edges, L, C, seed=4)
+    Y = oracle.sh(L, g.r).astype(np.float32)
+    _log(f"[many nodes] L={L} C={C} N={N} E={g.n_edges}")
+    plan = Plan(L, L, L, C)
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    rp, sr = T(g.row_ptr), T(g.src)
+    ws = plan.graph_prepare(rp, sr)
+    out = plan.conv_fwd(rp, sr, T(x), T(Y), T(W), ws).cpu().numpy()
+    assert_parity(out, oracle.conv_fwd(L, L, L, g.row_ptr, g.src, x, Y, W), "out")
+
+
 def test_conv_empty_graph(torch_dev, oracle):
     torch, dev = torch_dev
     from clebsch_gordan_tensor_cgtp_amd.ops import Plan
