@@ -292,7 +292,7 @@ __global__ void __launch_bounds__(256, (Tune<LIN, C>::fwd_occ)) k_conv_fwd(int32
 {
     using Tb = cgmath::Tables<LIN, LSH, LOUT>;
     using Gm = Geo<C>;
-    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH, DOUT = Tb::DOUT, S = Gm::S;
+    constexpr int DSH = Tb::DSH, DOUT = Tb::DOUT, S = Gm::S;
     constexpr bool kPf = Tune<LIN, C>::fwd_prefetch;
     // LDS: the streams' partial sums [stream][k][channel]
     __shared__ double red[S * DOUT * C];
@@ -521,7 +521,6 @@ __global__ void __launch_bounds__(256, (Tune<LIN, C>::bwd_occ)) k_conv_bwd(int32
     constexpr bool kPf = Tune<LIN, C>::bwd_prefetch;
     // LDS: per-wave grad_Y transpose tiles during the edge loop, then the
     // streams' grad_x partials
-    constexpr int DOUT = Tb::DOUT;
     constexpr bool kLdsSum = DY && LPE == 64;
     constexpr int kTiles = kLdsSum ? 4 * DSH * 64 : 0;
     constexpr int kDx = DX ? S * DIN * C : 0;
