@@ -664,6 +664,16 @@ constexpr KernelSet make_set()
                      &launch_fwd<L, L, L, C>, &launch_bwd<L, L, L, C>};
 }
 
+// the convolution kernels of one (L, C) without the SH launcher, for a
+// translation unit of its own (the SH kernel is instantiated once per degree
+// by the degree's registry)
+template <int L, int C>
+constexpr KernelSet make_conv_set()
+{
+    return KernelSet{L, L, L, C, Geo<C>::H > 1 ? Geo<C>::H * (L + 1) * (L + 1) : 0, nullptr,
+                     &launch_fwd<L, L, L, C>, &launch_bwd<L, L, L, C>};
+}
+
 template <int LIN, int LSH, int LOUT>
 static bool copy_table(int path, double* dense)
 {

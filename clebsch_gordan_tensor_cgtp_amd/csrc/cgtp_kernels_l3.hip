@@ -1,18 +1,26 @@
-// cgtp_kernels_l3.hip -- degree-3 specialisations (features, SH and outputs l = 0..3).
+// cgtp_kernels_l3.hip -- degree-3 registry (features, SH and outputs l = 0..3).
+// The convolution kernels of each channel count are compiled in a translation
+// unit of their own (cgtp_kernels_l3_c<C>.hip) so the builds run in parallel.
 #include "cgtp_kernels.h"
 
 namespace cgtp {
 
-static const KernelSet kSets[] = {
-    make_set<3, 8>(),
-    make_set<3, 16>(),
-    make_set<3, 32>(),
-    make_set<3, 64>(),
-};
+KernelSet conv_set_l3_c8();
+KernelSet conv_set_l3_c16();
+KernelSet conv_set_l3_c32();
+KernelSet conv_set_l3_c64();
+
+static KernelSet with_sh(KernelSet k)
+{
+    k.sh = &launch_sh<3>;
+    return k;
+}
 
 const KernelSet* kernels_l3(int channels)
 {
-    for (const KernelSet& k : kSets)
+    static const KernelSet sets[] = {with_sh(conv_set_l3_c8()), with_sh(conv_set_l3_c16()),
+                                     with_sh(conv_set_l3_c32()), with_sh(conv_set_l3_c64())};
+    for (const KernelSet& k : sets)
         if (k.channels == channels) return &k;
     return nullptr;
 }
