@@ -41,6 +41,10 @@ def _load():
     lib.orc_paths.argtypes = [ctypes.c_int] * 3 + [_ip]
     lib.orc_sh.restype = None
     lib.orc_sh.argtypes = [ctypes.c_int, ctypes.c_int64, _dp, _dp]
+    lib.orc_sh_bwd.restype = None
+    lib.orc_sh_bwd.argtypes = [ctypes.c_int, ctypes.c_int64, _dp, _dp, _dp]
+    lib.orc_node_grad.restype = None
+    lib.orc_node_grad.argtypes = [ctypes.c_int64, ctypes.c_int64, _i64p, _i64p, _dp, _dp]
     lib.orc_conv_fwd.restype = ctypes.c_int
     lib.orc_conv_fwd.argtypes = [ctypes.c_int] * 4 + [ctypes.c_int64] * 2 + [_i64p, _i64p] + [_dp] * 4
     lib.orc_conv_bwd.restype = ctypes.c_int
@@ -108,6 +112,27 @@ def sh(L, r):
     if E:
         _load().orc_sh(L, E, _p(r), _p(Y))
     return Y
+
+
+def sh_bwd(L, r, dY):
+    """Gradient of <dY, Y(r)> with respect to the edge vectors: [E][3]."""
+    r = _f64(r).reshape(-1, 3)
+    E = r.shape[0]
+    dY = _f64(dY).reshape(E, (L + 1) ** 2)
+    dr = np.zeros((E, 3))
+    if E:
+        _load().orc_sh_bwd(L, E, _p(r), _p(dY), _p(dr))
+    return dr
+
+
+def node_grad(row_ptr, src, dr):
+    """Per-node gradient [N][3] from per-edge gradients of r = pos[src] - pos[dst]."""
+    row_ptr, src = _i64(row_ptr), _i64(src)
+    N, E = row_ptr.shape[0] - 1, src.shape[0]
+    dr = _f64(dr).reshape(E, 3)
+    dpos = np.zeros((N, 3))
+    _load().orc_node_grad(N, E, _p(row_ptr, _i64p), _p(src, _i64p), _p(dr), _p(dpos))
+    return dpos
 
 
 def conv_fwd(l_in, l_sh, l_out, row_ptr, src, x, Y, W):
