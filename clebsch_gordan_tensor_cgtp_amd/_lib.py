@@ -22,6 +22,7 @@ CGTP_ERR_HIP = -4
 CGTP_ERR_ALLOC = -5
 CGTP_ERR_GRAPH = -6
 CGTP_FLAG_VALIDATE = 1
+CGTP_FLAG_NO_LOCALITY = 2
 
 _c_i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -36,6 +37,8 @@ SIGNATURES = {
     "cgtp_plan_export_cg": (ctypes.c_int, [_vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]),
     "cgtp_workspace_size": (ctypes.c_int, [_vp, _c_i64, _c_i64, ctypes.POINTER(ctypes.c_size_t)]),
     "cgtp_sh_fwd": (ctypes.c_int, [_vp, _c_i64, _vp, _vp, _vp]),
+    "cgtp_sh_bwd": (ctypes.c_int, [_vp, _c_i64, _vp, _vp, _vp, _vp]),
+    "cgtp_node_grad": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "cgtp_graph_prepare": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "cgtp_conv_fwd": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                      _vp]),

@@ -14,10 +14,11 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcgtp.so")
 BUILD = os.path.join(ROOT, "_build")
 
-# the degree-3 kernels are split by channel count: one translation unit each
-# compiles in about two minutes, all of them in one would take about ten
-SOURCES = ["cgtp_kernels_l3_c64.hip", "cgtp_kernels_l3_c32.hip", "cgtp_kernels_l3_c16.hip", "cgtp_kernels_l3_c8.hip",
-           "cgtp_kernels_l2.hip", "cgtp_kernels_l1.hip", "cgtp_kernels_l3.hip", "cgtp_graph.hip", "cgtp_api.cpp"]
+# the degree-3 kernels are split by lane geometry, one translation unit each,
+# so the slowest compiles run in parallel (longest first)
+SOURCES = ["cgtp_kernels_l3_c128.hip", "cgtp_kernels_l3_c64.hip", "cgtp_kernels_l3_c32.hip",
+           "cgtp_kernels_l3_c16.hip", "cgtp_kernels_l3_c8.hip", "cgtp_kernels_l2_wide.hip", "cgtp_kernels_l2.hip",
+           "cgtp_kernels_l1.hip", "cgtp_registry.hip", "cgtp_graph.hip", "cgtp_forces.hip", "cgtp_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [

@@ -1,5 +1,6 @@
 // cgtp_api.cpp -- the C ABI of libcgtp.so (see include/cgtp.h): plans,
-// argument checks, workspace sizing and dispatch to the gfx950 kernels.
+// argument checks, workspace sizing and records, and dispatch to the gfx950
+// kernels.
 #include "cgtp.h"
 
 #include <hip/hip_runtime.h>
@@ -7,7 +8,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+#include <mutex>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "cgtp_internal.h"
@@ -17,13 +21,21 @@ struct cgtp_plan_s {
     int l_in, l_sh, l_out, channels;
     unsigned flags;
     int P, d_in, d_sh, d_out;
-    std::vector<int> paths;  // [P][3]
+    int lm;                         // compiled degree serving this plan
+    bool sub;                       // degrees other than (lm, lm, lm)
+    std::vector<int> paths;         // [P][3]
+    std::vector<int> super_index;   // [P]: index of each path in the compiled degree's path list
+    cgtp::Shape shape;              // N and E filled in per call
     const cgtp::KernelSet* ks;
+    cgtp::ShLaunch sh;
+    cgtp::ShBwdLaunch sh_bwd;
 };
 
 namespace {
 
-bool aligned8(const void* p) { return ((uintptr_t)p & 7u) == 0; }
+constexpr unsigned kKnownFlags = CGTP_FLAG_VALIDATE | CGTP_FLAG_NO_LOCALITY;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 cgtp_status_t hip_status(hipError_t e) { return e == hipSuccess ? CGTP_OK : CGTP_ERR_HIP; }
 
@@ -48,18 +60,79 @@ cgtp_status_t check_graph_args(const cgtp_plan_s* plan, int64_t N, int64_t E, co
 {
     if (!plan) return CGTP_ERR_INVALID_ARG;
     if (N < 0 || E < 0 || N >= (int64_t)INT32_MAX || E >= (int64_t)INT32_MAX) return CGTP_ERR_INVALID_ARG;
-    if (!row_ptr) return CGTP_ERR_INVALID_ARG;
-    if (E > 0 && !src) return CGTP_ERR_INVALID_ARG;
+    if (!row_ptr || !aligned16(row_ptr)) return CGTP_ERR_INVALID_ARG;
+    if (E > 0 && (!src || !aligned16(src))) return CGTP_ERR_INVALID_ARG;
     if (plan->flags & CGTP_FLAG_VALIDATE) return validate_graph(N, E, row_ptr, src);
     return CGTP_OK;
 }
 
-cgtp_status_t check_ws(const cgtp_plan_s* plan, int64_t N, int64_t E, const void* ws, size_t ws_bytes)
+cgtp_status_t check_ws(int64_t N, int64_t E, const void* ws, size_t ws_bytes)
 {
-    const cgtp::WsLayout L = cgtp::ws_layout(N, E, plan->ks->dyp_per_edge);
-    if (!ws || ws_bytes < L.total) return CGTP_ERR_WORKSPACE;
+    if (!ws || ws_bytes < cgtp::ws_layout(N, E).total) return CGTP_ERR_WORKSPACE;
     if (((uintptr_t)ws & 255u) != 0) return CGTP_ERR_INVALID_ARG;
     return CGTP_OK;
+}
+
+// ---- records of prepared workspaces -----------------------------------------
+// A workspace counts as prepared for a graph when the last preparation into
+// it (on the same device) was for the same sizes and graph arrays and the
+// same schedule kind.
+struct Prepared {
+    int64_t N, E;
+    const void* row_ptr;
+    const void* src;
+    bool locality;
+    int device;
+};
+
+std::mutex g_mu;
+std::unordered_map<const void*, Prepared>& records()
+{
+    static std::unordered_map<const void*, Prepared> m;
+    return m;
+}
+
+cgtp_status_t prepare_into(const cgtp_plan_s* plan, int64_t N, int64_t E, const int32_t* row_ptr,
+                           const int32_t* src, void* ws, hipStream_t stream)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CGTP_ERR_HIP;
+    const bool loc = !(plan->flags & CGTP_FLAG_NO_LOCALITY);
+    const hipError_t e = cgtp::launch_graph_prepare((int32_t)N, (int32_t)E, row_ptr, src, ws, loc, stream);
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (e != hipSuccess) {
+        records().erase(ws);
+        return CGTP_ERR_HIP;
+    }
+    records()[ws] = Prepared{N, E, row_ptr, src, loc, dev};
+    return CGTP_OK;
+}
+
+// run the preparation unless `ws` already holds this graph's view
+cgtp_status_t ensure_prepared(const cgtp_plan_s* plan, int64_t N, int64_t E, const int32_t* row_ptr,
+                              const int32_t* src, void* ws, hipStream_t stream)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CGTP_ERR_HIP;
+    const bool loc = !(plan->flags & CGTP_FLAG_NO_LOCALITY);
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = records().find(ws);
+        if (it != records().end()) {
+            const Prepared& r = it->second;
+            if (r.N == N && r.E == E && r.row_ptr == row_ptr && r.src == src && r.locality == loc && r.device == dev)
+                return CGTP_OK;
+        }
+    }
+    return prepare_into(plan, N, E, row_ptr, src, ws, stream);
+}
+
+cgtp::Shape launch_shape(const cgtp_plan_s* plan, int64_t N, int64_t E)
+{
+    cgtp::Shape s = plan->shape;
+    s.N = (int32_t)N;
+    s.E = (int32_t)E;
+    return s;
 }
 
 }  // namespace
@@ -71,9 +144,14 @@ cgtp_status_t cgtp_plan_create(cgtp_plan_t* plan, int l_in, int l_sh, int l_out,
     if (!plan) return CGTP_ERR_INVALID_ARG;
     *plan = nullptr;
     if (l_in < 0 || l_sh < 0 || l_out < 0 || channels <= 0) return CGTP_ERR_INVALID_ARG;
-    if (flags & ~CGTP_FLAG_VALIDATE) return CGTP_ERR_INVALID_ARG;
-    const cgtp::KernelSet* ks = cgtp::find_kernels(l_in, l_sh, l_out, channels);
-    if (!ks) return CGTP_ERR_UNSUPPORTED;
+    if (flags & ~kKnownFlags) return CGTP_ERR_INVALID_ARG;
+    if (l_in > cgtp::cgmath::kMaxL || l_sh > cgtp::cgmath::kMaxL || l_out > cgtp::cgmath::kMaxL)
+        return CGTP_ERR_UNSUPPORTED;
+    const int lm = std::max(1, std::max(l_in, std::max(l_sh, l_out)));
+    const cgtp::KernelSet* ks = cgtp::find_kernels(lm, channels);
+    const cgtp::ShLaunch sh = cgtp::find_sh(l_sh);
+    const cgtp::ShBwdLaunch sh_bwd = cgtp::find_sh_bwd(l_sh);
+    if (!ks || !sh || !sh_bwd) return CGTP_ERR_UNSUPPORTED;
     cgtp_plan_s* p = new (std::nothrow) cgtp_plan_s();
     if (!p) return CGTP_ERR_ALLOC;
     p->l_in = l_in;
@@ -81,6 +159,8 @@ cgtp_status_t cgtp_plan_create(cgtp_plan_t* plan, int l_in, int l_sh, int l_out,
     p->l_out = l_out;
     p->channels = channels;
     p->flags = flags;
+    p->lm = lm;
+    p->sub = !(l_in == lm && l_sh == lm && l_out == lm);
     p->P = cgtp::cgmath::num_paths(l_in, l_sh, l_out);
     p->d_in = (l_in + 1) * (l_in + 1);
     p->d_sh = (l_sh + 1) * (l_sh + 1);
@@ -92,7 +172,29 @@ cgtp_status_t cgtp_plan_create(cgtp_plan_t* plan, int l_in, int l_sh, int l_out,
         p->paths[3 * q + 1] = t.l2;
         p->paths[3 * q + 2] = t.l3;
     }
+    // the compiled degree's paths this plan has, and where each one's weights sit
+    cgtp::Shape s{};
+    s.C = channels;
+    s.d_in = p->d_in;
+    s.d_sh = p->d_sh;
+    s.d_out = p->d_out;
+    s.P = p->P;
+    const int Pm = cgtp::cgmath::num_paths(lm, lm, lm);
+    int q = 0;
+    for (int k = 0; k < Pm; ++k) {
+        const cgtp::cgmath::Path t = cgtp::cgmath::path_at(lm, lm, lm, k);
+        const bool mine = t.l1 <= l_in && t.l2 <= l_sh && t.l3 <= l_out;
+        if (mine) {
+            s.active |= uint64_t(1) << k;
+            p->super_index.push_back(k);
+        }
+        s.woff[k] = std::min(q, p->P - 1) * channels;  // an inactive path reads a valid row (weight 0)
+        if (mine) ++q;
+    }
+    p->shape = s;
     p->ks = ks;
+    p->sh = sh;
+    p->sh_bwd = sh_bwd;
     *plan = p;
     return CGTP_OK;
 }
@@ -118,14 +220,13 @@ cgtp_status_t cgtp_plan_info(cgtp_plan_t plan, int* num_paths, int* paths_l1l2l3
 cgtp_status_t cgtp_plan_export_cg(cgtp_plan_t plan, int path, double* dense)
 {
     if (!plan || !dense || path < 0 || path >= plan->P) return CGTP_ERR_INVALID_ARG;
-    return cgtp::host_cg_table(plan->l_in, plan->l_sh, plan->l_out, path, dense) ? CGTP_OK
-                                                                                   : CGTP_ERR_UNSUPPORTED;
+    return cgtp::host_cg_table(plan->lm, plan->super_index[(size_t)path], dense) ? CGTP_OK : CGTP_ERR_UNSUPPORTED;
 }
 
 cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, size_t* bytes)
 {
     if (!plan || !bytes || n_nodes < 0 || n_edges < 0) return CGTP_ERR_INVALID_ARG;
-    *bytes = cgtp::ws_layout(n_nodes, n_edges, plan->ks->dyp_per_edge).total;
+    *bytes = cgtp::ws_layout(n_nodes, n_edges).total;
     return CGTP_OK;
 }
 
@@ -133,8 +234,40 @@ cgtp_status_t cgtp_sh_fwd(cgtp_plan_t plan, int64_t n_edges, const float* r, flo
 {
     if (!plan || n_edges < 0) return CGTP_ERR_INVALID_ARG;
     if (n_edges == 0) return CGTP_OK;
-    if (!r || !Y || !aligned8(Y) || ((uintptr_t)r & 3u)) return CGTP_ERR_INVALID_ARG;
-    return hip_status(plan->ks->sh(n_edges, r, Y, stream));
+    if (!r || !Y || !aligned16(Y) || !aligned16(r)) return CGTP_ERR_INVALID_ARG;
+    return hip_status(plan->sh(n_edges, r, Y, stream));
+}
+
+cgtp_status_t cgtp_sh_bwd(cgtp_plan_t plan, int64_t n_edges, const float* r, const float* grad_Y, float* grad_r,
+                          hipStream_t stream)
+{
+    if (!plan || n_edges < 0) return CGTP_ERR_INVALID_ARG;
+    if (n_edges == 0) return CGTP_OK;
+    if (!r || !grad_Y || !grad_r || !aligned16(r) || !aligned16(grad_Y) || !aligned16(grad_r))
+        return CGTP_ERR_INVALID_ARG;
+    return hip_status(plan->sh_bwd(n_edges, r, grad_Y, grad_r, stream));
+}
+
+cgtp_status_t cgtp_node_grad(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
+                             const int32_t* src, const float* grad_r, float* grad_pos, void* ws, size_t ws_bytes,
+                             hipStream_t stream)
+{
+    cgtp_status_t st = check_graph_args(plan, n_nodes, n_edges, row_ptr, src);
+    if (st != CGTP_OK) return st;
+    st = check_ws(n_nodes, n_edges, ws, ws_bytes);
+    if (st != CGTP_OK) return st;
+    if (n_nodes == 0) return CGTP_OK;
+    if (!grad_pos || !aligned16(grad_pos)) return CGTP_ERR_INVALID_ARG;
+    if (n_edges > 0 && (!grad_r || !aligned16(grad_r))) return CGTP_ERR_INVALID_ARG;
+    st = ensure_prepared(plan, n_nodes, n_edges, row_ptr, src, ws, stream);
+    if (st != CGTP_OK) return st;
+    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges);
+    const char* base = (const char*)ws;
+    const cgtp::GraphView g{(const int32_t*)(base + L.srow), (const int32_t*)(base + L.perm),
+                            (const int32_t*)(base + L.sdst), (const int32_t*)(base + L.rorder),
+                            (const int32_t*)(base + L.sorder)};
+    return hip_status(
+        cgtp::launch_node_grad((int32_t)n_nodes, (int32_t)n_edges, row_ptr, g, grad_r, grad_pos, stream));
 }
 
 cgtp_status_t cgtp_graph_prepare(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
@@ -142,25 +275,35 @@ cgtp_status_t cgtp_graph_prepare(cgtp_plan_t plan, int64_t n_nodes, int64_t n_ed
 {
     cgtp_status_t st = check_graph_args(plan, n_nodes, n_edges, row_ptr, src);
     if (st != CGTP_OK) return st;
-    st = check_ws(plan, n_nodes, n_edges, ws, ws_bytes);
+    st = check_ws(n_nodes, n_edges, ws, ws_bytes);
     if (st != CGTP_OK) return st;
-    return hip_status(cgtp::launch_graph_prepare((int32_t)n_nodes, (int32_t)n_edges, row_ptr, src, ws, stream));
+    return prepare_into(plan, n_nodes, n_edges, row_ptr, src, ws, stream);
 }
 
 cgtp_status_t cgtp_conv_fwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
                             const int32_t* src, const float* x, const float* Y, const float* W, float* out,
-                            const void* ws, size_t ws_bytes, hipStream_t stream)
+                            void* ws, size_t ws_bytes, hipStream_t stream)
 {
     cgtp_status_t st = check_graph_args(plan, n_nodes, n_edges, row_ptr, src);
     if (st != CGTP_OK) return st;
-    st = check_ws(plan, n_nodes, n_edges, ws, ws_bytes);
+    st = check_ws(n_nodes, n_edges, ws, ws_bytes);
     if (st != CGTP_OK) return st;
     if (n_nodes == 0) return CGTP_OK;
-    if (!out || !aligned8(out) || !x || !aligned8(x)) return CGTP_ERR_INVALID_ARG;
-    if (n_edges > 0 && (!Y || !W || !aligned8(W) || ((uintptr_t)Y & 3u))) return CGTP_ERR_INVALID_ARG;
-    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges, plan->ks->dyp_per_edge);
-    const int32_t* rorder = (const int32_t*)((const char*)ws + L.rorder);
-    return hip_status(plan->ks->fwd((int32_t)n_nodes, row_ptr, src, rorder, x, Y, W, out, stream));
+    if (!out || !aligned16(out) || !x || !aligned16(x)) return CGTP_ERR_INVALID_ARG;
+    if (n_edges > 0 && (!Y || !W || !aligned16(W) || !aligned16(Y))) return CGTP_ERR_INVALID_ARG;
+    st = ensure_prepared(plan, n_nodes, n_edges, row_ptr, src, ws, stream);
+    if (st != CGTP_OK) return st;
+    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges);
+    cgtp::FwdArgs a{};
+    a.sh = launch_shape(plan, n_nodes, n_edges);
+    a.row_ptr = row_ptr;
+    a.src = src;
+    a.rorder = (const int32_t*)((const char*)ws + L.rorder);
+    a.x = x;
+    a.Y = Y;
+    a.W = W;
+    a.out = out;
+    return hip_status(plan->ks->fwd[plan->sub ? 1 : 0](a, stream));
 }
 
 cgtp_status_t cgtp_conv_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
@@ -170,22 +313,31 @@ cgtp_status_t cgtp_conv_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
 {
     cgtp_status_t st = check_graph_args(plan, n_nodes, n_edges, row_ptr, src);
     if (st != CGTP_OK) return st;
-    st = check_ws(plan, n_nodes, n_edges, ws, ws_bytes);
+    st = check_ws(n_nodes, n_edges, ws, ws_bytes);
     if (st != CGTP_OK) return st;
-    int mask = (grad_x ? cgtp::kGradX : 0) | (grad_W ? cgtp::kGradW : 0) | (grad_Y ? cgtp::kGradY : 0);
-    if (mask == 0 || n_nodes == 0) return CGTP_OK;
-    if (!x || !aligned8(x) || !grad_out || !aligned8(grad_out)) return CGTP_ERR_INVALID_ARG;
-    if (grad_x && !aligned8(grad_x)) return CGTP_ERR_INVALID_ARG;
-    if (n_edges > 0 && (!Y || !W || !aligned8(W) || ((uintptr_t)Y & 3u))) return CGTP_ERR_INVALID_ARG;
-    if (grad_W && !aligned8(grad_W)) return CGTP_ERR_INVALID_ARG;
-    if (grad_Y && ((uintptr_t)grad_Y & 3u)) return CGTP_ERR_INVALID_ARG;
-    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges, plan->ks->dyp_per_edge);
-    char* base = (char*)ws;
-    cgtp::GraphView g{(const int32_t*)(base + L.srow), (const int32_t*)(base + L.perm),
-                      (const int32_t*)(base + L.sdst), (const int32_t*)(base + L.sorder),
-                      (double*)(base + L.dyp), (int32_t)n_edges};
-    return hip_status(
-        plan->ks->bwd((int32_t)n_nodes, g, x, Y, W, grad_out, grad_x, grad_W, grad_Y, mask, stream));
+    if ((!grad_x && !grad_W && !grad_Y) || n_nodes == 0) return CGTP_OK;
+    if (!x || !aligned16(x) || !grad_out || !aligned16(grad_out)) return CGTP_ERR_INVALID_ARG;
+    if (grad_x && !aligned16(grad_x)) return CGTP_ERR_INVALID_ARG;
+    if (n_edges > 0 && (!Y || !W || !aligned16(W) || !aligned16(Y))) return CGTP_ERR_INVALID_ARG;
+    if (grad_W && !aligned16(grad_W)) return CGTP_ERR_INVALID_ARG;
+    if (grad_Y && !aligned16(grad_Y)) return CGTP_ERR_INVALID_ARG;
+    st = ensure_prepared(plan, n_nodes, n_edges, row_ptr, src, ws, stream);
+    if (st != CGTP_OK) return st;
+    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges);
+    const char* base = (const char*)ws;
+    cgtp::BwdArgs a{};
+    a.sh = launch_shape(plan, n_nodes, n_edges);
+    a.g = cgtp::GraphView{(const int32_t*)(base + L.srow), (const int32_t*)(base + L.perm),
+                          (const int32_t*)(base + L.sdst), (const int32_t*)(base + L.rorder),
+                          (const int32_t*)(base + L.sorder)};
+    a.x = x;
+    a.Y = Y;
+    a.W = W;
+    a.G = grad_out;
+    a.dx = grad_x;
+    a.dW = grad_W;
+    a.dY = grad_Y;
+    return hip_status(plan->ks->bwd[plan->sub ? 1 : 0](a, stream));
 }
 
 const char* cgtp_status_string(cgtp_status_t status)

@@ -1,33 +1,86 @@
-// cgtp_graph.hip -- graph preparation (sender-sorted view of the receiver CSR)
-// and the registry of compiled kernel specialisations.
+// cgtp_graph.hip -- graph preparation: the sender-sorted view of the receiver
+// CSR that the backward walks, and the block schedules of both convolution
+// kernels.
+//
+// The view is the stable counting sort of the edges by sender (per sender,
+// edges in ascending id), so the backward's grad_x sums run in a fixed order.
+//
+// The schedules decide which node each block of a convolution launch serves.
+// Blocks are dealt to the eight XCDs in turn (block b runs on XCD b % 8) and
+// each XCD has its own L2, so the nodes are split into eight ranges of
+// ceil(N/8), range x served by the blocks b = x, x+8, x+16, ...  A range
+// should be a compact piece of the atomic system, so that the rows its blocks
+// gather (x_j in the forward, grad_out_i in the backward) are shared through
+// that XCD's L2 instead of fetched again by every XCD.  The caller's node ids
+// carry no spatial order, so it is read off the graph itself with two rounds
+// of min-hash clustering: every node draws a pseudo-random key, key1(i) is
+// the smallest key in the closed neighbourhood of i, and the cluster centre
+// of i is the node holding the smallest key1 over the closed neighbourhood
+// of i (nodes within two hops share it).  Nodes are ordered by centre and cut
+// into the eight ranges; inside a range the blocks run longest segment first
+// so the last blocks to start are short.  The order only schedules blocks:
+// every output row has one writer and a fixed summation order, so results do
+// not depend on it (the placement inside a cluster and a degree bin comes from
+// integer atomics and may differ between runs).
 #include <hip/hip_runtime.h>
 
+#include <limits.h>
 #include <stdint.h>
 
 #include "cgtp_internal.h"
 
 namespace cgtp {
 
-// ----------------------------------------------------------------------------
-// graph preparation: sender-sorted view of the receiver CSR
-// ----------------------------------------------------------------------------
-// zero the padded per-sender counters and cursors
-__global__ void __launch_bounds__(256) k_zero_counters(int32_t n, int32_t* __restrict__ cnt,
-                                                        int32_t* __restrict__ cursor)
+namespace {
+
+__device__ __forceinline__ int32_t clampi(int32_t v, int32_t lo, int32_t hi)
 {
-    const int32_t t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (t < n) {
-        cnt[(int64_t)t * kCounterStride] = 0;
-        cursor[(int64_t)t * kCounterStride] = 0;
-    }
+    return v < lo ? lo : (v > hi ? hi : v);
 }
 
-constexpr int kDegBins = 1024;  // degrees at or above kDegBins-1 share the first bin
+// a sender id outside [0, N) breaks the CSR contract; it is read as node 0 so
+// every count and index below stays in range
+__device__ __forceinline__ int32_t valid_node(int32_t j, int32_t N) { return (uint32_t)j < (uint32_t)N ? j : 0; }
+
+// segment [e0, e1) of receiver i, clamped to [0, E]
+__device__ __forceinline__ void segment(const int32_t* __restrict__ row_ptr, int32_t i, int32_t E, int32_t& e0,
+                                        int32_t& e1)
+{
+    e0 = clampi(row_ptr[i], 0, E);
+    e1 = clampi(row_ptr[i + 1], e0, E);
+}
+
+// pseudo-random 32-bit key of node j (an invertible multiply / xor-shift
+// mix), paired with j so keys are distinct and ties cannot occur
+__device__ __forceinline__ uint64_t node_key(int32_t j)
+{
+    uint32_t h = (uint32_t)j * 0x9E3779B1u;
+    h ^= h >> 15;
+    h *= 0x85EBCA77u;
+    h ^= h >> 13;
+    return ((uint64_t)h << 32) | (uint32_t)j;
+}
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, off, 64);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), off, 64);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o < v ? o : v;
+    }
+    return v;
+}
+
+constexpr int kDegBins = 1024;  // in-range order bins; degrees >= kDegBins-1 share the first bin
+
+__device__ __forceinline__ int deg_bin(int32_t d) { return kDegBins - 1 - (d < kDegBins - 1 ? d : kDegBins - 1); }
 
 // Inclusive prefix sum of one value per thread over a 1024-thread block:
 // shuffle scans inside each wave, then the 16 wave totals.  `tot` is LDS
-// scratch of 16 ints; ends with a barrier.
-__device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* tot)
+// scratch of 16 ints; *total receives the block's sum.  Ends with a barrier.
+__device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* tot, int32_t* total)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -37,114 +90,212 @@ __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* tot)
     }
     if (lane == 63) tot[w] = v;
     __syncthreads();
-    int32_t base = 0;
-    for (int k = 0; k < w; ++k) base += tot[k];
+    int32_t base = 0, all = 0;
+    for (int k = 0; k < 16; ++k) {
+        base += k < w ? tot[k] : 0;
+        all += tot[k];
+    }
     __syncthreads();  // tot may be reused after this
+    *total = all;
     return v + base;
 }
 
-// Sender offsets and block orders, run by one block of 1024 threads, each
-// owning a contiguous chunk of nodes:
-//   srow[0] = 0, srow[j+1] = srow[j] + cnt[j]  (sender offsets);
-//   rorder / sorder: nodes ordered by in-degree / out-degree, longest first, so
-//   the convolution kernels start the longest segments first (ties in any
-//   order: the order only schedules blocks, every output has a fixed sum order).
-__device__ void offsets_and_orders(int32_t N, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ cnt,
-                                   int32_t* __restrict__ srow, int32_t* __restrict__ rorder,
-                                   int32_t* __restrict__ sorder)
+}  // namespace
+
+// Step 1, one wave per receiver i: clear i's counters (used from step 2 on)
+// and, for the clustered schedule, key1(i) = min node_key over i and its
+// senders.
+__global__ void __launch_bounds__(256) k_prep_keys(int32_t N, int32_t E, const int32_t* __restrict__ row_ptr,
+                                                    const int32_t* __restrict__ src, int32_t locality,
+                                                    uint64_t* __restrict__ key1, int32_t* __restrict__ cnt,
+                                                    int32_t* __restrict__ cursor, int32_t* __restrict__ ccnt)
 {
-    __shared__ int32_t hin[kDegBins], hout[kDegBins], tot[16];
+    const int32_t i = (int32_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (i >= N) return;
+    if (lane == 0) {
+        cnt[(int64_t)i * kCounterStride] = 0;
+        cursor[(int64_t)i * kCounterStride] = 0;
+        ccnt[i] = 0;
+    }
+    if (!locality) return;
+    int32_t e0, e1;
+    segment(row_ptr, i, E, e0, e1);
+    uint64_t m = node_key(i);
+    for (int32_t e = e0 + lane; e < e1; e += 64) {
+        const uint64_t k = node_key(valid_node(src[e], N));
+        m = k < m ? k : m;
+    }
+    m = wave_min_u64(m);
+    if (lane == 0) key1[i] = m;
+}
+
+// Step 2, one wave per receiver i: its cluster centre and its rank inside
+// the cluster (integer atomics), and the out-degree count of every sender.
+__global__ void __launch_bounds__(256) k_prep_centers(int32_t N, int32_t E, const int32_t* __restrict__ row_ptr,
+                                                       const int32_t* __restrict__ src, int32_t locality,
+                                                       const uint64_t* __restrict__ key1, int32_t* __restrict__ center,
+                                                       int32_t* __restrict__ crank, int32_t* ccnt, int32_t* cnt)
+{
+    const int32_t i = (int32_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (i >= N) return;
+    int32_t e0, e1;
+    segment(row_ptr, i, E, e0, e1);
+    int32_t c = i;
+    if (locality) {
+        uint64_t m = key1[i];
+        for (int32_t e = e0 + lane; e < e1; e += 64) {
+            const uint64_t k = key1[valid_node(src[e], N)];
+            m = k < m ? k : m;
+        }
+        c = (int32_t)(uint32_t)wave_min_u64(m);
+    }
+    if (lane == 0) {
+        center[i] = c;
+        crank[i] = atomicAdd(&ccnt[c], 1);
+    }
+    for (int32_t e = e0 + lane; e < e1; e += 64) atomicAdd(&cnt[(int64_t)valid_node(src[e], N) * kCounterStride], 1);
+}
+
+// Step 3, one block of 1024 threads: the sender offsets srow (prefix sum of
+// the out-degrees), the cluster offsets, and the two block schedules.
+// Node i's place in the cluster order is g = coff[centre] + rank; its range
+// is x = g / Q; inside a range the nodes go longest first by LDS histograms of
+// (range, degree bin).
+__global__ void __launch_bounds__(1024) k_prep_orders(int32_t N, int32_t E, const int32_t* __restrict__ row_ptr,
+                                                       const int32_t* __restrict__ cnt, const int32_t* __restrict__ ccnt,
+                                                       const int32_t* __restrict__ center,
+                                                       const int32_t* __restrict__ crank, int32_t* __restrict__ srow,
+                                                       int32_t* __restrict__ coff, int32_t* __restrict__ rorder,
+                                                       int32_t* __restrict__ sorder)
+{
+    __shared__ int32_t hin[kXcds][kDegBins], hout[kXcds][kDegBins], tot[16];
     const int t = threadIdx.x;
-    const int32_t chunk = (N + 1023) / 1024;
-    const int32_t b = t * chunk;
-    const int32_t end = b + chunk < N ? b + chunk : N;
-    auto bin = [](int32_t deg) { return kDegBins - 1 - (deg < kDegBins - 1 ? deg : kDegBins - 1); };
-    hin[t] = 0;
-    hout[t] = 0;
-    __syncthreads();
-    // one pass: this chunk's out-degree total and both degree histograms
-    int32_t s = 0;
-    for (int32_t j = b; j < end; ++j) {
-        const int32_t c = cnt[(int64_t)j * kCounterStride];
-        s += c;
-        atomicAdd(&hin[bin(row_ptr[j + 1] - row_ptr[j])], 1);
-        atomicAdd(&hout[bin(c)], 1);
-    }
-    __syncthreads();  // histograms complete before they are scanned
-    const int32_t run0 = block_scan_1024(s, tot) - s;  // exclusive prefix of this chunk
-    const int32_t hi = hin[t], ho = hout[t];
-    const int32_t hi_incl = block_scan_1024(hi, tot), ho_incl = block_scan_1024(ho, tot);
-    hin[t] = hi_incl - hi;  // exclusive bin starts
-    hout[t] = ho_incl - ho;
-    __syncthreads();
-    int32_t run = run0;
     if (t == 0) srow[0] = 0;
-    for (int32_t j = b; j < end; ++j) {
-        const int32_t c = cnt[(int64_t)j * kCounterStride];
-        run += c;
-        srow[j + 1] = run;
-        rorder[atomicAdd(&hin[bin(row_ptr[j + 1] - row_ptr[j])], 1)] = j;
-        sorder[atomicAdd(&hout[bin(c)], 1)] = j;
+    if (N == 0) return;
+    const int32_t Q = (N + kXcds - 1) / kXcds;
+    // prefix sums, a tile of 1024 nodes at a time
+    int32_t carry_o = 0, carry_c = 0;
+    for (int32_t base = 0; base < N; base += 1024) {
+        const int32_t i = base + t;
+        const int32_t co = i < N ? cnt[(int64_t)i * kCounterStride] : 0;
+        const int32_t cc = i < N ? ccnt[i] : 0;
+        int32_t to, tc;
+        const int32_t io = block_scan_1024(co, tot, &to);
+        const int32_t ic = block_scan_1024(cc, tot, &tc);
+        if (i < N) {
+            srow[i + 1] = carry_o + io;
+            coff[i] = carry_c + ic - cc;
+        }
+        carry_o += to;
+        carry_c += tc;
+    }
+    for (int k = t; k < kXcds * kDegBins; k += 1024) {
+        (&hin[0][0])[k] = 0;
+        (&hout[0][0])[k] = 0;
+    }
+    __syncthreads();  // srow and coff (global) and the cleared histograms are visible block-wide
+    auto place = [&](int32_t i, int32_t& x, int& bi, int& bo) {
+        int32_t g = coff[clampi(center[i], 0, N - 1)] + crank[i];
+        g = clampi(g, 0, N - 1);
+        x = g / Q;
+        int32_t e0 = clampi(row_ptr[i], 0, E), e1 = clampi(row_ptr[i + 1], e0, E);
+        bi = deg_bin(e1 - e0);
+        bo = deg_bin(srow[i + 1] - srow[i]);
+    };
+    for (int32_t i = t; i < N; i += 1024) {
+        int32_t x;
+        int bi, bo;
+        place(i, x, bi, bo);
+        atomicAdd(&hin[x][bi], 1);
+        atomicAdd(&hout[x][bo], 1);
+    }
+    __syncthreads();
+    // exclusive bin starts inside each range (one bin per thread)
+    for (int x = 0; x < kXcds; ++x) {
+        int32_t tt;
+        const int32_t vi = hin[x][t], vo = hout[x][t];
+        const int32_t si = block_scan_1024(vi, tot, &tt) - vi;
+        const int32_t so = block_scan_1024(vo, tot, &tt) - vo;
+        hin[x][t] = si;
+        hout[x][t] = so;
+    }
+    __syncthreads();
+    for (int32_t i = t; i < N; i += 1024) {
+        int32_t x;
+        int bi, bo;
+        place(i, x, bi, bo);
+        rorder[x + kXcds * atomicAdd(&hin[x][bi], 1)] = i;
+        sorder[x + kXcds * atomicAdd(&hout[x][bo], 1)] = i;
+    }
+    // blocks past the end of a short range are idle
+    for (int32_t b = t; b < kXcds * Q; b += 1024) {
+        const int32_t x = b % kXcds, s = b / kXcds;
+        const int32_t nx = clampi(N - x * Q, 0, Q);
+        if (s >= nx) {
+            rorder[b] = -1;
+            sorder[b] = -1;
+        }
     }
 }
 
-// out-degree histogram (integer atomics: the counts do not depend on order)
-__global__ void __launch_bounds__(256) k_outdeg(int32_t E, const int32_t* __restrict__ src, int32_t* cnt)
-{
-    const int32_t e = blockIdx.x * blockDim.x + threadIdx.x;
-    if (e < E) atomicAdd(&cnt[(int64_t)src[e] * kCounterStride], 1);
-}
-
-// sender offsets and block orders: a single block of 1024 threads
-__global__ void __launch_bounds__(1024) k_offsets(int32_t N, const int32_t* __restrict__ row_ptr,
-                                                   const int32_t* __restrict__ cnt, int32_t* __restrict__ srow,
-                                                   int32_t* __restrict__ rorder, int32_t* __restrict__ sorder)
-{
-    offsets_and_orders(N, row_ptr, cnt, srow, rorder, sorder);
-}
-
-// Place every edge in its sender's bucket (arbitrary order within a bucket),
-// one wave per receiver, recording the receiver beside the edge.
-__global__ void __launch_bounds__(256) k_scatter(int32_t N, const int32_t* __restrict__ row_ptr,
-                                                  const int32_t* __restrict__ src, const int32_t* __restrict__ srow,
-                                                  int32_t* cursor, int32_t* __restrict__ perm,
-                                                  int32_t* __restrict__ sdst)
+// Step 4, one wave per receiver i: place every in-edge of i in its sender's
+// bucket of the unsorted view (arbitrary order inside a bucket), with i
+// beside it.
+__global__ void __launch_bounds__(256) k_prep_scatter(int32_t N, int32_t E, const int32_t* __restrict__ row_ptr,
+                                                       const int32_t* __restrict__ src, const int32_t* __restrict__ srow,
+                                                       int32_t* cursor, int32_t* __restrict__ uperm,
+                                                       int32_t* __restrict__ usdst)
 {
     const int32_t i = (int32_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (i >= N) return;
-    const int32_t end = row_ptr[i + 1];
-    for (int32_t e = row_ptr[i] + (threadIdx.x & 63); e < end; e += 64) {
-        const int32_t j = src[e];
+    int32_t e0, e1;
+    segment(row_ptr, i, E, e0, e1);
+    for (int32_t e = e0 + (threadIdx.x & 63); e < e1; e += 64) {
+        const int32_t j = valid_node(src[e], N);
         const int32_t k = srow[j] + atomicAdd(&cursor[(int64_t)j * kCounterStride], 1);
-        perm[k] = e;
-        sdst[k] = i;
+        if ((uint32_t)k < (uint32_t)E) {
+            uperm[k] = e;
+            usdst[k] = i;
+        }
     }
 }
 
-constexpr int kBucketLds = 1024;  // bucket entries a wave sorts in LDS
+constexpr int kBucketLds = 1024;  // bucket entries a wave ranks in one LDS tile
 
-// One wave per sender: order its bucket's (edge, receiver) pairs by edge id,
-// so the view is the stable counting sort of the edges by sender.  Buckets up
-// to kBucketLds are ranked in LDS (edge ids are distinct, so rank = number of
-// smaller ids); longer ones fall back to a serial insertion sort by lane 0.
-__global__ void __launch_bounds__(256) k_sort_buckets(int32_t N, const int32_t* __restrict__ srow,
-                                                       int32_t* __restrict__ perm, int32_t* __restrict__ sdst)
+// Order this wave's LDS writes before its lanes read what other lanes wrote.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Step 5, one wave per sender j: write j's bucket of the view ordered by edge
+// id (edge ids are distinct, so an entry's place is the number of smaller
+// ids in the bucket).  A bucket of up to kBucketLds entries is ranked against
+// itself in LDS; a longer one (a hub) ranks each 1024-entry chunk against the
+// whole bucket one LDS tile at a time, O(n^2/64) steps per wave.
+__global__ void __launch_bounds__(256) k_prep_sort(int32_t N, int32_t E, const int32_t* __restrict__ srow,
+                                                    const int32_t* __restrict__ uperm,
+                                                    const int32_t* __restrict__ usdst, int32_t* __restrict__ perm,
+                                                    int32_t* __restrict__ sdst)
 {
     __shared__ int32_t ebuf[4][kBucketLds], ibuf[4][kBucketLds];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int32_t j = (int32_t)blockIdx.x * 4 + w;
     if (j >= N) return;  // whole wave; no block-level barrier below
-    const int32_t b = srow[j], n = srow[j + 1] - b;
+    const int32_t b = clampi(srow[j], 0, E);
+    const int32_t n = clampi(srow[j + 1], b, E) - b;
+    int32_t* se = ebuf[w];
     if (n <= kBucketLds) {
-        int32_t* se = ebuf[w];
         int32_t* si = ibuf[w];
         for (int32_t k = lane; k < n; k += 64) {
-            se[k] = perm[b + k];
-            si[k] = sdst[b + k];
+            se[k] = uperm[b + k];
+            si[k] = usdst[b + k];
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_lds_sync();
         for (int32_t k = lane; k < n; k += 64) {
             const int32_t v = se[k];
             int32_t rank = 0;
@@ -154,77 +305,62 @@ __global__ void __launch_bounds__(256) k_sort_buckets(int32_t N, const int32_t* 
         }
         return;
     }
-    if (lane == 0) {
-        int32_t* a = perm + b;
-        int32_t* r = sdst + b;
-        for (int32_t q = 1; q < n; ++q) {
-            const int32_t v = a[q], vr = r[q];
-            int32_t p = q - 1;
-            while (p >= 0 && a[p] > v) {
-                a[p + 1] = a[p];
-                r[p + 1] = r[p];
-                --p;
+    constexpr int kPer = kBucketLds / 64;  // entries of a chunk per lane
+    for (int32_t c = 0; c < n; c += kBucketLds) {
+        int32_t v[kPer], r[kPer], rank[kPer];
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            const int32_t idx = c + lane + 64 * t;
+            v[t] = idx < n ? uperm[b + idx] : INT_MAX;
+            r[t] = idx < n ? usdst[b + idx] : 0;
+            rank[t] = 0;
+        }
+        for (int32_t c2 = 0; c2 < n; c2 += kBucketLds) {
+            const int32_t m = n - c2 < kBucketLds ? n - c2 : kBucketLds;
+            wave_lds_sync();  // the previous tile's reads are done
+            for (int32_t k = lane; k < m; k += 64) se[k] = uperm[b + c2 + k];
+            wave_lds_sync();
+            for (int32_t u = 0; u < m; ++u) {
+                const int32_t y = se[u];
+#pragma unroll
+                for (int t = 0; t < kPer; ++t) rank[t] += y < v[t] ? 1 : 0;
             }
-            a[p + 1] = v;
-            r[p + 1] = vr;
+        }
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            const int32_t idx = c + lane + 64 * t;
+            if (idx < n && (uint32_t)rank[t] < (uint32_t)n) {
+                perm[b + rank[t]] = v[t];
+                sdst[b + rank[t]] = r[t];
+            }
         }
     }
 }
 
 hipError_t launch_graph_prepare(int32_t N, int32_t E, const int32_t* row_ptr, const int32_t* src, void* ws,
-                                hipStream_t s)
+                                bool locality, hipStream_t s)
 {
     const WsLayout L = ws_layout(N, E);
     char* base = (char*)ws;
-    int32_t* srow = (int32_t*)(base + L.srow);
-    int32_t* perm = (int32_t*)(base + L.perm);
-    int32_t* sdst = (int32_t*)(base + L.sdst);
-    int32_t* cnt = (int32_t*)(base + L.cnt);
-    int32_t* cursor = (int32_t*)(base + L.cursor);
-    int32_t* rorder = (int32_t*)(base + L.rorder);
-    int32_t* sorder = (int32_t*)(base + L.sorder);
-    const unsigned bN = (unsigned)((N + 255) / 256), bE = (unsigned)((E + 255) / 256);
-    if (N > 0) hipLaunchKernelGGL(k_zero_counters, dim3(bN), dim3(256), 0, s, N, cnt, cursor);
-    if (E > 0) hipLaunchKernelGGL(k_outdeg, dim3(bE), dim3(256), 0, s, E, src, cnt);
-    hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, s, N, row_ptr, cnt, srow, rorder, sorder);
+    auto at = [&](size_t off) { return (int32_t*)(base + off); };
+    int32_t *srow = at(L.srow), *perm = at(L.perm), *sdst = at(L.sdst), *uperm = at(L.uperm), *usdst = at(L.usdst);
+    int32_t *cnt = at(L.cnt), *cursor = at(L.cursor), *center = at(L.center), *crank = at(L.crank);
+    int32_t *ccnt = at(L.ccnt), *coff = at(L.coff), *rorder = at(L.rorder), *sorder = at(L.sorder);
+    uint64_t* key1 = (uint64_t*)(base + L.key1);
+    const unsigned b4 = (unsigned)((N + 3) / 4);
+    const int32_t loc = locality ? 1 : 0;
+    if (N > 0) {
+        hipLaunchKernelGGL(k_prep_keys, dim3(b4), dim3(256), 0, s, N, E, row_ptr, src, loc, key1, cnt, cursor, ccnt);
+        hipLaunchKernelGGL(k_prep_centers, dim3(b4), dim3(256), 0, s, N, E, row_ptr, src, loc, key1, center, crank,
+                           ccnt, cnt);
+    }
+    hipLaunchKernelGGL(k_prep_orders, dim3(1), dim3(1024), 0, s, N, E, row_ptr, cnt, ccnt, center, crank, srow, coff,
+                       rorder, sorder);
     if (E > 0 && N > 0) {
-        const unsigned b4 = (unsigned)((N + 3) / 4);
-        hipLaunchKernelGGL(k_scatter, dim3(b4), dim3(256), 0, s, N, row_ptr, src, srow, cursor, perm, sdst);
-        hipLaunchKernelGGL(k_sort_buckets, dim3(b4), dim3(256), 0, s, N, srow, perm, sdst);
+        hipLaunchKernelGGL(k_prep_scatter, dim3(b4), dim3(256), 0, s, N, E, row_ptr, src, srow, cursor, uperm, usdst);
+        hipLaunchKernelGGL(k_prep_sort, dim3(b4), dim3(256), 0, s, N, E, srow, uperm, usdst, perm, sdst);
     }
     return hipGetLastError();
-}
-
-// ----------------------------------------------------------------------------
-// registry
-// ----------------------------------------------------------------------------
-const KernelSet* kernels_l1(int channels);
-const KernelSet* kernels_l2(int channels);
-const KernelSet* kernels_l3(int channels);
-bool table_l1(int path, double* dense);
-bool table_l2(int path, double* dense);
-bool table_l3(int path, double* dense);
-
-const KernelSet* find_kernels(int l_in, int l_sh, int l_out, int channels)
-{
-    if (l_in != l_sh || l_sh != l_out) return nullptr;
-    switch (l_in) {
-        case 1: return kernels_l1(channels);
-        case 2: return kernels_l2(channels);
-        case 3: return kernels_l3(channels);
-        default: return nullptr;
-    }
-}
-
-bool host_cg_table(int l_in, int l_sh, int l_out, int path, double* dense)
-{
-    if (l_in != l_sh || l_sh != l_out) return false;
-    switch (l_in) {
-        case 1: return table_l1(path, dense);
-        case 2: return table_l2(path, dense);
-        case 3: return table_l3(path, dense);
-        default: return false;
-    }
 }
 
 }  // namespace cgtp

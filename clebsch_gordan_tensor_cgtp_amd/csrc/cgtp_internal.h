@@ -1,4 +1,5 @@
-// cgtp_internal.h -- launcher table shared by the C-ABI layer and the kernels.
+// cgtp_internal.h -- workspace layout, kernel arguments and the launcher
+// table shared by the C-ABI layer, the graph preparation and the kernels.
 #pragma once
 
 #include <stddef.h>
@@ -8,9 +9,16 @@
 
 namespace cgtp {
 
-// Byte offsets of the sender-sorted graph view inside the workspace.
+// Blocks of one launch are dealt to the chip's eight XCDs in turn (block b
+// runs on XCD b % 8), each XCD with its own L2.
+constexpr int kXcds = 8;
+
+// Largest path count of any compiled degree set (l_in = l_sh = l_out = 3).
+constexpr int kMaxPaths = 34;
+
+// Byte offsets of the graph view inside the caller's workspace.
 struct WsLayout {
-    size_t srow, perm, sdst, cnt, cursor, rorder, sorder, dyp, total;
+    size_t srow, perm, sdst, uperm, usdst, cnt, cursor, key1, center, crank, ccnt, coff, rorder, sorder, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -20,66 +28,120 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // shared lines
 constexpr int kCounterStride = 32;
 
-// dyp_per_edge: fp64 values per edge of the grad_Y slice partials (0 when the
-// plan's channels fit one 64-lane slice)
-inline WsLayout ws_layout(int64_t N, int64_t E, int64_t dyp_per_edge = 0)
+// grid size of the convolution kernels: the nodes are split into kXcds
+// contiguous ranges of ceil(N / kXcds) (see the block orders below)
+inline int64_t conv_grid(int64_t N) { return kXcds * ((N + kXcds - 1) / kXcds); }
+
+inline WsLayout ws_layout(int64_t N, int64_t E)
 {
     WsLayout w{};
+    const size_t n1 = (size_t)(N > 0 ? N : 1), e1 = (size_t)(E > 0 ? E : 1);
+    const size_t grid = (size_t)(conv_grid(N) > 0 ? conv_grid(N) : 1);
     size_t o = 0;
-    w.srow = o;
-    o += align256(sizeof(int32_t) * (size_t)(N + 1));
-    w.perm = o;
-    o += align256(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
-    w.sdst = o;
-    o += align256(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
-    w.cnt = o;
-    o += align256(sizeof(int32_t) * kCounterStride * (size_t)(N > 0 ? N : 1));
-    w.cursor = o;
-    o += align256(sizeof(int32_t) * kCounterStride * (size_t)(N > 0 ? N : 1));
-    w.rorder = o;
-    o += align256(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
-    w.sorder = o;
-    o += align256(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
-    w.dyp = o;
-    o += align256(sizeof(double) * (size_t)(E > 0 ? E : 0) * (size_t)dyp_per_edge);
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += align256(bytes);
+        return at;
+    };
+    w.srow = take(sizeof(int32_t) * (n1 + 1));
+    w.perm = take(sizeof(int32_t) * e1);
+    w.sdst = take(sizeof(int32_t) * e1);
+    w.uperm = take(sizeof(int32_t) * e1);  // the view before its buckets are sorted
+    w.usdst = take(sizeof(int32_t) * e1);
+    w.cnt = take(sizeof(int32_t) * kCounterStride * n1);
+    w.cursor = take(sizeof(int32_t) * kCounterStride * n1);
+    w.key1 = take(sizeof(uint64_t) * n1);
+    w.center = take(sizeof(int32_t) * n1);
+    w.crank = take(sizeof(int32_t) * n1);
+    w.ccnt = take(sizeof(int32_t) * n1);
+    w.coff = take(sizeof(int32_t) * n1);
+    w.rorder = take(sizeof(int32_t) * grid);
+    w.sorder = take(sizeof(int32_t) * grid);
     w.total = o;
     return w;
 }
 
+// The sender-sorted view of the receiver CSR and the block schedules.
 struct GraphView {
     const int32_t* srow;    // [N+1] sender offsets
-    const int32_t* perm;    // [E]  edge ids grouped by sender
+    const int32_t* perm;    // [E]  edge ids grouped by sender, ascending within a sender
     const int32_t* sdst;    // [E]  receiver of perm[k]
-    const int32_t* sorder;  // [N]  senders, longest out-edge list first
-    double* dyp;            // [E][H][D_sh] grad_Y slice partials (C > 64 only)
-    int32_t n_edges;        // E
+    const int32_t* rorder;  // [conv_grid(N)] receiver of each forward block (-1: idle block)
+    const int32_t* sorder;  // [conv_grid(N)] sender of each backward block (-1: idle block)
+};
+
+// Degrees and channel count of a launch.  The kernels are compiled for the
+// full path set of degree LM (l_in = l_sh = l_out = LM); a plan with smaller
+// degrees runs the paths it has (bit p of `active`) and reads its weight row
+// p at element offset woff[p] (a multiple of C) inside the edge's [P][C] row.
+struct Shape {
+    int32_t N, E, C;
+    int32_t d_in, d_sh, d_out;  // (l+1)^2 of the plan's degrees
+    int32_t P;                  // the plan's path count
+    uint64_t active;            // compiled paths the plan uses
+    int32_t woff[kMaxPaths];    // weight offset of every compiled path (clamped for inactive ones)
 };
 
 enum GradMask : int { kGradX = 1, kGradW = 2, kGradY = 4 };
 
-using ShLaunch = hipError_t (*)(int64_t E, const float* r, float* Y, hipStream_t s);
-using FwdLaunch = hipError_t (*)(int32_t N, const int32_t* row_ptr, const int32_t* src, const int32_t* rorder,
-                                 const float* x, const float* Y, const float* W, float* out, hipStream_t s);
-using BwdLaunch = hipError_t (*)(int32_t N, GraphView g, const float* x, const float* Y, const float* W,
-                                 const float* G, float* dx, float* dW, float* dY, int mask, hipStream_t s);
-
-struct KernelSet {
-    int l_in, l_sh, l_out, channels;
-    int dyp_per_edge;  // workspace fp64 values per edge for grad_Y slice partials
-    ShLaunch sh;
-    FwdLaunch fwd;
-    BwdLaunch bwd;
+struct FwdArgs {
+    Shape sh;
+    const int32_t* row_ptr;
+    const int32_t* src;
+    const int32_t* rorder;
+    const float* x;
+    const float* Y;
+    const float* W;
+    float* out;
 };
 
-// Kernels compiled for (l_in, l_sh, l_out, C), or nullptr.
-const KernelSet* find_kernels(int l_in, int l_sh, int l_out, int channels);
+struct BwdArgs {
+    Shape sh;
+    GraphView g;
+    const float* x;
+    const float* Y;
+    const float* W;
+    const float* G;
+    float* dx;
+    float* dW;
+    float* dY;
+};
 
-// Graph preparation into `ws` (layout ws_layout(N, E)).
+using ShLaunch = hipError_t (*)(int64_t E, const float* r, float* Y, hipStream_t s);
+using FwdLaunch = hipError_t (*)(const FwdArgs& a, hipStream_t s);
+using BwdLaunch = hipError_t (*)(const BwdArgs& a, hipStream_t s);
+
+// The kernels of one compiled degree LM and one lane geometry: LPE lanes per
+// edge slice and H slices (waves) per edge; they serve every channel count C
+// with LPE*(H-1) < C <= LPE*H (lanes beyond C idle).
+struct KernelSet {
+    int lm, lpe, h;
+    FwdLaunch fwd[2];  // [0]: complete degree set; [1]: SUB (smaller or mixed degrees)
+    BwdLaunch bwd[2];
+};
+
+// Kernels for compiled degree lm and channel count C, or nullptr.
+const KernelSet* find_kernels(int lm, int channels);
+
+// Real spherical harmonics of degrees 0..l (l <= 3), or nullptr.
+ShLaunch find_sh(int l);
+
+// Their backward: grad_r[E][3] from grad_Y[E][(l+1)^2] (l <= 3), or nullptr.
+using ShBwdLaunch = hipError_t (*)(int64_t E, const float* r, const float* gY, float* gr, hipStream_t s);
+ShBwdLaunch find_sh_bwd(int l);
+
+// Per-node gradient gpos[N][3] = sum over out-edges of grad_r - sum over
+// in-edges, over the prepared view g.
+hipError_t launch_node_grad(int32_t N, int32_t E, const int32_t* row_ptr, const GraphView& g, const float* gr,
+                            float* gpos, hipStream_t s);
+
+// Graph preparation into `ws` (layout ws_layout(N, E)).  `locality` selects
+// the cluster-ordered block schedule (false: node-id order), see cgtp_graph.hip.
 hipError_t launch_graph_prepare(int32_t N, int32_t E, const int32_t* row_ptr, const int32_t* src, void* ws,
-                                hipStream_t s);
+                                bool locality, hipStream_t s);
 
-// Host copy of the real CG table for a path (the same constexpr tables the
-// kernels are compiled with).
-bool host_cg_table(int l_in, int l_sh, int l_out, int path, double* dense);
+// Host copy of the real CG table of path `path` of the compiled degree lm
+// (the same constexpr tables the kernels are compiled with).
+bool host_cg_table(int lm, int path, double* dense);
 
 }  // namespace cgtp

@@ -1,5 +1,5 @@
-// cgtp_kernels.h -- gfx950 kernels of the CGTP convolution (templates; each
-// cgtp_kernels_l<L>.hip instantiates one degree).
+// cgtp_kernels.h -- gfx950 kernels of the CGTP convolution (templates; the
+// cgtp_kernels_l<L>*.hip units instantiate them).
 //
 // Hot path (the convolution LunaTP's abstract calls the cost centre of
 // equivariant MLIPs; "LunaTP: Enabling Efficient and Scalable Tensor Product
@@ -18,13 +18,22 @@
 // a segment and over channels keep fp64 accuracy, and fp64 FMA issues at the
 // same rate as unpacked fp32 on this chip.
 //
-// Lane mapping: a lane owns one channel of one edge.  For C >= 64 a node's
-// channels are split over C/64 waves (each owning a 64-channel slice of the
-// node's rows); for C < 64 a wave covers 64/C edges of the segment at once and
-// reduces across those edge groups at the end.  The CG values and their
-// nonzero pattern are compile-time constants of the (L_in, L_sh, L_out)
-// specialisation, so every contraction below is a straight line of fp64 FMAs
-// over the nonzero coefficients only.
+// Lane mapping: a lane owns one channel of one edge.  A kernel is compiled
+// for LPE lanes per edge slice and H slices per edge: for C <= 64 a wave
+// covers 64/LPE edges at once (LPE the smallest power of two >= C); for
+// 64 < C <= 128 a node's channels are split over two waves (H = 2).  The
+// channel count itself is a run-time value; lanes past C load channel 0, take
+// no part in any sum and store nothing.
+//
+// Degrees: each unit is compiled for the complete path set of one degree LM
+// (l_in = l_sh = l_out = LM).  A plan with l_in, l_sh, l_out <= LM, not all
+// equal to LM, runs the SUB variant: it uses the same compiled contraction,
+// gives every path the plan does not have the weight 0 and stores no grad_W
+// for it, and reads feature, SH and output rows of the plan's own widths
+// (components past a width are read at the last valid index and only ever
+// meet a zero weight).  The CG values and their nonzero pattern are
+// compile-time constants, so every contraction below is a straight line of
+// fp64 FMAs over the nonzero coefficients only.
 //
 // Reuse inside an edge ("multi-level reuse" in the LunaTP abstract, done here
 // per channel):
@@ -85,6 +94,31 @@ struct PathK {
     }
 };
 
+__device__ __forceinline__ int32_t clampi(int32_t v, int32_t lo, int32_t hi)
+{
+    return v < lo ? lo : (v > hi ? hi : v);
+}
+
+// element of `row` at byte offset `lb` (a lane's channel times 4): written as
+// a pointer plus a zero-extended 32-bit byte offset so that a row pointer
+// equal in every lane becomes the scalar base of the load or store.  The
+// offset must be defined where it is used (see lane_offset), or the
+// compiler hoists its 64-bit extension and adds it with vector instructions.
+template <class T>
+__device__ __forceinline__ T* at_lane(T* row, uint32_t lb)
+{
+    using B = typename std::conditional<std::is_const<T>::value, const char, char>::type;
+    return (T*)((B*)row + lb);
+}
+
+// the lane's byte offset, re-defined at this point (an empty asm the
+// optimiser cannot see through) for at_lane
+__device__ __forceinline__ uint32_t lane_offset(uint32_t lb)
+{
+    asm volatile("" : "+v"(lb));
+    return lb;
+}
+
 // ----------------------------------------------------------------------------
 // real spherical harmonics (orthonormal, l <= 3), fp64 from fp32 vectors
 // ----------------------------------------------------------------------------
@@ -97,6 +131,7 @@ __global__ void __launch_bounds__(256) k_sh(int64_t E, const float* __restrict__
     const double rx = r[3 * e + 0], ry = r[3 * e + 1], rz = r[3 * e + 2];
     const double n = sqrt(rx * rx + ry * ry + rz * rz);
     const double x = rx / n, y = ry / n, z = rz / n;
+    (void)x, (void)y, (void)z;
     constexpr double pi = 3.14159265358979323846;
     constexpr double c0 = 0.5 * cgmath::csqrt(1.0 / pi);
     double o[D];
@@ -148,49 +183,47 @@ hipError_t launch_sh(int64_t E, const float* r, float* Y, hipStream_t s)
 // ----------------------------------------------------------------------------
 // work decomposition
 // ----------------------------------------------------------------------------
-// One 256-thread block (four waves) per node.  A lane owns one channel of an
-// edge: LPE = min(C, 64) lanes cover a 64-channel slice, and for C > 64 the
-// H = C/64 slices of a node go to different waves, so every wave carries the
-// state of a single slice (the register budget decides occupancy here).  The
-// node's edges are interleaved over the block's S edge streams (stream s takes
-// the node's edges s, s+S, s+2S, ...), which keeps a long segment from
-// serialising on one wave; the streams' partial sums are combined in LDS in a
-// fixed order at the end (atomic-free, deterministic).
-template <int C>
+// One 256-thread block (four waves) per node.  LPE lanes cover a slice of up
+// to LPE channels, and for H = 2 the two slices of a node go to different
+// waves, so every wave carries the state of a single slice (the register
+// budget decides occupancy here).  The node's edges are interleaved over the
+// block's S edge streams (stream s takes the node's edges s, s+S, s+2S, ...),
+// which keeps a long segment from serialising on one wave; the streams'
+// partial sums are combined in LDS in a fixed order at the end (atomic-free,
+// deterministic).
+template <int LPE, int H>
 struct Geo {
-    static_assert(C > 0 && (C & (C - 1)) == 0 && C <= 256, "C must be a power of two <= 256");
-    static constexpr int LPE = C < 64 ? C : 64;      // lanes per edge slice
-    static constexpr int H = C / LPE;                // channel slices (waves) per edge
-    static_assert(H <= 4, "at most four slices per block");
+    static_assert(LPE == 8 || LPE == 16 || LPE == 32 || LPE == 64, "lanes per edge slice");
+    static_assert(H == 1 || (H == 2 && LPE == 64), "two slices only with full waves");
+    static constexpr int CP = LPE * H;               // padded channel count
     static constexpr int S = (4 / H) * (64 / LPE);   // edge streams per block
 };
 
 // position of this thread: channel slice, channel within the slice, stream
-template <int C>
+template <int LPE, int H>
 struct Pos {
     int h, cl, s;
     __device__ __forceinline__ explicit Pos(int tid)
     {
-        using G = Geo<C>;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        h = wave % G::H;
-        cl = (tid & 63) % G::LPE;
-        if constexpr (G::LPE == 64) s = wave / G::H;  // wave-uniform
-        else s = (wave / G::H) * (64 / G::LPE) + (tid & 63) / G::LPE;
+        h = wave % H;
+        cl = (tid & 63) % LPE;
+        if constexpr (LPE == 64) s = wave / H;  // wave-uniform
+        else s = wave * (64 / LPE) + (tid & 63) / LPE;
     }
-    __device__ __forceinline__ int channel() const { return h * Geo<C>::LPE + cl; }
+    __device__ __forceinline__ int channel() const { return h * LPE + cl; }
 };
 
 // Per-specialisation tuning: the minimum waves per SIMD the register
-// allocation must allow, and whether the next edge's operands are loaded
-// before the current edge is computed.  Chosen so that no specialisation
-// spills vector registers (a spill costs far more than the occupancy it buys).
-template <int L, int C>
+// allocation must allow, and whether the forward loads the next edge's
+// operands before the current edge is computed.  Chosen so that no
+// specialisation spills vector registers (a spill costs far more than the
+// occupancy it buys).
+template <int LM, int LPE>
 struct Tune {
-    static constexpr int fwd_occ = L <= 2 ? 4 : 2;
-    static constexpr int bwd_occ = L == 1 || (L == 2 && C >= 64) ? 4 : (L == 2 ? 3 : 2);
-    static constexpr bool fwd_prefetch = L <= 2;
-    static constexpr bool bwd_prefetch = false;
+    static constexpr int fwd_occ = LM <= 2 ? 4 : 2;
+    static constexpr int bwd_occ = LM == 1 || (LM == 2 && LPE == 64) ? 4 : (LM == 2 ? 3 : 2);
+    static constexpr bool fwd_prefetch = LM <= 2;
 };
 
 // An empty asm that takes a register value and hands it back: the optimiser
@@ -220,6 +253,34 @@ __device__ __forceinline__ void edge_sh(const float (&y)[DSH], double (&yv)[DSH]
     }
 }
 
+// Row widths and weight offsets of a launch: compile-time for the complete
+// degree set, run-time (from the Shape) for a SUB plan.
+template <class Tb, bool SUB>
+struct Dims {
+    int32_t d_in, d_sh, d_out, P;
+    __device__ __forceinline__ explicit Dims(const Shape& s)
+    {
+        if constexpr (SUB) {
+            d_in = s.d_in;
+            d_sh = s.d_sh;
+            d_out = s.d_out;
+            P = s.P;
+        } else {
+            d_in = Tb::DIN;
+            d_sh = Tb::DSH;
+            d_out = Tb::DOUT;
+            P = Tb::P;
+        }
+    }
+    // component k of a row of width d (SUB: clamped to the last valid one)
+    template <int k>
+    __device__ __forceinline__ static int32_t comp(int32_t d)
+    {
+        if constexpr (SUB) return k < d ? k : d - 1;
+        else return k;
+    }
+};
+
 // ----------------------------------------------------------------------------
 // forward
 // ----------------------------------------------------------------------------
@@ -229,23 +290,34 @@ struct FwdEdge {
     float w[P], x[DIN], y[DSH];
 };
 
-// operands of edge e for channel ch
-template <class Tb, int C>
-__device__ __forceinline__ void fwd_load(FwdEdge<Tb>& d, int32_t e, int ch, const int32_t* __restrict__ src,
-                                         const float* __restrict__ x, const float* __restrict__ Y,
-                                         const float* __restrict__ W)
+// operands of edge e for the lane at byte offset chl (an in-range channel
+// times 4).  Every row is
+// addressed as a row pointer (uniform when the whole wave works on one edge)
+// plus the lane's channel as an unsigned 32-bit index, which the compiler
+// turns into scalar-base + lane-offset loads without 64-bit vector adds.
+template <class Tb, bool SUB>
+__device__ __forceinline__ void fwd_load(FwdEdge<Tb>& d, int32_t e, uint32_t chl, const FwdArgs& a,
+                                         const Dims<Tb, SUB>& dm)
 {
     constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH;
-    const int32_t j = src[e];
-    const float* wp = W + (int64_t)e * (P * C) + ch;
-#pragma unroll
-    for (int p = 0; p < P; ++p) d.w[p] = __builtin_nontemporal_load(wp + p * C);
-    const float* xp = x + (int64_t)j * (DIN * C) + ch;
-#pragma unroll
-    for (int k = 0; k < DIN; ++k) d.x[k] = xp[k * C];
-    const float* yp = Y + (int64_t)e * DSH;
-#pragma unroll
-    for (int k = 0; k < DSH; ++k) d.y[k] = yp[k];
+    const int32_t C = a.sh.C;
+    chl = lane_offset(chl);
+    int32_t j = a.src[e];
+    j = (uint32_t)j < (uint32_t)a.sh.N ? j : 0;  // a sender outside [0, N) breaks the CSR contract
+    const float* wrow = a.W + (int64_t)e * (dm.P * C);
+    static_for<0, P>([&](auto PI) {
+        constexpr int p = decltype(PI)::value;
+        if constexpr (SUB) {
+            const float v = __builtin_nontemporal_load(at_lane(wrow + a.sh.woff[p], chl));
+            d.w[p] = ((a.sh.active >> p) & 1) ? v : 0.0f;
+        } else {
+            d.w[p] = __builtin_nontemporal_load(at_lane(wrow + p * C, chl));
+        }
+    });
+    const float* xrow = a.x + (int64_t)j * (dm.d_in * C);
+    static_for<0, DIN>([&](auto K) { d.x[K] = *at_lane(xrow + Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_in) * C, chl); });
+    const float* yp = a.Y + (int64_t)e * dm.d_sh;
+    static_for<0, DSH>([&](auto K) { d.y[K] = yp[Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_sh)]; });
 }
 
 // acc[l3,m3] += sum_p W_p sum_{a,b} T_p[a][b][m3] x[l1,a] y[l2,b] for one channel
@@ -281,28 +353,27 @@ __device__ __forceinline__ void fwd_slice(const float (&w)[Tb::P], const float (
     });
 }
 
-template <int LIN, int LSH, int LOUT, int C>
-__global__ void __launch_bounds__(256, (Tune<LIN, C>::fwd_occ)) k_conv_fwd(int32_t N, const int32_t* __restrict__ row_ptr,
-                                                                         const int32_t* __restrict__ src,
-                                                                         const int32_t* __restrict__ rorder,
-                                                                         const float* __restrict__ x,
-                                                                         const float* __restrict__ Y,
-                                                                         const float* __restrict__ W,
-                                                                         float* __restrict__ out)
+template <int LM, int LPE, int H, bool SUB>
+__global__ void __launch_bounds__(256, (Tune<LM, LPE>::fwd_occ)) k_conv_fwd(FwdArgs a)
 {
-    using Tb = cgmath::Tables<LIN, LSH, LOUT>;
-    using Gm = Geo<C>;
-    constexpr int DSH = Tb::DSH, DOUT = Tb::DOUT, S = Gm::S;
-    constexpr bool kPf = Tune<LIN, C>::fwd_prefetch;
+    using Tb = cgmath::Tables<LM, LM, LM>;
+    using Gm = Geo<LPE, H>;
+    constexpr int DSH = Tb::DSH, DOUT = Tb::DOUT, S = Gm::S, CP = Gm::CP;
+    constexpr bool kPf = Tune<LM, LPE>::fwd_prefetch;
     // LDS: the streams' partial sums [stream][k][channel]
-    __shared__ double red[S * DOUT * C];
+    __shared__ double red[S * DOUT * CP];
 
     const int tid = threadIdx.x;
-    const Pos<C> ps(tid);
+    const Pos<LPE, H> ps(tid);
     const int ch = ps.channel();
-    const int32_t i = rorder[blockIdx.x];
-    if ((uint32_t)i >= (uint32_t)N) return;  // unprepared workspace: never index with it
-    const int32_t end = row_ptr[i + 1];
+    const int32_t C = a.sh.C;
+    const uint32_t chl = ch < C ? 4u * ch : 0u;  // byte offset; lanes past C read channel 0 and store nothing
+    const Dims<Tb, SUB> dm(a.sh);
+    const int32_t i = a.rorder[blockIdx.x];
+    if ((uint32_t)i >= (uint32_t)a.sh.N) return;  // idle block (or an unprepared schedule)
+    const int32_t E = a.sh.E;
+    const int32_t e0 = clampi(a.row_ptr[i], 0, E);
+    const int32_t end = clampi(a.row_ptr[i + 1], e0, E);
 
     double acc[DOUT];
 #pragma unroll
@@ -311,19 +382,19 @@ __global__ void __launch_bounds__(256, (Tune<LIN, C>::fwd_occ)) k_conv_fwd(int32
     // with prefetch, the stream's next edge is loaded before the current one
     // is computed (the copy `cur = nxt` costs fewer registers than
     // alternating two named buffers, which would spill at this occupancy)
-    int32_t e = row_ptr[i] + ps.s;
+    int32_t e = e0 + ps.s;
     FwdEdge<Tb> cur;
-    if (kPf && e < end) fwd_load<Tb, C>(cur, e, ch, src, x, Y, W);
+    if (kPf && e < end) fwd_load<Tb, SUB>(cur, e, chl, a, dm);
     while (e < end) {
         const int32_t en = e + S;
         FwdEdge<Tb> nxt;
         if constexpr (kPf) {
-            if (en < end) fwd_load<Tb, C>(nxt, en, ch, src, x, Y, W);
+            if (en < end) fwd_load<Tb, SUB>(nxt, en, chl, a, dm);
         } else {
-            fwd_load<Tb, C>(cur, e, ch, src, x, Y, W);
+            fwd_load<Tb, SUB>(cur, e, chl, a, dm);
         }
         double yv[DSH];
-        edge_sh<DSH, Gm::LPE>(cur.y, yv);
+        edge_sh<DSH, LPE>(cur.y, yv);
         fwd_slice<Tb>(cur.w, cur.x, yv, acc);
         if constexpr (kPf) cur = nxt;
         e = en;
@@ -331,24 +402,25 @@ __global__ void __launch_bounds__(256, (Tune<LIN, C>::fwd_occ)) k_conv_fwd(int32
 
     // combine the streams in a fixed order; out[i] has this block as its only writer
 #pragma unroll
-    for (int k = 0; k < DOUT; ++k) red[(ps.s * DOUT + k) * C + ch] = acc[k];
+    for (int k = 0; k < DOUT; ++k) red[(ps.s * DOUT + k) * CP + ch] = acc[k];
     __syncthreads();
-    float* op = out + (int64_t)i * (DOUT * C);
-    for (int t = tid; t < DOUT * C; t += 256) {
-        double v = 0.0;
+    float* op = a.out + (int64_t)i * (dm.d_out * C);
+    for (int t = tid; t < DOUT * CP; t += 256) {
+        const int k = t / CP, c = t % CP;
+        if (k < dm.d_out && c < C) {
+            double v = 0.0;
 #pragma unroll
-        for (int q = 0; q < S; ++q) v += red[q * DOUT * C + t];
-        op[t] = (float)v;
+            for (int q = 0; q < S; ++q) v += red[q * DOUT * CP + t];
+            op[k * C + c] = (float)v;
+        }
     }
 }
 
-template <int LIN, int LSH, int LOUT, int C>
-hipError_t launch_fwd(int32_t N, const int32_t* row_ptr, const int32_t* src, const int32_t* rorder, const float* x,
-                      const float* Y, const float* W, float* out, hipStream_t s)
+template <int LM, int LPE, int H, bool SUB>
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t s)
 {
-    if (N == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_conv_fwd<LIN, LSH, LOUT, C>), dim3((unsigned)N), dim3(256), 0, s, N, row_ptr, src, rorder,
-                       x, Y, W, out);
+    if (a.sh.N == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_conv_fwd<LM, LPE, H, SUB>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -363,29 +435,36 @@ struct BwdEdge {
     float w[P], g[DOUT], y[DSH];
 };
 
-// operands of the q-th edge of the sender-sorted view for channel ch; a
+// operands of the q-th edge of the sender-sorted view for the lane at byte
+// offset chl; a
 // corrupt entry (possible only if the view was not prepared for this graph)
 // is read as edge 0 / receiver 0 and flagged, never used out of bounds
-template <class Tb, int C>
-__device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, int ch, int32_t N, const GraphView& gv,
-                                         const float* __restrict__ Y, const float* __restrict__ W,
-                                         const float* __restrict__ Gr)
+template <class Tb, bool SUB>
+__device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, uint32_t chl, const BwdArgs& a,
+                                         const Dims<Tb, SUB>& dm)
 {
     constexpr int P = Tb::P, DSH = Tb::DSH, DOUT = Tb::DOUT;
-    int32_t e = gv.perm[q];
-    int32_t i = gv.sdst[q];
-    d.ok = (uint32_t)e < (uint32_t)gv.n_edges && (uint32_t)i < (uint32_t)N;
+    const int32_t C = a.sh.C;
+    chl = lane_offset(chl);
+    int32_t e = a.g.perm[q];
+    int32_t i = a.g.sdst[q];
+    d.ok = (uint32_t)e < (uint32_t)a.sh.E && (uint32_t)i < (uint32_t)a.sh.N;
     if (!d.ok) e = i = 0;
     d.e = e;
-    const float* wp = W + (int64_t)e * (P * C) + ch;
-#pragma unroll
-    for (int p = 0; p < P; ++p) d.w[p] = __builtin_nontemporal_load(wp + p * C);
-    const float* gp = Gr + (int64_t)i * (DOUT * C) + ch;
-#pragma unroll
-    for (int k = 0; k < DOUT; ++k) d.g[k] = gp[k * C];
-    const float* yp = Y + (int64_t)e * DSH;
-#pragma unroll
-    for (int k = 0; k < DSH; ++k) d.y[k] = yp[k];
+    const float* wrow = a.W + (int64_t)e * (dm.P * C);
+    static_for<0, P>([&](auto PI) {
+        constexpr int p = decltype(PI)::value;
+        if constexpr (SUB) {
+            const float v = __builtin_nontemporal_load(at_lane(wrow + a.sh.woff[p], chl));
+            d.w[p] = ((a.sh.active >> p) & 1) ? v : 0.0f;
+        } else {
+            d.w[p] = __builtin_nontemporal_load(at_lane(wrow + p * C, chl));
+        }
+    });
+    const float* grow = a.G + (int64_t)i * (dm.d_out * C);
+    static_for<0, DOUT>([&](auto K) { d.g[K] = *at_lane(grow + Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_out) * C, chl); });
+    const float* yp = a.Y + (int64_t)e * dm.d_sh;
+    static_for<0, DSH>([&](auto K) { d.y[K] = yp[Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_sh)]; });
 }
 
 // One edge of the backward for one channel:
@@ -394,11 +473,12 @@ __device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, int ch, int3
 //   v_p[b] = sum_a R_p[a][b] x[l1,a]   -> dy[l2,b] += W_p v_p[b]
 // The paths are taken grouped by l2, so only one degree's grad_Y partials
 // are live at a time; flush_y(k2, dy) receives each degree's partials
-// (components k2 .. k2+2*l2) as soon as its last path is done.
-template <class Tb, int C, bool DX, bool DW, bool DY, class FlushY>
+// (components k2 .. k2+2*l2) as soon as its last path is done.  store_w(p, v)
+// receives grad_W of path p.
+template <class Tb, class StoreW, class FlushY>
 __device__ __forceinline__ void bwd_slice(const float (&w)[Tb::P], const float (&g)[Tb::DOUT],
                                           const double (&yv)[Tb::DSH], const double (&xv)[Tb::DIN],
-                                          double (&dxa)[Tb::DIN], float* __restrict__ dwp, FlushY&& flush_y)
+                                          double (&dxa)[Tb::DIN], StoreW&& store_w, FlushY&& flush_y)
 {
     constexpr int DOUT = Tb::DOUT;
     double gv[DOUT];
@@ -438,34 +518,31 @@ __device__ __forceinline__ void bwd_slice(const float (&w)[Tb::P], const float (
                                 });
                                 if (any) {
                                     h = __builtin_fma(r, yv[k2 + b], h);
-                                    if constexpr (DY) v[b] = __builtin_fma(r, xv[K::k1 + a], v[b]);
+                                    v[b] = __builtin_fma(r, xv[K::k1 + a], v[b]);
                                 }
                             });
-                            if constexpr (DX) dxa[K::k1 + a] = __builtin_fma(wd, h, dxa[K::k1 + a]);
-                            if constexpr (DW) dw = __builtin_fma(xv[K::k1 + a], h, dw);
+                            dxa[K::k1 + a] = __builtin_fma(wd, h, dxa[K::k1 + a]);
+                            dw = __builtin_fma(xv[K::k1 + a], h, dw);
                         }
                     });
-                    if constexpr (DW) __builtin_nontemporal_store((float)dw, dwp + p * C);
-                    if constexpr (DY)
-                        static_for<0, d2>([&](auto B) {
-                            constexpr int b = decltype(B)::value;
-                            if constexpr (K::COL2(b)) dyb[b] = __builtin_fma(wd, v[b], dyb[b]);
-                        });
+                    store_w(std::integral_constant<int, p>{}, dw);
+                    static_for<0, d2>([&](auto B) {
+                        constexpr int b = decltype(B)::value;
+                        if constexpr (K::COL2(b)) dyb[b] = __builtin_fma(wd, v[b], dyb[b]);
+                    });
                     // Pin this path's accumulator updates here: without it the
                     // compiler sinks every accumulation to the end of the edge
                     // and keeps all paths' h and v values live at once.
-                    if constexpr (DX)
-                        static_for<0, K::d1>([&](auto A) {
-                            if constexpr (K::ROW(decltype(A)::value)) opaque(dxa[K::k1 + decltype(A)::value]);
-                        });
-                    if constexpr (DY)
-                        static_for<0, d2>([&](auto B) {
-                            if constexpr (K::COL2(decltype(B)::value)) opaque(dyb[decltype(B)::value]);
-                        });
+                    static_for<0, K::d1>([&](auto A) {
+                        if constexpr (K::ROW(decltype(A)::value)) opaque(dxa[K::k1 + decltype(A)::value]);
+                    });
+                    static_for<0, d2>([&](auto B) {
+                        if constexpr (K::COL2(decltype(B)::value)) opaque(dyb[decltype(B)::value]);
+                    });
                     __builtin_amdgcn_sched_barrier(0);
                 }
             });
-            if constexpr (DY) flush_y(std::integral_constant<int, k2>{}, dyb);
+            flush_y(std::integral_constant<int, k2>{}, dyb);
         }
     });
 }
@@ -479,16 +556,25 @@ __device__ __forceinline__ double dpp_quad(double v)
     return __hiloint2double(hi, lo);
 }
 
+// Order this wave's LDS writes before its lanes read what other lanes wrote
+// (and, used again afterwards, the reads before the next overwrite).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Sum over the 64 lanes of a wave of the per-wave LDS tile red[D][64]
 // (D <= 16; row k holds every lane's partial of component k, written by the
 // caller): lane 4k+q adds red[k][16q .. 16q+15], and a quad exchange (DPP)
 // completes the sum.  Returns the total of component lane/4 in lanes with
-// lane%4 == 0.
+// lane%4 == 0.  The tile may be overwritten once this returns.
 template <int D>
 __device__ __forceinline__ double wave_sum_tile(const double* __restrict__ red, int lane)
 {
     static_assert(D <= 16, "at most 16 components");
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
     const int k = lane >> 2, q = lane & 3;
     double s = 0.0;
     if (k < D) {
@@ -499,187 +585,179 @@ __device__ __forceinline__ double wave_sum_tile(const double* __restrict__ red, 
 #pragma unroll
         for (int t = 0; t < 8; ++t) s += acc2[t].x + acc2[t].y;
     }
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
     s += dpp_quad<0xB1>(s);  // lanes ^1
     s += dpp_quad<0x4E>(s);  // lanes ^2
     return s;
 }
 
-template <int LIN, int LSH, int LOUT, int C, bool DX, bool DW, bool DY>
-__global__ void __launch_bounds__(256, (Tune<LIN, C>::bwd_occ)) k_conv_bwd(int32_t N, GraphView gv,
-                                                                         const float* __restrict__ x,
-                                                                         const float* __restrict__ Y,
-                                                                         const float* __restrict__ W,
-                                                                         const float* __restrict__ Gr,
-                                                                         float* __restrict__ dx,
-                                                                         float* __restrict__ dW,
-                                                                         float* __restrict__ dY)
+// Edges per stream between two grad_Y combines of the two channel slices of
+// a C > 64 backward block.
+constexpr int kDyChunk = 16;
+
+template <int LM, int LPE, int H, bool SUB>
+__global__ void __launch_bounds__(256, (Tune<LM, LPE>::bwd_occ)) k_conv_bwd(BwdArgs a)
 {
-    using Tb = cgmath::Tables<LIN, LSH, LOUT>;
-    using Gm = Geo<C>;
-    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH, S = Gm::S, LPE = Gm::LPE, H = Gm::H;
-    constexpr bool kPf = Tune<LIN, C>::bwd_prefetch;
-    // LDS: per-wave grad_Y transpose tiles during the edge loop, then the
-    // streams' grad_x partials
-    constexpr bool kLdsSum = DY && LPE == 64;
-    constexpr int kTiles = kLdsSum ? 4 * DSH * 64 : 0;
-    constexpr int kDx = DX ? S * DIN * C : 0;
-    constexpr int kLds = (kTiles > kDx ? kTiles : kDx) > 0 ? (kTiles > kDx ? kTiles : kDx) : 1;
+    using Tb = cgmath::Tables<LM, LM, LM>;
+    using Gm = Geo<LPE, H>;
+    constexpr int DIN = Tb::DIN, DSH = Tb::DSH, S = Gm::S, CP = Gm::CP;
+    constexpr int K = kDyChunk;
+    // LDS: per-wave grad_Y transpose tiles and, for H = 2, the slices'
+    // per-edge grad_Y sums of the current chunk [slice][stream][edge][k]
+    // during the edge loop; the streams' grad_x partials at the end
+    constexpr bool kTile = LPE == 64;
+    constexpr int kTiles = kTile ? 4 * DSH * 64 : 0;
+    constexpr int kDyl = H == 2 ? 2 * S * K * DSH : 0;
+    constexpr int kDx = S * DIN * CP;
+    constexpr int kMain = kTiles + kDyl;
+    constexpr int kLds = kMain > kDx ? kMain : kDx;
     __shared__ double lds[kLds];
+    __shared__ int32_t eslot[H == 2 ? S * K : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const Pos<C> ps(tid);
+    const Pos<LPE, H> ps(tid);
     const int ch = ps.channel();
-    const int32_t j = gv.sorder[blockIdx.x];
-    if ((uint32_t)j >= (uint32_t)N) return;  // unprepared workspace: never index with it
+    const int32_t C = a.sh.C, N = a.sh.N, E = a.sh.E;
+    const bool live = ch < C;
+    const uint32_t chl = live ? 4u * ch : 0u;  // byte offset of the lane's channel
+    // every lane of this wave holds a channel below C (uniform)
+    const bool full_c = C >= (ps.h + 1) * LPE;
+    const Dims<Tb, SUB> dm(a.sh);
+    const bool want_dx = a.dx != nullptr, want_dw = a.dW != nullptr, want_dy = a.dY != nullptr;
+    const int32_t j = a.g.sorder[blockIdx.x];
+    if ((uint32_t)j >= (uint32_t)N) return;  // idle block (or an unprepared schedule)
 
     double xv[DIN], dxa[DIN];
     {
-        const float* xp = x + (int64_t)j * (DIN * C) + ch;
-#pragma unroll
-        for (int k = 0; k < DIN; ++k) {
-            xv[k] = (double)xp[k * C];
-            dxa[k] = 0.0;
-        }
+        const float* xrow = a.x + (int64_t)j * (dm.d_in * C);
+        static_for<0, DIN>([&](auto Kc) {
+            xv[Kc] = (double)*at_lane(xrow + Dims<Tb, SUB>::template comp<decltype(Kc)::value>(dm.d_in) * C, chl);
+            dxa[Kc] = 0.0;
+        });
     }
-    const int32_t end = gv.srow[j + 1];
-    int32_t q = gv.srow[j] + ps.s;
-    // One edge: with prefetch, load the stream's next edge into `nxt` before
-    // computing `cur`.  The loop alternates the two buffers (no copies).
-    auto step = [&](BwdEdge<Tb>& cur, BwdEdge<Tb>& nxt) {
-        const int32_t qn = q + S;
-        if constexpr (kPf) {
-            if (qn < end) bwd_load<Tb, C>(nxt, qn, ch, N, gv, Y, W, Gr);
-        } else {
-            bwd_load<Tb, C>(cur, q, ch, N, gv, Y, W, Gr);
-        }
-        q = qn;
-        if (!cur.ok) return;
-        double yv[DSH];
-        edge_sh<DSH, LPE>(cur.y, yv);
-        float* dwp = dW + (int64_t)cur.e * (P * C) + ch;
-        if constexpr (kLdsSum) {
-            // grad_Y partials go to this wave's LDS tile degree by degree
-            double* tile = lds + (tid >> 6) * (DSH * 64);
-            bwd_slice<Tb, C, DX, DW, DY>(cur.w, cur.g, yv, xv, dxa, dwp, [&](auto K2, const auto& dyb) {
-                constexpr int k2 = decltype(K2)::value;
+    // the sender's range of the view, clamped to the view's bounds
+    const int32_t q0 = clampi(a.g.srow[j], 0, E);
+    const int32_t end = clampi(a.g.srow[j + 1], q0, E);
+    const int32_t T = (end - q0 + S - 1) / S;  // edges per stream (block-uniform bound)
+    double* tile = lds + (tid >> 6) * (DSH * 64);
+    double* dyl = lds + kTiles;
+
+    for (int32_t t0 = 0; t0 < T; t0 += (H == 2 ? K : T)) {
+        const int32_t t1 = H == 2 ? (t0 + K < T ? t0 + K : T) : T;
+        for (int32_t t = t0; t < t1; ++t) {
+            const int32_t q = q0 + ps.s + S * t;
+            if (q >= end) continue;  // uniform over the lanes of one edge
+            BwdEdge<Tb> cur;
+            bwd_load<Tb, SUB>(cur, q, chl, a, dm);
+            if constexpr (H == 2)
+                if (ps.h == 0 && lane == 0) eslot[ps.s * K + (t - t0)] = cur.ok ? cur.e : -1;
+            if (!cur.ok) continue;
+            double yv[DSH];
+            edge_sh<DSH, LPE>(cur.y, yv);
+            float* dwrow = a.dW + (int64_t)cur.e * (dm.P * C);
+            const uint32_t chs = lane_offset(chl);
+            auto store_w = [&](auto PI, double dw) {
+                constexpr int p = decltype(PI)::value;
+                bool keep = want_dw && (full_c || live);
+                if constexpr (SUB) keep = keep && ((a.sh.active >> p) & 1);
+                if (keep) __builtin_nontemporal_store((float)dw, at_lane(dwrow + (SUB ? a.sh.woff[p] : p * C), chs));
+            };
+            if constexpr (kTile) {
+                // grad_Y partials go to this wave's LDS tile degree by degree
+                bwd_slice<Tb>(cur.w, cur.g, yv, xv, dxa, store_w, [&](auto K2, const auto& dyb) {
+                    constexpr int k2 = decltype(K2)::value;
 #pragma unroll
-                for (int b = 0; b < (int)(sizeof(dyb) / sizeof(double)); ++b) tile[(k2 + b) * 64 + lane] = dyb[b];
-            });
-            const double t = wave_sum_tile<DSH>(tile, lane);
-            if ((lane & 3) == 0 && (lane >> 2) < DSH) {
-                if constexpr (H == 1) dY[(int64_t)cur.e * DSH + (lane >> 2)] = (float)t;
-                else gv.dyp[((int64_t)cur.e * H + ps.h) * DSH + (lane >> 2)] = t;
-            }
-        } else {
-            // an edge spans LPE < 64 lanes: reduce each degree's partials over them
-            float* yp = dY + (int64_t)cur.e * DSH;
-            bwd_slice<Tb, C, DX, DW, DY>(cur.w, cur.g, yv, xv, dxa, dwp, [&](auto K2, const auto& dyb) {
-                constexpr int k2 = decltype(K2)::value;
+                    for (int b = 0; b < (int)(sizeof(dyb) / sizeof(double)); ++b)
+                        tile[(k2 + b) * 64 + lane] = dyb[b];
+                });
+                // lanes past C hold channel 0's terms: they leave the sum
+                if (!full_c && !live)
 #pragma unroll
-                for (int b = 0; b < (int)(sizeof(dyb) / sizeof(double)); ++b) {
-                    double v = dyb[b];
-#pragma unroll
-                    for (int off = 1; off < LPE; off <<= 1) v += __shfl_xor(v, off, 64);
-                    if (ps.cl == 0) yp[k2 + b] = (float)v;
+                    for (int k = 0; k < DSH; ++k) tile[k * 64 + lane] = 0.0;
+                const double s = wave_sum_tile<DSH>(tile, lane);
+                const int k = lane >> 2;
+                if ((lane & 3) == 0 && k < DSH) {
+                    if constexpr (H == 1) {
+                        if (want_dy && k < dm.d_sh) a.dY[(int64_t)cur.e * dm.d_sh + k] = (float)s;
+                    } else {
+                        dyl[((ps.h * S + ps.s) * K + (t - t0)) * DSH + k] = s;
+                    }
                 }
-            });
+            } else {
+                // an edge spans LPE < 64 lanes: reduce each degree's partials over them
+                float* yp = a.dY + (int64_t)cur.e * dm.d_sh;
+                bwd_slice<Tb>(cur.w, cur.g, yv, xv, dxa, store_w, [&](auto K2, const auto& dyb) {
+                    constexpr int k2 = decltype(K2)::value;
+#pragma unroll
+                    for (int b = 0; b < (int)(sizeof(dyb) / sizeof(double)); ++b) {
+                        double v = (full_c || live) ? dyb[b] : 0.0;  // lanes past C leave the sum
+#pragma unroll
+                        for (int off = 1; off < LPE; off <<= 1) v += __shfl_xor(v, off, 64);
+                        if (want_dy && ps.cl == 0 && k2 + b < dm.d_sh) yp[k2 + b] = (float)v;
+                    }
+                });
+            }
         }
-    };
-    BwdEdge<Tb> ea, eb;
-    if (kPf && q < end) bwd_load<Tb, C>(ea, q, ch, N, gv, Y, W, Gr);
-    while (q < end) {
-        step(ea, eb);
-        if (q >= end) break;
-        step(eb, ea);
+        if constexpr (H == 2) {
+            // grad_Y of the chunk's edges: the two slices' sums, added in a fixed order
+            __syncthreads();
+            if (want_dy)
+                for (int idx = tid; idx < S * K * DSH; idx += 256) {
+                    const int s = idx / (K * DSH), tt = (idx / DSH) % K, k = idx % DSH;
+                    const int32_t t = t0 + tt;
+                    if (t >= t1 || q0 + s + S * t >= end || k >= dm.d_sh) continue;
+                    const int32_t e = eslot[s * K + tt];
+                    if (e < 0) continue;
+                    a.dY[(int64_t)e * dm.d_sh + k] =
+                        (float)(dyl[((0 * S + s) * K + tt) * DSH + k] + dyl[((1 * S + s) * K + tt) * DSH + k]);
+                }
+            __syncthreads();
+        }
     }
-    if constexpr (DX) {
+    if (want_dx) {
         // combine the streams in a fixed order; dx[j] has this block as its only writer
-        if constexpr (kLdsSum) __syncthreads();  // every wave is done with its grad_Y tile
+        if constexpr (kTile && H == 1) __syncthreads();  // every wave is done with its grad_Y tile
 #pragma unroll
-        for (int k = 0; k < DIN; ++k) lds[(ps.s * DIN + k) * C + ch] = dxa[k];
+        for (int k = 0; k < DIN; ++k) lds[(ps.s * DIN + k) * CP + ch] = dxa[k];
         __syncthreads();
-        float* dp = dx + (int64_t)j * (DIN * C);
-        for (int t = tid; t < DIN * C; t += 256) {
-            double v = 0.0;
+        float* dp = a.dx + (int64_t)j * (dm.d_in * C);
+        for (int t = tid; t < DIN * CP; t += 256) {
+            const int k = t / CP, c = t % CP;
+            if (k < dm.d_in && c < C) {
+                double v = 0.0;
 #pragma unroll
-            for (int r = 0; r < S; ++r) v += lds[r * DIN * C + t];
-            dp[t] = (float)v;
+                for (int r = 0; r < S; ++r) v += lds[r * DIN * CP + t];
+                dp[k * C + c] = (float)v;
+            }
         }
     }
 }
 
-// grad_Y of an edge = the sum of its H slice partials (fixed order)
-template <int DSH, int H>
-__global__ void __launch_bounds__(256) k_dy_combine(int32_t E, const double* __restrict__ dyp, float* __restrict__ dY)
+template <int LM, int LPE, int H, bool SUB>
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s)
 {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (t >= (int64_t)E * DSH) return;
-    const int64_t e = t / DSH;
-    const int k = (int)(t % DSH);
-    double v = 0.0;
-#pragma unroll
-    for (int h = 0; h < H; ++h) v += dyp[(e * H + h) * DSH + k];
-    dY[t] = (float)v;
-}
-
-template <int LIN, int LSH, int LOUT, int C, bool DX, bool DW, bool DY>
-hipError_t launch_bwd_t(int32_t N, GraphView g, const float* x, const float* Y, const float* W, const float* G,
-                        float* dx, float* dW, float* dY, hipStream_t s)
-{
-    hipLaunchKernelGGL((k_conv_bwd<LIN, LSH, LOUT, C, DX, DW, DY>), dim3((unsigned)N), dim3(256), 0, s, N, g, x, Y,
-                       W, G, dx, dW, dY);
-    if constexpr (DY && Geo<C>::H > 1) {
-        constexpr int DSH = (LSH + 1) * (LSH + 1);
-        const int64_t n = (int64_t)g.n_edges * DSH;
-        if (n > 0)
-            hipLaunchKernelGGL((k_dy_combine<DSH, Geo<C>::H>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                               g.n_edges, g.dyp, dY);
-    }
+    if (a.sh.N == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_conv_bwd<LM, LPE, H, SUB>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-template <int LIN, int LSH, int LOUT, int C>
-hipError_t launch_bwd(int32_t N, GraphView g, const float* x, const float* Y, const float* W, const float* G,
-                      float* dx, float* dW, float* dY, int mask, hipStream_t s)
-{
-    if (N == 0) return hipSuccess;
-    switch (mask) {
-        case 1: return launch_bwd_t<LIN, LSH, LOUT, C, true, false, false>(N, g, x, Y, W, G, dx, dW, dY, s);
-        case 2: return launch_bwd_t<LIN, LSH, LOUT, C, false, true, false>(N, g, x, Y, W, G, dx, dW, dY, s);
-        case 3: return launch_bwd_t<LIN, LSH, LOUT, C, true, true, false>(N, g, x, Y, W, G, dx, dW, dY, s);
-        case 4: return launch_bwd_t<LIN, LSH, LOUT, C, false, false, true>(N, g, x, Y, W, G, dx, dW, dY, s);
-        case 5: return launch_bwd_t<LIN, LSH, LOUT, C, true, false, true>(N, g, x, Y, W, G, dx, dW, dY, s);
-        case 6: return launch_bwd_t<LIN, LSH, LOUT, C, false, true, true>(N, g, x, Y, W, G, dx, dW, dY, s);
-        case 7: return launch_bwd_t<LIN, LSH, LOUT, C, true, true, true>(N, g, x, Y, W, G, dx, dW, dY, s);
-        default: return hipSuccess;
-    }
-}
-
-template <int L, int C>
+template <int LM, int LPE, int H>
 constexpr KernelSet make_set()
 {
-    return KernelSet{L, L, L, C, Geo<C>::H > 1 ? Geo<C>::H * (L + 1) * (L + 1) : 0, &launch_sh<L>,
-                     &launch_fwd<L, L, L, C>, &launch_bwd<L, L, L, C>};
+    return KernelSet{LM,
+                     LPE,
+                     H,
+                     {&launch_fwd<LM, LPE, H, false>, &launch_fwd<LM, LPE, H, true>},
+                     {&launch_bwd<LM, LPE, H, false>, &launch_bwd<LM, LPE, H, true>}};
 }
 
-// the convolution kernels of one (L, C) without the SH launcher, for a
-// translation unit of its own (the SH kernel is instantiated once per degree
-// by the degree's registry)
-template <int L, int C>
-constexpr KernelSet make_conv_set()
-{
-    return KernelSet{L, L, L, C, Geo<C>::H > 1 ? Geo<C>::H * (L + 1) * (L + 1) : 0, nullptr,
-                     &launch_fwd<L, L, L, C>, &launch_bwd<L, L, L, C>};
-}
-
-template <int LIN, int LSH, int LOUT>
+template <int LM>
 static bool copy_table(int path, double* dense)
 {
-    using Tb = cgmath::Tables<LIN, LSH, LOUT>;
+    using Tb = cgmath::Tables<LM, LM, LM>;
     if (path < 0 || path >= Tb::P) return false;
-    const int n = cgmath::path_size(cgmath::path_at(LIN, LSH, LOUT, path));
+    const int n = cgmath::path_size(cgmath::path_at(LM, LM, LM, path));
     for (int q = 0; q < n; ++q) dense[q] = Tb::data.T[Tb::data.off[path] + q];
     return true;
 }

@@ -1,23 +1,15 @@
-// cgtp_kernels_l1.hip -- degree-1 specialisations (features, SH and outputs l = 0..1).
+// cgtp_kernels_l1.hip -- degree-1 kernels (paths of l_in, l_sh, l_out <= 1),
+// every lane geometry.
 #include "cgtp_kernels.h"
 
 namespace cgtp {
 
-static const KernelSet kSets[] = {
-    make_set<1, 8>(),
-    make_set<1, 16>(),
-    make_set<1, 32>(),
-    make_set<1, 64>(),
-    make_set<1, 128>(),
-};
-
-const KernelSet* kernels_l1(int channels)
+// host-side table of this unit's kernels, indexed by lane geometry
+const KernelSet* kernels_l1(int g)
 {
-    for (const KernelSet& k : kSets)
-        if (k.channels == channels) return &k;
-    return nullptr;
+    static const KernelSet sets[5] = {make_set<1, 8, 1>(), make_set<1, 16, 1>(), make_set<1, 32, 1>(),
+                                      make_set<1, 64, 1>(), make_set<1, 64, 2>()};
+    return &sets[g];
 }
-
-bool table_l1(int path, double* dense) { return copy_table<1, 1, 1>(path, dense); }
 
 }  // namespace cgtp

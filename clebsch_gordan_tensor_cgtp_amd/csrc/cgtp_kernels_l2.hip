@@ -1,23 +1,14 @@
-// cgtp_kernels_l2.hip -- degree-2 specialisations (features, SH and outputs l = 0..2).
+// cgtp_kernels_l2.hip -- degree-2 kernels (paths of l_in, l_sh, l_out <= 2)
+// for up to 32 channels.
 #include "cgtp_kernels.h"
 
 namespace cgtp {
 
-static const KernelSet kSets[] = {
-    make_set<2, 8>(),
-    make_set<2, 16>(),
-    make_set<2, 32>(),
-    make_set<2, 64>(),
-    make_set<2, 128>(),
-};
-
-const KernelSet* kernels_l2(int channels)
+// host-side table of this unit's kernels: geometries 0..2 (8, 16, 32 lanes)
+const KernelSet* kernels_l2_narrow(int g)
 {
-    for (const KernelSet& k : kSets)
-        if (k.channels == channels) return &k;
-    return nullptr;
+    static const KernelSet sets[3] = {make_set<2, 8, 1>(), make_set<2, 16, 1>(), make_set<2, 32, 1>()};
+    return &sets[g];
 }
-
-bool table_l2(int path, double* dense) { return copy_table<2, 2, 2>(path, dense); }
 
 }  // namespace cgtp

@@ -38,10 +38,11 @@ def _need(t, name, dtype, shape=None, device=None):
 class Plan:
     """Compiled CGTP convolution for degrees (l_in, l_sh, l_out) and C channels."""
 
-    def __init__(self, l_in: int, l_sh: int, l_out: int, channels: int, validate: bool = False):
+    def __init__(self, l_in: int, l_sh: int, l_out: int, channels: int, validate: bool = False,
+                 locality: bool = True):
         lib = L.lib()
         h = ctypes.c_void_p()
-        flags = L.CGTP_FLAG_VALIDATE if validate else 0
+        flags = (L.CGTP_FLAG_VALIDATE if validate else 0) | (0 if locality else L.CGTP_FLAG_NO_LOCALITY)
         L.check("cgtp_plan_create", lib.cgtp_plan_create(ctypes.byref(h), l_in, l_sh, l_out, channels, flags))
         self._h = h
         self.l_in, self.l_sh, self.l_out, self.channels = l_in, l_sh, l_out, channels
@@ -83,6 +84,32 @@ class Plan:
         L.check("cgtp_sh_fwd", L.lib().cgtp_sh_fwd(self._h, E, _ptr(r), _ptr(Y), _stream(r.device)))
         return Y
 
+    def sh_bwd(self, r: torch.Tensor, grad_Y: torch.Tensor, grad_r: torch.Tensor | None = None) -> torch.Tensor:
+        """grad_r[E][3] = grad_Y[e] . dY/dr at r[e]."""
+        E = r.shape[0]
+        _need(r, "r", torch.float32, (E, 3))
+        _need(grad_Y, "grad_Y", torch.float32, (E, self.dim_sh), r.device)
+        if grad_r is None:
+            grad_r = torch.empty((E, 3), dtype=torch.float32, device=r.device)
+        _need(grad_r, "grad_r", torch.float32, (E, 3), r.device)
+        L.check("cgtp_sh_bwd", L.lib().cgtp_sh_bwd(self._h, E, _ptr(r), _ptr(grad_Y), _ptr(grad_r),
+                                                   _stream(r.device)))
+        return grad_r
+
+    def node_grad(self, row_ptr, src, grad_r, ws=None, grad_pos=None) -> torch.Tensor:
+        """grad_pos[N][3] from per-edge gradients of r = pos[src] - pos[dst]."""
+        N, E, dev = row_ptr.shape[0] - 1, src.shape[0], row_ptr.device
+        _need(row_ptr, "row_ptr", torch.int32)
+        _need(src, "src", torch.int32, (E,), dev)
+        _need(grad_r, "grad_r", torch.float32, (E, 3), dev)
+        ws = self._workspace(ws, N, E, dev)
+        if grad_pos is None:
+            grad_pos = torch.empty((N, 3), dtype=torch.float32, device=dev)
+        _need(grad_pos, "grad_pos", torch.float32, (N, 3), dev)
+        L.check("cgtp_node_grad", L.lib().cgtp_node_grad(self._h, N, E, _ptr(row_ptr), _ptr(src), _ptr(grad_r),
+                                                         _ptr(grad_pos), _ptr(ws), ws.numel(), _stream(dev)))
+        return grad_pos
+
     def graph_prepare(self, row_ptr: torch.Tensor, src: torch.Tensor,
                       ws: torch.Tensor | None = None) -> torch.Tensor:
         N, E = row_ptr.shape[0] - 1, src.shape[0]
@@ -96,14 +123,22 @@ class Plan:
             self._h, N, E, _ptr(row_ptr), _ptr(src), _ptr(ws), ws.numel(), _stream(row_ptr.device)))
         return ws
 
-    def conv_fwd(self, row_ptr, src, x, Y, W, ws, out=None) -> torch.Tensor:
+    def _workspace(self, ws, N, E, dev):
+        if ws is None:
+            ws = torch.empty(self.workspace_size(N, E), dtype=torch.uint8, device=dev)
+        _need(ws, "ws", torch.uint8, device=dev)
+        return ws
+
+    def conv_fwd(self, row_ptr, src, x, Y, W, ws=None, out=None) -> torch.Tensor:
+        """out[N][D_out][C].  ``ws``: the graph's workspace (from graph_prepare,
+        or any buffer of workspace_size bytes, which the call then prepares)."""
         N, E, C, dev = row_ptr.shape[0] - 1, src.shape[0], self.channels, row_ptr.device
         _need(row_ptr, "row_ptr", torch.int32)
         _need(src, "src", torch.int32, (E,), dev)
         _need(x, "x", torch.float32, (N, self.dim_in, C), dev)
         _need(Y, "Y", torch.float32, (E, self.dim_sh), dev)
         _need(W, "W", torch.float32, (E, self.num_paths, C), dev)
-        _need(ws, "ws", torch.uint8, device=dev)
+        ws = self._workspace(ws, N, E, dev)
         if out is None:
             out = torch.empty((N, self.dim_out, C), dtype=torch.float32, device=dev)
         _need(out, "out", torch.float32, (N, self.dim_out, C), dev)
@@ -112,7 +147,7 @@ class Plan:
             ws.numel(), _stream(dev)))
         return out
 
-    def conv_bwd(self, row_ptr, src, x, Y, W, grad_out, ws, want=("dx", "dW", "dY"),
+    def conv_bwd(self, row_ptr, src, x, Y, W, grad_out, ws=None, want=("dx", "dW", "dY"),
                  grad_x=None, grad_W=None, grad_Y=None):
         """(grad_x, grad_W, grad_Y); a gradient not in ``want`` comes back as None."""
         N, E, C, dev = row_ptr.shape[0] - 1, src.shape[0], self.channels, row_ptr.device
@@ -122,7 +157,7 @@ class Plan:
         _need(Y, "Y", torch.float32, (E, self.dim_sh), dev)
         _need(W, "W", torch.float32, (E, self.num_paths, C), dev)
         _need(grad_out, "grad_out", torch.float32, (N, self.dim_out, C), dev)
-        _need(ws, "ws", torch.uint8, device=dev)
+        ws = self._workspace(ws, N, E, dev)
         if "dx" in want and grad_x is None:
             grad_x = torch.empty((N, self.dim_in, C), dtype=torch.float32, device=dev)
         if "dW" in want and grad_W is None:

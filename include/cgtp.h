@@ -22,29 +22,34 @@
  * argument of this trilinear map.
  *
  * Conventions shared by every entry point:
- *   - paths (l1,l2,l3) in lexicographic order, every triangle-valid path
- *     (no parity filter); the path count P is reported by cgtp_plan_info.
+ *   - paths (l1,l2,l3) in lexicographic order, every triangle-valid path with
+ *     l1 <= l_in, l2 <= l_sh, l3 <= l_out (no parity filter); the path count
+ *     P and the list are reported by cgtp_plan_info.
  *   - T_p is the real part (even l1+l2+l3) or the imaginary part (odd) of the
  *     complex CG tensor (Condon-Shortley phase) carried to the real basis
  *     Y_{l,m} = sqrt2 (-1)^m Im Y_l^|m| (m<0), Y_l^0, sqrt2 (-1)^m Re Y_l^m (m>0).
  *   - layouts, all row-major fp32, channels fastest:
- *       x, grad_x       [N][(L_in+1)^2][C]
- *       out, grad_out   [N][(L_out+1)^2][C]
- *       Y, grad_Y       [E][(L_sh+1)^2]
+ *       x, grad_x       [N][(l_in+1)^2][C]
+ *       out, grad_out   [N][(l_out+1)^2][C]
+ *       Y, grad_Y       [E][(l_sh+1)^2]
  *       W, grad_W       [E][P][C]
  *       r               [E][3]
  *   - the graph is a receiver-sorted CSR: row_ptr[N+1] (int32, row_ptr[0] = 0,
  *     non-decreasing, row_ptr[N] = E) and src[E] (int32 sender of each edge,
- *     in [0, N)).  Well-formedness is a precondition, checked only when the
- *     plan was created with CGTP_FLAG_VALIDATE.
- *   - every array argument is a DEVICE pointer owned by the caller; calls are
- *     asynchronous on the given stream; outputs are overwritten, never
- *     accumulated; a NULL gradient pointer skips that gradient.
+ *     in [0, N)).  Well-formedness is a precondition, checked (on a host copy,
+ *     synchronously) only when the plan was created with CGTP_FLAG_VALIDATE.
+ *     A malformed graph never makes a kernel read or write out of bounds: the
+ *     kernels clamp every CSR and view index; the values are then unspecified.
+ *   - every array argument is a DEVICE pointer owned by the caller and aligned
+ *     to 16 bytes; calls are asynchronous on the given stream; outputs are
+ *     overwritten, never accumulated; a NULL gradient pointer skips that
+ *     gradient.
  *   - arithmetic is fp64 inside the kernels; inputs and outputs are fp32.
+ *     Every floating-point sum has a fixed order: results are bitwise
+ *     reproducible run to run (no floating-point atomics).
  *   - every function returns a status and never aborts.  Only host-side
- *     checks are made (null handles and pointers, sizes, 8-byte alignment of
- *     the channel arrays, workspace size); a HIP launch error returns
- *     CGTP_ERR_HIP.
+ *     checks are made (null handles and pointers, sizes, alignment, workspace
+ *     size); a HIP launch error returns CGTP_ERR_HIP.
  */
 #ifndef CGTP_H
 #define CGTP_H
@@ -63,7 +68,7 @@ typedef struct cgtp_plan_s* cgtp_plan_t;
 typedef enum {
     CGTP_OK = 0,
     CGTP_ERR_INVALID_ARG = -1,  /* null handle/pointer, negative size, misalignment */
-    CGTP_ERR_UNSUPPORTED = -2,  /* degrees or channel count without a compiled kernel */
+    CGTP_ERR_UNSUPPORTED = -2,  /* degrees or channel count outside the compiled range */
     CGTP_ERR_WORKSPACE = -3,    /* workspace missing or smaller than cgtp_workspace_size */
     CGTP_ERR_HIP = -4,          /* a HIP call or kernel launch failed */
     CGTP_ERR_ALLOC = -5,        /* host allocation failed */
@@ -72,57 +77,99 @@ typedef enum {
 
 /* Validate the CSR (on a host copy, synchronously) in every call taking a graph. */
 #define CGTP_FLAG_VALIDATE 1u
+/* Schedule convolution blocks in node-id order instead of the graph-derived
+ * locality order (a diagnostic: results are identical, only speed differs). */
+#define CGTP_FLAG_NO_LOCALITY 2u
 
-/* Create a plan for degrees (l_in, l_sh, l_out) and C channels.
- * Supported: l_in = l_sh = l_out = L with L in {1, 2} and C in {8, 16, 32, 64, 128},
- * or L = 3 and C in {8, 16, 32, 64}.  Host-only: no HIP call is made.
- * On success *plan owns host memory released by cgtp_plan_destroy. */
+/* Create a plan for degrees (l_in, l_sh, l_out) and C channels: the path list
+ * under the selection rules (TDN rebuttal to S6y1, first answer) and the real
+ * CG tables (TDN rebuttal to 7Mvd: the coordinates of the SO(3) tensor
+ * product in the coupled basis).
+ * Supported: 0 <= l_in, l_sh, l_out <= 3 and 1 <= C <= 128.  Host-only: no
+ * HIP call is made.  flags: CGTP_FLAG_* or 0; unknown bits -> INVALID_ARG.
+ * On success *plan owns host memory released by cgtp_plan_destroy; a plan
+ * is immutable and may be shared by threads. */
 cgtp_status_t cgtp_plan_create(cgtp_plan_t* plan, int l_in, int l_sh, int l_out, int channels,
                                unsigned flags);
 
 /* Release a plan (NULL is accepted). */
 cgtp_status_t cgtp_plan_destroy(cgtp_plan_t plan);
 
-/* Path count and dimensions.  paths_l1l2l3, if not NULL, receives [P][3]
- * (l1, l2, l3) in the order the weights use.  Any output pointer may be NULL. */
+/* Path count and dimensions of a plan (TDN rebuttal to S6y1, first answer:
+ * which (l1, l2, l3) couple).  paths_l1l2l3, if not NULL, receives [P][3]
+ * (l1, l2, l3) in the order the weights use.  Any output pointer may be NULL.
+ * dim_* = (l+1)^2 of each degree. */
 cgtp_status_t cgtp_plan_info(cgtp_plan_t plan, int* num_paths, int* paths_l1l2l3, int* dim_in,
                              int* dim_sh, int* dim_out);
 
-/* Test hook: the real CG tensor of path `path` exactly as the kernels use it,
- * dense [(2l1+1)][(2l2+1)][(2l3+1)] fp64 into host memory `dense`. */
+/* Test hook: the real CG tensor of path `path` exactly as the kernels use it
+ * (TDN rebuttal to 7Mvd), dense [(2l1+1)][(2l2+1)][(2l3+1)] fp64 into HOST
+ * memory `dense` (caller-owned, at least that many doubles). */
 cgtp_status_t cgtp_plan_export_cg(cgtp_plan_t plan, int path, double* dense);
 
-/* Bytes of device workspace for N nodes and E edges: the sender-sorted view
- * of the CSR and its temporaries, degree-ordered block schedules, and for
- * C > 64 a scratch section of 8*E*(C/64)*(l_sh+1)^2 bytes for the backward. */
+/* Bytes of device workspace for N nodes and E edges (independent of the
+ * plan's degrees): the sender-sorted view of the CSR and its temporaries and
+ * the block schedules, about 16*E + 300*N bytes. */
 cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, size_t* bytes);
 
-/* Real spherical harmonics, degrees 0..l_sh, of r[e]/|r[e]|: Y[E][(l_sh+1)^2].
+/* Real spherical harmonics Y_l(r/|r|), degrees 0..l_sh, orthonormal, of every
+ * edge vector (the SH that couple to the node features in the CGTP
+ * convolution, LunaTP Abstract): r[E][3] -> Y[E][(l_sh+1)^2].
  * A zero-length r[e] is a precondition violation (the result is unspecified). */
 cgtp_status_t cgtp_sh_fwd(cgtp_plan_t plan, int64_t n_edges, const float* r, float* Y, hipStream_t stream);
 
-/* Graph preparation: writes into `ws` the sender-sorted view of the CSR
+/* Backward of the spherical harmonics: grad_r[e] = sum_k grad_Y[e][k] dY_k/dr
+ * evaluated at r[e], for degrees 0..l_sh: r[E][3], grad_Y[E][(l_sh+1)^2] ->
+ * grad_r[E][3].  This is the path by which the convolution backward's grad_Y
+ * term feeds the forces of an interatomic potential (analytic forces checked
+ * by finite differences, AccelNet review, Referee Report).  Since Y depends on
+ * the direction only, grad_r is orthogonal to r.  A zero-length r[e] is a
+ * precondition violation. */
+cgtp_status_t cgtp_sh_bwd(cgtp_plan_t plan, int64_t n_edges, const float* r, const float* grad_Y, float* grad_r,
+                          hipStream_t stream);
+
+/* Per-node gradient from per-edge gradients of the edge vectors
+ * r[e] = pos[src e] - pos[dst e] (the forces on atoms are its negative):
+ *   grad_pos[n] = sum_{e: src e = n} grad_r[e] - sum_{e: dst e = n} grad_r[e],
+ * grad_r[E][3] -> grad_pos[N][3].  One writer per node, fixed summation
+ * order (the out-edges through the sender-sorted view in `ws`, prepared here
+ * first unless cgtp_graph_prepare already did, see there). */
+cgtp_status_t cgtp_node_grad(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
+                             const int32_t* src, const float* grad_r, float* grad_pos, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* Graph preparation (LunaTP Abstract: node-centric execution needs each
+ * node's edges together): writes into `ws` the sender-sorted view of the CSR
  * (sender offsets, edge permutation stable in edge id, receiver of each
- * permuted edge).  Must run, on the same stream or earlier, before
- * cgtp_conv_fwd / cgtp_conv_bwd are called with this (row_ptr, src, ws); a
- * prepared workspace can serve any number of such calls for the same graph. */
+ * permuted edge) and the block schedules of both convolution kernels.  The
+ * library records that `ws` now holds the view of (n_nodes, n_edges,
+ * row_ptr, src); cgtp_conv_fwd / cgtp_conv_bwd called with the same four
+ * values and `ws` use it as it is, and otherwise run this preparation
+ * themselves first.  The record is by pointer: after rewriting the contents
+ * of row_ptr or src in place, call cgtp_graph_prepare again.  ws must be
+ * 256-byte aligned and at least cgtp_workspace_size bytes. */
 cgtp_status_t cgtp_graph_prepare(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges,
                                  const int32_t* row_ptr, const int32_t* src, void* ws, size_t ws_bytes,
                                  hipStream_t stream);
 
-/* Forward: out[N][(l_out+1)^2][C] from x, Y, W over the CSR.  Node-centric and
- * atomic-free: each receiver's output row has exactly one writer. ws is the
- * workspace prepared by cgtp_graph_prepare for this graph. */
+/* Forward of the CGTP convolution (LunaTP Abstract; the formula above):
+ * out[N][(l_out+1)^2][C] from x, Y, W over the CSR.  Node-centric and
+ * atomic-free: each receiver's output row has exactly one writer, and a
+ * receiver without in-edges gets zeros.  ws: the workspace of this graph
+ * (prepared here first unless cgtp_graph_prepare already did, see there). */
 cgtp_status_t cgtp_conv_fwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
                             const int32_t* src, const float* x, const float* Y, const float* W, float* out,
-                            const void* ws, size_t ws_bytes, hipStream_t stream);
+                            void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Backward of L = <grad_out, out>: grad_x [N][(l_in+1)^2][C],
- * grad_W [E][P][C], grad_Y [E][(l_sh+1)^2]; each may be NULL to skip it.
- * Sender-centric and atomic-free over the prepared workspace `ws`.  For
- * C > 64 the backward also writes per-slice grad_Y partial sums into the
- * workspace's scratch section, so two backward calls in flight at the same
- * time must not share one workspace (the graph view itself is only read). */
+/* Backward of L = <grad_out, out> (TDN rebuttal to S6y1, the gradients after
+ * Equation (3), one per argument of the trilinear map):
+ *   grad_x [N][(l_in+1)^2][C]   (a sender without out-edges gets zeros)
+ *   grad_W [E][P][C]
+ *   grad_Y [E][(l_sh+1)^2]      (summed over the channels)
+ * each may be NULL to skip it.  Sender-centric and atomic-free over the
+ * sender-sorted view in `ws` (prepared here first unless cgtp_graph_prepare
+ * already did).  The view is only read, so backward and forward calls of one
+ * graph may share a workspace. */
 cgtp_status_t cgtp_conv_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
                             const int32_t* src, const float* x, const float* Y, const float* W,
                             const float* grad_out, float* grad_x, float* grad_W, float* grad_Y,

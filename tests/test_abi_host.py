@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(L.lib(), n), n
         assert n in L.SIGNATURES, n
@@ -47,23 +47,29 @@ def test_plan_create_arguments(L):
     assert L.lib().cgtp_plan_create(None, 2, 2, 2, 128, 0) == L.CGTP_ERR_INVALID_ARG
     assert _create(L, -1, 2, 2, 128, 0)[0] == L.CGTP_ERR_INVALID_ARG
     assert _create(L, 2, 2, 2, 0, 0)[0] == L.CGTP_ERR_INVALID_ARG
-    assert _create(L, 2, 2, 2, 128, 8)[0] == L.CGTP_ERR_INVALID_ARG
+    assert _create(L, 2, 2, 2, 128, 4)[0] == L.CGTP_ERR_INVALID_ARG      # unknown flag bit
     assert _create(L, 4, 4, 4, 16, 0)[0] == L.CGTP_ERR_UNSUPPORTED
-    assert _create(L, 2, 2, 2, 96, 0)[0] == L.CGTP_ERR_UNSUPPORTED
-    assert _create(L, 3, 3, 3, 128, 0)[0] == L.CGTP_ERR_UNSUPPORTED
-    for Lx, C in ((1, 8), (1, 128), (2, 8), (2, 64), (2, 128), (3, 8), (3, 64)):
-        st, h = _create(L, Lx, Lx, Lx, C, 0)
-        assert st == L.CGTP_OK
-        assert L.lib().cgtp_plan_destroy(h) == L.CGTP_OK
+    assert _create(L, 1, 4, 1, 16, 0)[0] == L.CGTP_ERR_UNSUPPORTED
+    assert _create(L, 2, 2, 2, 129, 0)[0] == L.CGTP_ERR_UNSUPPORTED     # more than 128 channels
+    # every degree triple up to 3 and every channel count from 1 to 128
+    for (a, b, c) in ((0, 0, 0), (1, 1, 1), (2, 3, 2), (3, 0, 3), (0, 2, 2), (3, 3, 3)):
+        for C in (1, 7, 8, 24, 64, 65, 96, 127, 128):
+            for flags in (0, L.CGTP_FLAG_VALIDATE, L.CGTP_FLAG_NO_LOCALITY):
+                st, h = _create(L, a, b, c, C, flags)
+                assert st == L.CGTP_OK, (a, b, c, C, flags)
+                assert L.lib().cgtp_plan_destroy(h) == L.CGTP_OK
     assert L.lib().cgtp_plan_destroy(None) == L.CGTP_OK
 
 
-@pytest.mark.parametrize("Lx", [1, 2, 3])
-def test_plan_paths_and_tables_match_oracle(L, oracle, Lx):
+TRIPLES = [(a, b, c) for a in range(4) for b in range(4) for c in range(4)]
+
+
+@pytest.mark.parametrize("a,b,c", TRIPLES)
+def test_plan_paths_and_tables_match_oracle(L, oracle, a, b, c):
     from clebsch_gordan_tensor_cgtp_amd.ops import Plan
-    plan = Plan(Lx, Lx, Lx, 8)
-    assert plan.paths == [tuple(int(v) for v in p) for p in oracle.paths(Lx, Lx, Lx)]
-    assert (plan.dim_in, plan.dim_sh, plan.dim_out) == ((Lx + 1) ** 2,) * 3
+    plan = Plan(a, b, c, 8)
+    assert plan.paths == [tuple(int(v) for v in p) for p in oracle.paths(a, b, c)]
+    assert (plan.dim_in, plan.dim_sh, plan.dim_out) == ((a + 1) ** 2, (b + 1) ** 2, (c + 1) ** 2)
     for q, (l1, l2, l3) in enumerate(plan.paths):
         got = plan.export_cg(q)
         want = oracle.real_cg(l1, l2, l3)
@@ -82,11 +88,13 @@ def test_export_bad_path(L):
 
 
 def test_workspace_size(L):
+    from tests.layout import ws_sections
     st, h = _create(L, 2, 2, 2, 128, 0)
     b = ctypes.c_size_t()
-    assert L.lib().cgtp_workspace_size(h, 2000, 105730, ctypes.byref(b)) == L.CGTP_OK
-    a = lambda v: (v + 255) // 256 * 256
-    assert b.value == a(4 * 2001) + 2 * a(4 * 105730) + 2 * a(4 * 32 * 2000) + 2 * a(4 * 2000) + a(8 * 105730 * 2 * 9)
+    for N, E in ((2000, 105730), (0, 0), (1, 0), (13, 5), (50000, 2616668)):
+        assert L.lib().cgtp_workspace_size(h, N, E, ctypes.byref(b)) == L.CGTP_OK
+        assert b.value == ws_sections(N, E)["total"]
+        assert b.value <= 16 * max(E, 1) + 300 * max(N, 1) + 14 * 256  # the header's estimate, plus alignment
     assert L.lib().cgtp_workspace_size(h, -1, 5, ctypes.byref(b)) == L.CGTP_ERR_INVALID_ARG
     assert L.lib().cgtp_workspace_size(h, 5, 5, None) == L.CGTP_ERR_INVALID_ARG
     L.lib().cgtp_plan_destroy(h)
@@ -97,7 +105,7 @@ def test_calls_reject_bad_arguments_without_a_gpu(L):
     lib = L.lib()
     st, h = _create(L, 2, 2, 2, 128, 0)
     fake = ctypes.c_void_p(4096)       # never dereferenced: the checks fail first
-    odd = ctypes.c_void_p(4096 + 4)    # not 8-byte aligned
+    odd = ctypes.c_void_p(4096 + 8)    # not 16-byte aligned
     ws = ctypes.c_void_p(1 << 20)
     big = 1 << 30
     # null plan
