@@ -137,8 +137,8 @@ def main():
                     help="extra untimed warm-up, in seconds of sustained load, after the --warmup steps")
     ap.add_argument("--workload", default="layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-locality", action="store_true",
-                    help="schedule blocks in node-id order instead of the graph-derived locality order")
+    ap.add_argument("--locality", action="store_true",
+                    help="schedule blocks by graph-derived clusters per XCD instead of longest first")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy kernel (PMC byte calibration)")
     ap.add_argument("--copy-ceiling", action="store_true",
@@ -169,7 +169,7 @@ def main():
 
     w, g, rp, src, r, x, W, G = make_inputs(torch, dev, args.workload)
     N, E, L, C = g.n_nodes, g.n_edges, w.l_max, w.channels
-    plan = Plan(L, L, L, C, locality=not args.no_locality)
+    plan = Plan(L, L, L, C, locality=args.locality)
     P = plan.num_paths
     Y = torch.empty((E, plan.dim_sh), device=dev)
     out = torch.empty((N, plan.dim_out, C), device=dev)

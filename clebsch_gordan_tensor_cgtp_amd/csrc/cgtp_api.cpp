@@ -33,7 +33,7 @@ struct cgtp_plan_s {
 
 namespace {
 
-constexpr unsigned kKnownFlags = CGTP_FLAG_VALIDATE | CGTP_FLAG_NO_LOCALITY;
+constexpr unsigned kKnownFlags = CGTP_FLAG_VALIDATE | CGTP_FLAG_LOCALITY;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -97,7 +97,7 @@ cgtp_status_t prepare_into(const cgtp_plan_s* plan, int64_t N, int64_t E, const 
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return CGTP_ERR_HIP;
-    const bool loc = !(plan->flags & CGTP_FLAG_NO_LOCALITY);
+    const bool loc = (plan->flags & CGTP_FLAG_LOCALITY) != 0;
     const hipError_t e = cgtp::launch_graph_prepare((int32_t)N, (int32_t)E, row_ptr, src, ws, loc, stream);
     std::lock_guard<std::mutex> lk(g_mu);
     if (e != hipSuccess) {
@@ -114,7 +114,7 @@ cgtp_status_t ensure_prepared(const cgtp_plan_s* plan, int64_t N, int64_t E, con
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return CGTP_ERR_HIP;
-    const bool loc = !(plan->flags & CGTP_FLAG_NO_LOCALITY);
+    const bool loc = (plan->flags & CGTP_FLAG_LOCALITY) != 0;
     {
         std::lock_guard<std::mutex> lk(g_mu);
         auto it = records().find(ws);

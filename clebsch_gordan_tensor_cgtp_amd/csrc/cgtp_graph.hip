@@ -6,22 +6,29 @@
 // edges in ascending id), so the backward's grad_x sums run in a fixed order.
 //
 // The schedules decide which node each block of a convolution launch serves.
-// Blocks are dealt to the eight XCDs in turn (block b runs on XCD b % 8) and
-// each XCD has its own L2, so the nodes are split into eight ranges of
-// ceil(N/8), range x served by the blocks b = x, x+8, x+16, ...  A range
-// should be a compact piece of the atomic system, so that the rows its blocks
-// gather (x_j in the forward, grad_out_i in the backward) are shared through
-// that XCD's L2 instead of fetched again by every XCD.  The caller's node ids
-// carry no spatial order, so it is read off the graph itself with two rounds
-// of min-hash clustering: every node draws a pseudo-random key, key1(i) is
-// the smallest key in the closed neighbourhood of i, and the cluster centre
-// of i is the node holding the smallest key1 over the closed neighbourhood
-// of i (nodes within two hops share it).  Nodes are ordered by centre and cut
-// into the eight ranges; inside a range the blocks run longest segment first
-// so the last blocks to start are short.  The order only schedules blocks:
-// every output row has one writer and a fixed summation order, so results do
-// not depend on it (the placement inside a cluster and a degree bin comes from
-// integer atomics and may differ between runs).
+// By default every node is placed by degree, longest segment first: blocks
+// are dealt to the eight XCDs in turn (block b runs on XCD b % 8), so each XCD
+// receives the same mix of long and short segments and the last blocks to
+// start are short.
+//
+// The locality schedule (CGTP_FLAG_LOCALITY) instead gives each XCD, with its
+// own L2, a compact piece of the atomic system, so the rows its blocks gather
+// (x_j in the forward, grad_out_i in the backward) are shared through that L2
+// instead of fetched again by every XCD.  The caller's node ids carry no
+// spatial order, so it is read off the graph itself with two rounds of
+// min-hash clustering: every node draws a pseudo-random key, key1(i) is the
+// smallest key in the closed neighbourhood of i, and the cluster centre of i
+// is the node holding the smallest key1 over the closed neighbourhood of i
+// (nodes within two hops share it).  Nodes are ordered by centre and cut into
+// eight ranges of ceil(N/8), range x served by the blocks b = x, x+8, ...;
+// inside a range the blocks run longest segment first.  It cuts the gathered
+// bytes but not the kernel time on this chip (the re-fetched rows come from
+// the 256 MB last-level cache), and with skewed degrees the clusters can
+// leave the ranges unequal in edges, hence it is not the default.
+//
+// Either order only schedules blocks: every output row has one writer and a
+// fixed summation order, so results do not depend on it (placement inside a
+// degree bin comes from integer atomics and may differ between runs).
 #include <hip/hip_runtime.h>
 
 #include <limits.h>
@@ -130,8 +137,9 @@ __global__ void __launch_bounds__(256) k_prep_keys(int32_t N, int32_t E, const i
     if (lane == 0) key1[i] = m;
 }
 
-// Step 2, one wave per receiver i: its cluster centre and its rank inside
-// the cluster (integer atomics), and the out-degree count of every sender.
+// Step 2, one wave per receiver i: the out-degree count of every sender and,
+// for the locality schedule, i's cluster centre and its rank inside the
+// cluster (integer atomics).
 __global__ void __launch_bounds__(256) k_prep_centers(int32_t N, int32_t E, const int32_t* __restrict__ row_ptr,
                                                        const int32_t* __restrict__ src, int32_t locality,
                                                        const uint64_t* __restrict__ key1, int32_t* __restrict__ center,
@@ -142,96 +150,129 @@ __global__ void __launch_bounds__(256) k_prep_centers(int32_t N, int32_t E, cons
     if (i >= N) return;
     int32_t e0, e1;
     segment(row_ptr, i, E, e0, e1);
-    int32_t c = i;
     if (locality) {
         uint64_t m = key1[i];
         for (int32_t e = e0 + lane; e < e1; e += 64) {
             const uint64_t k = key1[valid_node(src[e], N)];
             m = k < m ? k : m;
         }
-        c = (int32_t)(uint32_t)wave_min_u64(m);
-    }
-    if (lane == 0) {
-        center[i] = c;
-        crank[i] = atomicAdd(&ccnt[c], 1);
+        const int32_t c = (int32_t)(uint32_t)wave_min_u64(m);
+        if (lane == 0) {
+            center[i] = c;
+            crank[i] = atomicAdd(&ccnt[c], 1);
+        }
     }
     for (int32_t e = e0 + lane; e < e1; e += 64) atomicAdd(&cnt[(int64_t)valid_node(src[e], N) * kCounterStride], 1);
 }
 
 // Step 3, one block of 1024 threads: the sender offsets srow (prefix sum of
-// the out-degrees), the cluster offsets, and the two block schedules.
-// Node i's place in the cluster order is g = coff[centre] + rank; its range
-// is x = g / Q; inside a range the nodes go longest first by LDS histograms of
-// (range, degree bin).
-__global__ void __launch_bounds__(1024) k_prep_orders(int32_t N, int32_t E, const int32_t* __restrict__ row_ptr,
+// the out-degrees) and the two block schedules.  Default: one range of all N
+// nodes, longest first (LDS histogram of degree bins), block b serving entry
+// b.  Locality: node i's place in the cluster order is g = coff[centre] +
+// rank (coff the prefix sum of the cluster sizes), its range is x = g / Q,
+// and inside a range the nodes go longest first by LDS histograms of
+// (range, degree bin); block x + 8s serves entry s of range x.
+__global__ void __launch_bounds__(1024) k_prep_orders(int32_t N, int32_t E, int32_t locality,
+                                                       const int32_t* __restrict__ row_ptr,
                                                        const int32_t* __restrict__ cnt, const int32_t* __restrict__ ccnt,
                                                        const int32_t* __restrict__ center,
                                                        const int32_t* __restrict__ crank, int32_t* __restrict__ srow,
                                                        int32_t* __restrict__ coff, int32_t* __restrict__ rorder,
                                                        int32_t* __restrict__ sorder)
 {
-    __shared__ int32_t hin[kXcds][kDegBins], hout[kXcds][kDegBins], tot[16];
+    __shared__ int32_t hin[kXcds * kDegBins], hout[kXcds * kDegBins], tot[16], xbase[2][kXcds];
     const int t = threadIdx.x;
     if (t == 0) srow[0] = 0;
     if (N == 0) return;
-    const int32_t Q = (N + kXcds - 1) / kXcds;
-    // prefix sums, a tile of 1024 nodes at a time
-    int32_t carry_o = 0, carry_c = 0;
-    for (int32_t base = 0; base < N; base += 1024) {
-        const int32_t i = base + t;
-        const int32_t co = i < N ? cnt[(int64_t)i * kCounterStride] : 0;
-        const int32_t cc = i < N ? ccnt[i] : 0;
-        int32_t to, tc;
-        const int32_t io = block_scan_1024(co, tot, &to);
-        const int32_t ic = block_scan_1024(cc, tot, &tc);
-        if (i < N) {
-            srow[i + 1] = carry_o + io;
-            coff[i] = carry_c + ic - cc;
+    const int32_t nr = locality ? kXcds : 1;  // ranges
+    const int32_t Q = (N + nr - 1) / nr;       // nodes per range
+    // prefix sums over each thread's contiguous chunk of nodes
+    {
+        const int32_t ch = (N + 1023) / 1024;
+        const int32_t b = t * ch < N ? t * ch : N, e = b + ch < N ? b + ch : N;
+        int32_t so = 0, sc = 0;
+        for (int32_t i = b; i < e; ++i) {
+            so += cnt[(int64_t)i * kCounterStride];
+            sc += locality ? ccnt[i] : 0;
         }
-        carry_o += to;
-        carry_c += tc;
+        int32_t tt;
+        int32_t ro = block_scan_1024(so, tot, &tt) - so;
+        int32_t rc = block_scan_1024(sc, tot, &tt) - sc;
+        for (int32_t i = b; i < e; ++i) {
+            if (locality) {
+                const int32_t c = ccnt[i];
+                coff[i] = rc;
+                rc += c;
+            }
+            ro += cnt[(int64_t)i * kCounterStride];
+            srow[i + 1] = ro;
+        }
     }
     for (int k = t; k < kXcds * kDegBins; k += 1024) {
-        (&hin[0][0])[k] = 0;
-        (&hout[0][0])[k] = 0;
+        hin[k] = 0;
+        hout[k] = 0;
     }
     __syncthreads();  // srow and coff (global) and the cleared histograms are visible block-wide
-    auto place = [&](int32_t i, int32_t& x, int& bi, int& bo) {
-        int32_t g = coff[clampi(center[i], 0, N - 1)] + crank[i];
-        g = clampi(g, 0, N - 1);
-        x = g / Q;
-        int32_t e0 = clampi(row_ptr[i], 0, E), e1 = clampi(row_ptr[i + 1], e0, E);
-        bi = deg_bin(e1 - e0);
-        bo = deg_bin(srow[i + 1] - srow[i]);
+    auto place = [&](int32_t i, int& hi, int& ho) {
+        int32_t x = 0;
+        if (locality) {
+            const int32_t g = clampi(coff[clampi(center[i], 0, N - 1)] + crank[i], 0, N - 1);
+            x = g / Q;
+        }
+        const int32_t e0 = clampi(row_ptr[i], 0, E), e1 = clampi(row_ptr[i + 1], e0, E);
+        hi = x * kDegBins + deg_bin(e1 - e0);
+        ho = x * kDegBins + deg_bin(srow[i + 1] - srow[i]);
     };
     for (int32_t i = t; i < N; i += 1024) {
-        int32_t x;
-        int bi, bo;
-        place(i, x, bi, bo);
-        atomicAdd(&hin[x][bi], 1);
-        atomicAdd(&hout[x][bo], 1);
+        int hi, ho;
+        place(i, hi, ho);
+        atomicAdd(&hin[hi], 1);
+        atomicAdd(&hout[ho], 1);
     }
     __syncthreads();
-    // exclusive bin starts inside each range (one bin per thread)
-    for (int x = 0; x < kXcds; ++x) {
+    // exclusive bin starts inside each range: one scan over all kXcds*kDegBins
+    // bins (thread t owns bins 8t .. 8t+7, all in range t / 128), minus the
+    // range's own start
+    static_assert(kXcds * kDegBins == 8 * 1024, "eight bins per thread");
+    {
+        int32_t vi[8], vo[8], si = 0, so = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            vi[k] = hin[8 * t + k];
+            vo[k] = hout[8 * t + k];
+            si += vi[k];
+            so += vo[k];
+        }
         int32_t tt;
-        const int32_t vi = hin[x][t], vo = hout[x][t];
-        const int32_t si = block_scan_1024(vi, tot, &tt) - vi;
-        const int32_t so = block_scan_1024(vo, tot, &tt) - vo;
-        hin[x][t] = si;
-        hout[x][t] = so;
+        int32_t pi = block_scan_1024(si, tot, &tt) - si;
+        int32_t po = block_scan_1024(so, tot, &tt) - so;
+        if ((t & 127) == 0) {
+            xbase[0][t >> 7] = pi;
+            xbase[1][t >> 7] = po;
+        }
+        __syncthreads();
+        pi -= xbase[0][t >> 7];
+        po -= xbase[1][t >> 7];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            hin[8 * t + k] = pi;
+            hout[8 * t + k] = po;
+            pi += vi[k];
+            po += vo[k];
+        }
     }
     __syncthreads();
     for (int32_t i = t; i < N; i += 1024) {
-        int32_t x;
-        int bi, bo;
-        place(i, x, bi, bo);
-        rorder[x + kXcds * atomicAdd(&hin[x][bi], 1)] = i;
-        sorder[x + kXcds * atomicAdd(&hout[x][bo], 1)] = i;
+        int hi, ho;
+        place(i, hi, ho);
+        const int32_t x = hi / kDegBins;
+        rorder[x + nr * atomicAdd(&hin[hi], 1)] = i;
+        sorder[x + nr * atomicAdd(&hout[ho], 1)] = i;
     }
-    // blocks past the end of a short range are idle
-    for (int32_t b = t; b < kXcds * Q; b += 1024) {
-        const int32_t x = b % kXcds, s = b / kXcds;
+    // blocks past the end of a short range, or past N, are idle
+    const int32_t grid = kXcds * ((N + kXcds - 1) / kXcds);
+    for (int32_t b = t; b < grid; b += 1024) {
+        const int32_t x = b % nr, s = b / nr;
         const int32_t nx = clampi(N - x * Q, 0, Q);
         if (s >= nx) {
             rorder[b] = -1;
@@ -354,8 +395,8 @@ hipError_t launch_graph_prepare(int32_t N, int32_t E, const int32_t* row_ptr, co
         hipLaunchKernelGGL(k_prep_centers, dim3(b4), dim3(256), 0, s, N, E, row_ptr, src, loc, key1, center, crank,
                            ccnt, cnt);
     }
-    hipLaunchKernelGGL(k_prep_orders, dim3(1), dim3(1024), 0, s, N, E, row_ptr, cnt, ccnt, center, crank, srow, coff,
-                       rorder, sorder);
+    hipLaunchKernelGGL(k_prep_orders, dim3(1), dim3(1024), 0, s, N, E, loc, row_ptr, cnt, ccnt, center, crank, srow,
+                       coff, rorder, sorder);
     if (E > 0 && N > 0) {
         hipLaunchKernelGGL(k_prep_scatter, dim3(b4), dim3(256), 0, s, N, E, row_ptr, src, srow, cursor, uperm, usdst);
         hipLaunchKernelGGL(k_prep_sort, dim3(b4), dim3(256), 0, s, N, E, srow, uperm, usdst, perm, sdst);

@@ -28,8 +28,8 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // shared lines
 constexpr int kCounterStride = 32;
 
-// grid size of the convolution kernels: the nodes are split into kXcds
-// contiguous ranges of ceil(N / kXcds) (see the block orders below)
+// grid size of the convolution kernels: N rounded up to a multiple of kXcds
+// (the locality schedule splits the nodes into kXcds ranges of ceil(N/kXcds))
 inline int64_t conv_grid(int64_t N) { return kXcds * ((N + kXcds - 1) / kXcds); }
 
 inline WsLayout ws_layout(int64_t N, int64_t E)
@@ -136,7 +136,7 @@ hipError_t launch_node_grad(int32_t N, int32_t E, const int32_t* row_ptr, const 
                             float* gpos, hipStream_t s);
 
 // Graph preparation into `ws` (layout ws_layout(N, E)).  `locality` selects
-// the cluster-ordered block schedule (false: node-id order), see cgtp_graph.hip.
+// the cluster-ordered block schedule (false: longest first), see cgtp_graph.hip.
 hipError_t launch_graph_prepare(int32_t N, int32_t E, const int32_t* row_ptr, const int32_t* src, void* ws,
                                 bool locality, hipStream_t s);
 

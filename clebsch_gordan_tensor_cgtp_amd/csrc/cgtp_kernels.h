@@ -111,12 +111,32 @@ __device__ __forceinline__ T* at_lane(T* row, uint32_t lb)
     return (T*)((B*)row + lb);
 }
 
+// Read a value that is the same for every lane of the wave (a uniform
+// address) through the scalar data cache into scalar registers, where a vector
+// load would spend a vector register per lane and a read-first-lane move.
+// Only data no kernel writes while this one runs is read this way.
+template <class T>
+__device__ __forceinline__ T scalar_load(const T* p)
+{
+    return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // the lane's byte offset, re-defined at this point (an empty asm the
 // optimiser cannot see through) for at_lane
 __device__ __forceinline__ uint32_t lane_offset(uint32_t lb)
 {
     asm volatile("" : "+v"(lb));
     return lb;
+}
+
+// the channel count, re-defined at this point: the row offsets p*C of an
+// edge are then formed per edge with scalar arithmetic instead of being
+// hoisted out of the edge loop, where they would hold 30 scalar registers
+// and push others into spills
+__device__ __forceinline__ int32_t edge_stride(int32_t C)
+{
+    asm volatile("" : "+s"(C));
+    return C;
 }
 
 // ----------------------------------------------------------------------------
@@ -226,6 +246,15 @@ struct Tune {
     static constexpr bool fwd_prefetch = LM <= 2;
 };
 
+// acc += a*b, where the first term of a sum (`started` false, known at
+// compile time after unrolling) is a plain product: a product with a unit CG
+// coefficient then folds to a copy or a sign flip instead of an FMA with 0.
+__device__ __forceinline__ void mac(double& acc, double a, double b, bool& started)
+{
+    acc = started ? __builtin_fma(a, b, acc) : a * b;
+    started = true;
+}
+
 // An empty asm that takes a register value and hands it back: the optimiser
 // must materialise the value at that point and cannot match it with values
 // computed before it.  Used to keep accumulations in path order (otherwise
@@ -295,14 +324,14 @@ struct FwdEdge {
 // addressed as a row pointer (uniform when the whole wave works on one edge)
 // plus the lane's channel as an unsigned 32-bit index, which the compiler
 // turns into scalar-base + lane-offset loads without 64-bit vector adds.
-template <class Tb, bool SUB>
+template <class Tb, bool SUB, bool UNI>
 __device__ __forceinline__ void fwd_load(FwdEdge<Tb>& d, int32_t e, uint32_t chl, const FwdArgs& a,
                                          const Dims<Tb, SUB>& dm)
 {
     constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH;
-    const int32_t C = a.sh.C;
+    const int32_t C = edge_stride(a.sh.C);
     chl = lane_offset(chl);
-    int32_t j = a.src[e];
+    int32_t j = UNI ? scalar_load(a.src + e) : a.src[e];
     j = (uint32_t)j < (uint32_t)a.sh.N ? j : 0;  // a sender outside [0, N) breaks the CSR contract
     const float* wrow = a.W + (int64_t)e * (dm.P * C);
     static_for<0, P>([&](auto PI) {
@@ -316,6 +345,8 @@ __device__ __forceinline__ void fwd_load(FwdEdge<Tb>& d, int32_t e, uint32_t chl
     });
     const float* xrow = a.x + (int64_t)j * (dm.d_in * C);
     static_for<0, DIN>([&](auto K) { d.x[K] = *at_lane(xrow + Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_in) * C, chl); });
+    // (the edge's SH stay vector loads here: held across the prefetch, they
+    // would occupy scalar registers the contraction needs)
     const float* yp = a.Y + (int64_t)e * dm.d_sh;
     static_for<0, DSH>([&](auto K) { d.y[K] = yp[Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_sh)]; });
 }
@@ -340,10 +371,7 @@ __device__ __forceinline__ void fwd_slice(const float (&w)[Tb::P], const float (
                 static_for<0, K::d2>([&](auto B) {
                     constexpr int a = decltype(A)::value, b = decltype(B)::value;
                     constexpr double t = K::T(a, b, m3);
-                    if constexpr (t != 0.0) {
-                        z = __builtin_fma(t, xv[K::k1 + a] * yv[K::k2 + b], z);
-                        any = true;
-                    }
+                    if constexpr (t != 0.0) mac(z, t, xv[K::k1 + a] * yv[K::k2 + b], any);
                 });
             });
             if (any) acc[K::k3 + m3] = __builtin_fma(wd, z, acc[K::k3 + m3]);
@@ -384,14 +412,14 @@ __global__ void __launch_bounds__(256, (Tune<LM, LPE>::fwd_occ)) k_conv_fwd(FwdA
     // alternating two named buffers, which would spill at this occupancy)
     int32_t e = e0 + ps.s;
     FwdEdge<Tb> cur;
-    if (kPf && e < end) fwd_load<Tb, SUB>(cur, e, chl, a, dm);
+    if (kPf && e < end) fwd_load<Tb, SUB, LPE == 64>(cur, e, chl, a, dm);
     while (e < end) {
         const int32_t en = e + S;
         FwdEdge<Tb> nxt;
         if constexpr (kPf) {
-            if (en < end) fwd_load<Tb, SUB>(nxt, en, chl, a, dm);
+            if (en < end) fwd_load<Tb, SUB, LPE == 64>(nxt, en, chl, a, dm);
         } else {
-            fwd_load<Tb, SUB>(cur, e, chl, a, dm);
+            fwd_load<Tb, SUB, LPE == 64>(cur, e, chl, a, dm);
         }
         double yv[DSH];
         edge_sh<DSH, LPE>(cur.y, yv);
@@ -439,15 +467,15 @@ struct BwdEdge {
 // offset chl; a
 // corrupt entry (possible only if the view was not prepared for this graph)
 // is read as edge 0 / receiver 0 and flagged, never used out of bounds
-template <class Tb, bool SUB>
+template <class Tb, bool SUB, bool UNI>
 __device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, uint32_t chl, const BwdArgs& a,
                                          const Dims<Tb, SUB>& dm)
 {
     constexpr int P = Tb::P, DSH = Tb::DSH, DOUT = Tb::DOUT;
-    const int32_t C = a.sh.C;
+    const int32_t C = edge_stride(a.sh.C);
     chl = lane_offset(chl);
-    int32_t e = a.g.perm[q];
-    int32_t i = a.g.sdst[q];
+    int32_t e = UNI ? scalar_load(a.g.perm + q) : a.g.perm[q];
+    int32_t i = UNI ? scalar_load(a.g.sdst + q) : a.g.sdst[q];
     d.ok = (uint32_t)e < (uint32_t)a.sh.E && (uint32_t)i < (uint32_t)a.sh.N;
     if (!d.ok) e = i = 0;
     d.e = e;
@@ -464,7 +492,10 @@ __device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, uint32_t chl
     const float* grow = a.G + (int64_t)i * (dm.d_out * C);
     static_for<0, DOUT>([&](auto K) { d.g[K] = *at_lane(grow + Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_out) * C, chl); });
     const float* yp = a.Y + (int64_t)e * dm.d_sh;
-    static_for<0, DSH>([&](auto K) { d.y[K] = yp[Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_sh)]; });
+    static_for<0, DSH>([&](auto K) {
+        const float* p = yp + Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_sh);
+        d.y[K] = UNI ? scalar_load(p) : *p;
+    });
 }
 
 // One edge of the backward for one channel:
@@ -489,8 +520,12 @@ __device__ __forceinline__ void bwd_slice(const float (&w)[Tb::P], const float (
         constexpr int d2 = 2 * l2 + 1, k2 = l2 * l2;
         if constexpr ((l2 + 1) * (l2 + 1) <= Tb::DSH) {
             double dyb[d2];
+            bool dys[d2];
 #pragma unroll
-            for (int b = 0; b < d2; ++b) dyb[b] = 0.0;
+            for (int b = 0; b < d2; ++b) {
+                dyb[b] = 0.0;
+                dys[b] = false;
+            }
             static_for<0, Tb::P>([&](auto PI) {
                 constexpr int p = decltype(PI)::value;
                 using K = PathK<Tb, p>;
@@ -498,12 +533,18 @@ __device__ __forceinline__ void bwd_slice(const float (&w)[Tb::P], const float (
                     const double wd = (double)w[p];
                     static_for<0, K::d3>([&](auto M3) { opaque(gv[K::k3 + decltype(M3)::value]); });
                     double v[d2];
-                    static_for<0, d2>([&](auto B) { v[decltype(B)::value] = 0.0; });
+                    bool vs[d2];
+                    static_for<0, d2>([&](auto B) {
+                        v[decltype(B)::value] = 0.0;
+                        vs[decltype(B)::value] = false;
+                    });
                     double dw = 0.0;
+                    bool dws = false;
                     static_for<0, K::d1>([&](auto A) {
                         constexpr int a = decltype(A)::value;
                         if constexpr (K::ROW(a)) {
                             double h = 0.0;
+                            bool hs = false;
                             static_for<0, d2>([&](auto B) {
                                 constexpr int b = decltype(B)::value;
                                 double r = 0.0;
@@ -511,24 +552,21 @@ __device__ __forceinline__ void bwd_slice(const float (&w)[Tb::P], const float (
                                 static_for<0, K::d3>([&](auto M3) {
                                     constexpr int m3 = decltype(M3)::value;
                                     constexpr double t = K::T(a, b, m3);
-                                    if constexpr (t != 0.0) {
-                                        r = __builtin_fma(t, gv[K::k3 + m3], r);
-                                        any = true;
-                                    }
+                                    if constexpr (t != 0.0) mac(r, t, gv[K::k3 + m3], any);
                                 });
                                 if (any) {
-                                    h = __builtin_fma(r, yv[k2 + b], h);
-                                    v[b] = __builtin_fma(r, xv[K::k1 + a], v[b]);
+                                    mac(h, r, yv[k2 + b], hs);
+                                    mac(v[b], r, xv[K::k1 + a], vs[b]);
                                 }
                             });
                             dxa[K::k1 + a] = __builtin_fma(wd, h, dxa[K::k1 + a]);
-                            dw = __builtin_fma(xv[K::k1 + a], h, dw);
+                            mac(dw, xv[K::k1 + a], h, dws);
                         }
                     });
                     store_w(std::integral_constant<int, p>{}, dw);
                     static_for<0, d2>([&](auto B) {
                         constexpr int b = decltype(B)::value;
-                        if constexpr (K::COL2(b)) dyb[b] = __builtin_fma(wd, v[b], dyb[b]);
+                        if constexpr (K::COL2(b)) mac(dyb[b], wd, v[b], dys[b]);
                     });
                     // Pin this path's accumulator updates here: without it the
                     // compiler sinks every accumulation to the end of the edge
@@ -593,7 +631,7 @@ __device__ __forceinline__ double wave_sum_tile(const double* __restrict__ red, 
 
 // Edges per stream between two grad_Y combines of the two channel slices of
 // a C > 64 backward block.
-constexpr int kDyChunk = 16;
+constexpr int kDyChunk = 64;
 
 template <int LM, int LPE, int H, bool SUB>
 __global__ void __launch_bounds__(256, (Tune<LM, LPE>::bwd_occ)) k_conv_bwd(BwdArgs a)
@@ -649,19 +687,20 @@ __global__ void __launch_bounds__(256, (Tune<LM, LPE>::bwd_occ)) k_conv_bwd(BwdA
             const int32_t q = q0 + ps.s + S * t;
             if (q >= end) continue;  // uniform over the lanes of one edge
             BwdEdge<Tb> cur;
-            bwd_load<Tb, SUB>(cur, q, chl, a, dm);
+            bwd_load<Tb, SUB, LPE == 64>(cur, q, chl, a, dm);
             if constexpr (H == 2)
                 if (ps.h == 0 && lane == 0) eslot[ps.s * K + (t - t0)] = cur.ok ? cur.e : -1;
             if (!cur.ok) continue;
             double yv[DSH];
             edge_sh<DSH, LPE>(cur.y, yv);
-            float* dwrow = a.dW + (int64_t)cur.e * (dm.P * C);
+            const int32_t Ce = edge_stride(C);
+            float* dwrow = a.dW + (int64_t)cur.e * (dm.P * Ce);
             const uint32_t chs = lane_offset(chl);
             auto store_w = [&](auto PI, double dw) {
                 constexpr int p = decltype(PI)::value;
                 bool keep = want_dw && (full_c || live);
                 if constexpr (SUB) keep = keep && ((a.sh.active >> p) & 1);
-                if (keep) __builtin_nontemporal_store((float)dw, at_lane(dwrow + (SUB ? a.sh.woff[p] : p * C), chs));
+                if (keep) __builtin_nontemporal_store((float)dw, at_lane(dwrow + (SUB ? a.sh.woff[p] : p * Ce), chs));
             };
             if constexpr (kTile) {
                 // grad_Y partials go to this wave's LDS tile degree by degree

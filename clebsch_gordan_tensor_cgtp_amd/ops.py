@@ -39,10 +39,10 @@ class Plan:
     """Compiled CGTP convolution for degrees (l_in, l_sh, l_out) and C channels."""
 
     def __init__(self, l_in: int, l_sh: int, l_out: int, channels: int, validate: bool = False,
-                 locality: bool = True):
+                 locality: bool = False):
         lib = L.lib()
         h = ctypes.c_void_p()
-        flags = (L.CGTP_FLAG_VALIDATE if validate else 0) | (0 if locality else L.CGTP_FLAG_NO_LOCALITY)
+        flags = (L.CGTP_FLAG_VALIDATE if validate else 0) | (L.CGTP_FLAG_LOCALITY if locality else 0)
         L.check("cgtp_plan_create", lib.cgtp_plan_create(ctypes.byref(h), l_in, l_sh, l_out, channels, flags))
         self._h = h
         self.l_in, self.l_sh, self.l_out, self.channels = l_in, l_sh, l_out, channels

@@ -15,7 +15,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(HERE, "liboracle.so")
+# CGTP_ORACLE_LIB names another build of the oracle source (the mutation
+# tests load deliberately broken copies this way, on the CPU only)
+_LIB_PATH = os.environ.get("CGTP_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)
@@ -28,6 +30,8 @@ def _load():
     if _lib is not None:
         return _lib
     if not os.path.exists(_LIB_PATH):
+        if os.environ.get("CGTP_ORACLE_LIB"):
+            raise RuntimeError(f"oracle library {_LIB_PATH} (CGTP_ORACLE_LIB) not found")
         from .build import build_oracle
         build_oracle()
     lib = ctypes.CDLL(_LIB_PATH)

@@ -11,16 +11,17 @@ SRC = os.path.join(HERE, "cgtp_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build_oracle(verbose: bool = False) -> str:
-    """Compile ``cgtp_oracle.c`` into ``liboracle.so`` (always recompiles)."""
-    tmp = LIB + ".tmp"
+def build_oracle(verbose: bool = False, src: str = SRC, lib: str = LIB) -> str:
+    """Compile ``src`` (default ``cgtp_oracle.c``) into ``lib`` (default
+    ``liboracle.so``); always recompiles."""
+    tmp = lib + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-o", tmp, SRC, "-lm"]
+           "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

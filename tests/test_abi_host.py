@@ -54,7 +54,7 @@ def test_plan_create_arguments(L):
     # every degree triple up to 3 and every channel count from 1 to 128
     for (a, b, c) in ((0, 0, 0), (1, 1, 1), (2, 3, 2), (3, 0, 3), (0, 2, 2), (3, 3, 3)):
         for C in (1, 7, 8, 24, 64, 65, 96, 127, 128):
-            for flags in (0, L.CGTP_FLAG_VALIDATE, L.CGTP_FLAG_NO_LOCALITY):
+            for flags in (0, L.CGTP_FLAG_VALIDATE, L.CGTP_FLAG_LOCALITY):
                 st, h = _create(L, a, b, c, C, flags)
                 assert st == L.CGTP_OK, (a, b, c, C, flags)
                 assert L.lib().cgtp_plan_destroy(h) == L.CGTP_OK

@@ -129,15 +129,21 @@ def read_view(ws, N, E):
                                      ("rorder", s["grid"]), ("sorder", s["grid"]))}
 
 
-def check_schedule(order, deg, N, name):
-    """A block schedule: range x (blocks x, x+8, ...) holds n_x = clamp(N - xQ, 0, Q)
-    nodes, longest first, then idle blocks; every node exactly once."""
-    Q = (N + 7) // 8
-    assert order.shape[0] == 8 * Q
+def check_schedule(order, deg, N, name, locality):
+    """A block schedule over 8*ceil(N/8) blocks; every node exactly once.
+    Default: all nodes longest first, then idle blocks.  Locality: range x
+    (blocks x, x+8, ...) holds n_x = clamp(N - xQ, 0, Q) nodes, longest first,
+    then idle blocks."""
+    assert order.shape[0] == 8 * ((N + 7) // 8)
     got = order[order >= 0]
     np.testing.assert_array_equal(np.sort(got), np.arange(N), err_msg=name)
     assert np.all(order[order < 0] == -1)
     d = np.minimum(deg, 1023)
+    if not locality:
+        assert np.all(order[:N] >= 0)
+        assert np.all(np.diff(d[order[:N]]) <= 0), name
+        return
+    Q = (N + 7) // 8
     for x in range(8):
         part = order[x::8]
         nx = min(max(N - x * Q, 0), Q)
@@ -162,19 +168,15 @@ def test_graph_prepare(torch_dev, oracle, key, locality):
     np.testing.assert_array_equal(v["srow"], rs)
     np.testing.assert_array_equal(v["perm"], rp)
     np.testing.assert_array_equal(v["sdst"], rd)
-    check_schedule(v["rorder"], np.diff(g.row_ptr), N, "rorder")
-    check_schedule(v["sorder"], np.diff(rs), N, "sorder")
-    Q = (N + 7) // 8
-    xcd_of = np.empty(N, np.int64)
-    for x in range(8):
-        part = v["rorder"][x::8]
-        xcd_of[part[part >= 0]] = x
-    if not locality:
-        # node-id ranges
-        np.testing.assert_array_equal(xcd_of, np.arange(N) // Q)
-    else:
-        # clusters: every centre is a node within two hops, and each cluster's
-        # members occupy consecutive ranges
+    check_schedule(v["rorder"], np.diff(g.row_ptr), N, "rorder", locality)
+    check_schedule(v["sorder"], np.diff(rs), N, "sorder", locality)
+    if locality:
+        xcd_of = np.empty(N, np.int64)
+        for x in range(8):
+            part = v["rorder"][x::8]
+            xcd_of[part[part >= 0]] = x
+        # clusters: every centre is a valid node, and each cluster's members
+        # occupy consecutive ranges
         c = v["center"]
         assert np.all((c >= 0) & (c < N))
         for cc in np.unique(c):
