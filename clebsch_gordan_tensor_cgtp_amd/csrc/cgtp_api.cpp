@@ -127,6 +127,38 @@ cgtp_status_t ensure_prepared(const cgtp_plan_s* plan, int64_t N, int64_t E, con
     return prepare_into(plan, N, E, row_ptr, src, ws, stream);
 }
 
+// ---- the allocation-free backward's scratch --------------------------------
+// A file-scope device array holds the graph view for cgtp_conv_bwd_noalloc.
+// Host code never passes `scratch` itself (in host code the name is only a
+// stand-in for the symbol): each device's copy is looked up once with
+// hipGetSymbolAddress and that address is used.  The record of which graph
+// the scratch holds is a fixed per-device slot, so this path allocates
+// nothing, host or device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+struct ScratchSlot {
+    void* ptr;        // this device's copy of `scratch`, or nullptr until set up
+    bool valid;       // rec holds the graph last prepared into it
+    Prepared rec;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// this device's scratch address (looked up on its first use, with the device current)
+cgtp_status_t scratch_ptr(int dev, void** out)
+{
+    if (dev < 0 || dev >= kMaxDevices) return CGTP_ERR_UNSUPPORTED;
+    ScratchSlot& s = g_scratch[dev];
+    if (!s.ptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CGTP_ERR_HIP;
+        s.ptr = p;
+    }
+    *out = s.ptr;
+    return CGTP_OK;
+}
+
 cgtp::Shape launch_shape(const cgtp_plan_s* plan, int64_t N, int64_t E)
 {
     cgtp::Shape s = plan->shape;
@@ -323,6 +355,57 @@ cgtp_status_t cgtp_conv_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
     if (grad_Y && !aligned16(grad_Y)) return CGTP_ERR_INVALID_ARG;
     st = ensure_prepared(plan, n_nodes, n_edges, row_ptr, src, ws, stream);
     if (st != CGTP_OK) return st;
+    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges);
+    const char* base = (const char*)ws;
+    cgtp::BwdArgs a{};
+    a.sh = launch_shape(plan, n_nodes, n_edges);
+    a.g = cgtp::GraphView{(const int32_t*)(base + L.srow), (const int32_t*)(base + L.perm),
+                          (const int32_t*)(base + L.sdst), (const int32_t*)(base + L.rorder),
+                          (const int32_t*)(base + L.sorder)};
+    a.x = x;
+    a.Y = Y;
+    a.W = W;
+    a.G = grad_out;
+    a.dx = grad_x;
+    a.dW = grad_W;
+    a.dY = grad_Y;
+    return hip_status(plan->ks->bwd[plan->sub ? 1 : 0](a, stream));
+}
+
+cgtp_status_t cgtp_conv_bwd_noalloc(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
+                                    const int32_t* src, const float* x, const float* Y, const float* W,
+                                    const float* grad_out, float* grad_x, float* grad_W, float* grad_Y,
+                                    hipStream_t stream)
+{
+    cgtp_status_t st = check_graph_args(plan, n_nodes, n_edges, row_ptr, src);
+    if (st != CGTP_OK) return st;
+    if (cgtp::ws_layout(n_nodes, n_edges).total > kScratchBytes) return CGTP_ERR_WORKSPACE;
+    if ((!grad_x && !grad_W && !grad_Y) || n_nodes == 0) return CGTP_OK;
+    if (!x || !aligned16(x) || !grad_out || !aligned16(grad_out)) return CGTP_ERR_INVALID_ARG;
+    if (grad_x && !aligned16(grad_x)) return CGTP_ERR_INVALID_ARG;
+    if (n_edges > 0 && (!Y || !W || !aligned16(W) || !aligned16(Y))) return CGTP_ERR_INVALID_ARG;
+    if (grad_W && !aligned16(grad_W)) return CGTP_ERR_INVALID_ARG;
+    if (grad_Y && !aligned16(grad_Y)) return CGTP_ERR_INVALID_ARG;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CGTP_ERR_HIP;
+    void* ws = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        st = scratch_ptr(dev, &ws);
+        if (st != CGTP_OK) return st;
+        ScratchSlot& s = g_scratch[dev];
+        const bool loc = (plan->flags & CGTP_FLAG_LOCALITY) != 0;
+        const bool same = s.valid && s.rec.N == n_nodes && s.rec.E == n_edges && s.rec.row_ptr == row_ptr &&
+                          s.rec.src == src && s.rec.locality == loc;
+        if (!same) {
+            s.valid = false;
+            if (cgtp::launch_graph_prepare((int32_t)n_nodes, (int32_t)n_edges, row_ptr, src, ws, loc, stream) !=
+                hipSuccess)
+                return CGTP_ERR_HIP;
+            s.rec = Prepared{n_nodes, n_edges, row_ptr, src, loc, dev};
+            s.valid = true;
+        }
+    }
     const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges);
     const char* base = (const char*)ws;
     cgtp::BwdArgs a{};

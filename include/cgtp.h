@@ -176,6 +176,24 @@ cgtp_status_t cgtp_conv_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
                             const float* grad_out, float* grad_x, float* grad_W, float* grad_Y,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * backward exactly as cgtp_conv_bwd computes it, with the graph view held in
+ * a static device array of the library (64 MiB per GPU, held from the
+ * library's first use of that GPU until the process ends) instead of a
+ * caller workspace.  Calls no allocating routine.  The array is prepared by
+ * this call for (n_nodes, n_edges, row_ptr, src) unless the previous call on
+ * this GPU prepared it for the same four values (the record is by pointer, as
+ * for cgtp_graph_prepare); the preparation clears every counter it uses.
+ * Returns CGTP_ERR_WORKSPACE when the graph's workspace
+ * (cgtp_workspace_size) exceeds 64 MiB.  Every call on one GPU shares the
+ * array: calls that overlap on one GPU (other streams or threads) race and
+ * must be ordered by the caller. */
+cgtp_status_t cgtp_conv_bwd_noalloc(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
+                                    const int32_t* src, const float* x, const float* Y, const float* W,
+                                    const float* grad_out, float* grad_x, float* grad_W, float* grad_Y,
+                                    hipStream_t stream);
+
 /* Static text for a status code. */
 const char* cgtp_status_string(cgtp_status_t status);
 

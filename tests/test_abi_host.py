@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(L.lib(), n), n
         assert n in L.SIGNATURES, n
@@ -145,3 +145,19 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="libcgtp.so not found"):
         _lib.lib()
+
+
+def test_noalloc_backward_rejects_graphs_beyond_its_scratch(L):
+    """The allocation-free backward refuses a graph whose workspace exceeds
+    its 64 MiB static scratch, before any HIP call."""
+    lib = L.lib()
+    st, h = _create(L, 2, 2, 2, 128, 0)
+    fake = ctypes.c_void_p(4096)
+    b = ctypes.c_size_t()
+    lib.cgtp_workspace_size(h, 100000, 5_000_000, ctypes.byref(b))
+    assert b.value > 64 << 20
+    assert lib.cgtp_conv_bwd_noalloc(h, 100000, 5_000_000, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                     None) == L.CGTP_ERR_WORKSPACE
+    assert lib.cgtp_conv_bwd_noalloc(None, 10, 10, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                     None) == L.CGTP_ERR_INVALID_ARG
+    lib.cgtp_plan_destroy(h)
