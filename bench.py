@@ -339,7 +339,12 @@ def summarize(d, workload):
     from the rocprofv3 output under `d` (subdirectories named as in the
     commands each summary lists)."""
     cmd = f"python3 bench.py --workloads {workload} --steps 10 --warmup 2 --settle 0.3 --no-cpu-baseline"
-    find = lambda sub, f: os.path.join(d, sub, f)
+    def find(sub, f):
+        # the copy calibration may sit beside the workload's directory
+        for base in (d, os.path.dirname(os.path.normpath(d))):
+            if os.path.exists(os.path.join(base, sub, f)):
+                return os.path.join(base, sub, f)
+        return os.path.join(d, sub, f)
     out = os.path.join(ROOT, "profiles")
     sha = kernel_source_sha()
     # kernel trace
