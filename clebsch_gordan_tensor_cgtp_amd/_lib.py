@@ -23,6 +23,7 @@ CGTP_ERR_ALLOC = -5
 CGTP_ERR_GRAPH = -6
 CGTP_FLAG_VALIDATE = 1
 CGTP_FLAG_LOCALITY = 2
+CGTP_FLAG_SHARED_WEIGHTS = 4
 
 _c_i64 = ctypes.c_int64
 _vp = ctypes.c_void_p

@@ -33,7 +33,7 @@ struct cgtp_plan_s {
 
 namespace {
 
-constexpr unsigned kKnownFlags = CGTP_FLAG_VALIDATE | CGTP_FLAG_LOCALITY;
+constexpr unsigned kKnownFlags = CGTP_FLAG_VALIDATE | CGTP_FLAG_LOCALITY | CGTP_FLAG_SHARED_WEIGHTS;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -192,7 +192,8 @@ cgtp_status_t cgtp_plan_create(cgtp_plan_t* plan, int l_in, int l_sh, int l_out,
     p->channels = channels;
     p->flags = flags;
     p->lm = lm;
-    p->sub = !(l_in == lm && l_sh == lm && l_out == lm);
+    const bool shared = (flags & CGTP_FLAG_SHARED_WEIGHTS) != 0;
+    p->sub = shared || !(l_in == lm && l_sh == lm && l_out == lm);
     p->P = cgtp::cgmath::num_paths(l_in, l_sh, l_out);
     p->d_in = (l_in + 1) * (l_in + 1);
     p->d_sh = (l_sh + 1) * (l_sh + 1);
@@ -210,7 +211,8 @@ cgtp_status_t cgtp_plan_create(cgtp_plan_t* plan, int l_in, int l_sh, int l_out,
     s.d_in = p->d_in;
     s.d_sh = p->d_sh;
     s.d_out = p->d_out;
-    s.P = p->P;
+    s.P = shared ? 1 : p->P;
+    s.shared = shared ? 1 : 0;
     const int Pm = cgtp::cgmath::num_paths(lm, lm, lm);
     int q = 0;
     for (int k = 0; k < Pm; ++k) {
@@ -220,7 +222,8 @@ cgtp_status_t cgtp_plan_create(cgtp_plan_t* plan, int l_in, int l_sh, int l_out,
             s.active |= uint64_t(1) << k;
             p->super_index.push_back(k);
         }
-        s.woff[k] = std::min(q, p->P - 1) * channels;  // an inactive path reads a valid row (weight 0)
+        // an inactive path reads a valid row (and gets weight 0)
+        s.woff[k] = shared ? 0 : std::min(q, p->P - 1) * channels;
         if (mine) ++q;
     }
     p->shape = s;

@@ -72,12 +72,15 @@ struct GraphView {
 
 // Degrees and channel count of a launch.  The kernels are compiled for the
 // full path set of degree LM (l_in = l_sh = l_out = LM); a plan with smaller
-// degrees runs the paths it has (bit p of `active`) and reads its weight row
-// p at element offset woff[p] (a multiple of C) inside the edge's [P][C] row.
+// degrees runs the paths it has (bit p of `active`) and reads path p's
+// weights at element offset woff[p] (a multiple of C) inside the edge's
+// [P][C] weight row.  With path-weight sharing the row is [1][C]: every
+// woff[p] is 0 and the backward sums grad_W over the paths.
 struct Shape {
     int32_t N, E, C;
     int32_t d_in, d_sh, d_out;  // (l+1)^2 of the plan's degrees
-    int32_t P;                  // the plan's path count
+    int32_t P;                  // weight rows per edge: the plan's path count, or 1 when shared
+    int32_t shared;             // 1: one weight per edge and channel for every path
     uint64_t active;            // compiled paths the plan uses
     int32_t woff[kMaxPaths];    // weight offset of every compiled path (clamped for inactive ones)
 };

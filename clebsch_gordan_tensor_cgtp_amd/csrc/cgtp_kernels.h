@@ -238,12 +238,15 @@ struct Pos {
 // allocation must allow, and whether the forward loads the next edge's
 // operands before the current edge is computed.  Chosen so that no
 // specialisation spills vector registers (a spill costs far more than the
-// occupancy it buys).
+// occupancy it buys).  From degree 2 on the forward is bound by fp64 issue,
+// and the copies that rotate a prefetched edge into place cost more than the
+// latency they hide (measured: 4% slower on the 50,000-atom layer), so only
+// degree 1 prefetches.
 template <int LM, int LPE>
 struct Tune {
     static constexpr int fwd_occ = LM <= 2 ? 4 : 2;
     static constexpr int bwd_occ = LM == 1 || (LM == 2 && LPE == 64) ? 4 : (LM == 2 ? 3 : 2);
-    static constexpr bool fwd_prefetch = LM <= 2;
+    static constexpr bool fwd_prefetch = LM == 1;
 };
 
 // acc += a*b, where the first term of a sum (`started` false, known at
@@ -286,7 +289,7 @@ __device__ __forceinline__ void edge_sh(const float (&y)[DSH], double (&yv)[DSH]
 // degree set, run-time (from the Shape) for a SUB plan.
 template <class Tb, bool SUB>
 struct Dims {
-    int32_t d_in, d_sh, d_out, P;
+    int32_t d_in, d_sh, d_out, P;  // P: weight rows per edge
     __device__ __forceinline__ explicit Dims(const Shape& s)
     {
         if constexpr (SUB) {
@@ -696,11 +699,23 @@ __global__ void __launch_bounds__(256, (Tune<LM, LPE>::bwd_occ)) k_conv_bwd(BwdA
             const int32_t Ce = edge_stride(C);
             float* dwrow = a.dW + (int64_t)cur.e * (dm.P * Ce);
             const uint32_t chs = lane_offset(chl);
+            double dwsum = 0.0;  // shared path weights: grad_W is the sum over the paths
             auto store_w = [&](auto PI, double dw) {
                 constexpr int p = decltype(PI)::value;
                 bool keep = want_dw && (full_c || live);
-                if constexpr (SUB) keep = keep && ((a.sh.active >> p) & 1);
+                if constexpr (SUB) {
+                    keep = keep && ((a.sh.active >> p) & 1);
+                    if (a.sh.shared) {
+                        if (keep) dwsum += dw;
+                        return;
+                    }
+                }
                 if (keep) __builtin_nontemporal_store((float)dw, at_lane(dwrow + (SUB ? a.sh.woff[p] : p * Ce), chs));
+            };
+            auto store_shared = [&]() {
+                if constexpr (SUB)
+                    if (a.sh.shared && want_dw && (full_c || live))
+                        __builtin_nontemporal_store((float)dwsum, at_lane(dwrow, chs));
             };
             if constexpr (kTile) {
                 // grad_Y partials go to this wave's LDS tile degree by degree
@@ -710,6 +725,7 @@ __global__ void __launch_bounds__(256, (Tune<LM, LPE>::bwd_occ)) k_conv_bwd(BwdA
                     for (int b = 0; b < (int)(sizeof(dyb) / sizeof(double)); ++b)
                         tile[(k2 + b) * 64 + lane] = dyb[b];
                 });
+                store_shared();
                 // lanes past C hold channel 0's terms: they leave the sum
                 if (!full_c && !live)
 #pragma unroll
@@ -736,6 +752,7 @@ __global__ void __launch_bounds__(256, (Tune<LM, LPE>::bwd_occ)) k_conv_bwd(BwdA
                         if (want_dy && ps.cl == 0 && k2 + b < dm.d_sh) yp[k2 + b] = (float)v;
                     }
                 });
+                store_shared();
             }
         }
         if constexpr (H == 2) {

@@ -39,10 +39,12 @@ class Plan:
     """Compiled CGTP convolution for degrees (l_in, l_sh, l_out) and C channels."""
 
     def __init__(self, l_in: int, l_sh: int, l_out: int, channels: int, validate: bool = False,
-                 locality: bool = False):
+                 locality: bool = False, shared_weights: bool = False):
         lib = L.lib()
         h = ctypes.c_void_p()
-        flags = (L.CGTP_FLAG_VALIDATE if validate else 0) | (L.CGTP_FLAG_LOCALITY if locality else 0)
+        flags = (L.CGTP_FLAG_VALIDATE if validate else 0) | (L.CGTP_FLAG_LOCALITY if locality else 0) | \
+            (L.CGTP_FLAG_SHARED_WEIGHTS if shared_weights else 0)
+        self.shared_weights = shared_weights
         L.check("cgtp_plan_create", lib.cgtp_plan_create(ctypes.byref(h), l_in, l_sh, l_out, channels, flags))
         self._h = h
         self.l_in, self.l_sh, self.l_out, self.channels = l_in, l_sh, l_out, channels
@@ -54,6 +56,7 @@ class Plan:
         arr = (ctypes.c_int * (3 * self.num_paths))()
         L.check("cgtp_plan_info", lib.cgtp_plan_info(h, None, arr, None, None, None))
         self.paths = [tuple(arr[3 * q:3 * q + 3]) for q in range(self.num_paths)]
+        self.weight_rows = 1 if shared_weights else self.num_paths   # W is [E][weight_rows][C]
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -137,7 +140,7 @@ class Plan:
         _need(src, "src", torch.int32, (E,), dev)
         _need(x, "x", torch.float32, (N, self.dim_in, C), dev)
         _need(Y, "Y", torch.float32, (E, self.dim_sh), dev)
-        _need(W, "W", torch.float32, (E, self.num_paths, C), dev)
+        _need(W, "W", torch.float32, (E, self.weight_rows, C), dev)
         ws = self._workspace(ws, N, E, dev)
         if out is None:
             out = torch.empty((N, self.dim_out, C), dtype=torch.float32, device=dev)
@@ -155,13 +158,13 @@ class Plan:
         _need(src, "src", torch.int32, (E,), dev)
         _need(x, "x", torch.float32, (N, self.dim_in, C), dev)
         _need(Y, "Y", torch.float32, (E, self.dim_sh), dev)
-        _need(W, "W", torch.float32, (E, self.num_paths, C), dev)
+        _need(W, "W", torch.float32, (E, self.weight_rows, C), dev)
         _need(grad_out, "grad_out", torch.float32, (N, self.dim_out, C), dev)
         ws = self._workspace(ws, N, E, dev)
         if "dx" in want and grad_x is None:
             grad_x = torch.empty((N, self.dim_in, C), dtype=torch.float32, device=dev)
         if "dW" in want and grad_W is None:
-            grad_W = torch.empty((E, self.num_paths, C), dtype=torch.float32, device=dev)
+            grad_W = torch.empty((E, self.weight_rows, C), dtype=torch.float32, device=dev)
         if "dY" in want and grad_Y is None:
             grad_Y = torch.empty((E, self.dim_sh), dtype=torch.float32, device=dev)
         if "dx" not in want:
@@ -170,7 +173,7 @@ class Plan:
             grad_W = None
         if "dY" not in want:
             grad_Y = None
-        for t, n, s in ((grad_x, "grad_x", (N, self.dim_in, C)), (grad_W, "grad_W", (E, self.num_paths, C)),
+        for t, n, s in ((grad_x, "grad_x", (N, self.dim_in, C)), (grad_W, "grad_W", (E, self.weight_rows, C)),
                         (grad_Y, "grad_Y", (E, self.dim_sh))):
             if t is not None:
                 _need(t, n, torch.float32, s, dev)

@@ -32,7 +32,7 @@
  *       x, grad_x       [N][(l_in+1)^2][C]
  *       out, grad_out   [N][(l_out+1)^2][C]
  *       Y, grad_Y       [E][(l_sh+1)^2]
- *       W, grad_W       [E][P][C]
+ *       W, grad_W       [E][P][C]   ([E][C] with CGTP_FLAG_SHARED_WEIGHTS)
  *       r               [E][3]
  *   - the graph is a receiver-sorted CSR: row_ptr[N+1] (int32, row_ptr[0] = 0,
  *     non-decreasing, row_ptr[N] = E) and src[E] (int32 sender of each edge,
@@ -81,6 +81,11 @@ typedef enum {
  * per XCD, instead of longest segment first over the whole graph (results
  * are identical; only the L2 reuse of gathered rows and the balance differ). */
 #define CGTP_FLAG_LOCALITY 2u
+/* Path-weight sharing ("Tensor Decomposition Networks ...", rebuttal to
+ * reviewer oXft: one weight matrix shared across the paths): W and grad_W are
+ * [E][C], one weight per edge and channel used by every path, and
+ * grad_W[e][u] = sum over the paths of dL/dW[e][p][u]. */
+#define CGTP_FLAG_SHARED_WEIGHTS 4u
 
 /* Create a plan for degrees (l_in, l_sh, l_out) and C channels: the path list
  * under the selection rules (TDN rebuttal to S6y1, first answer) and the real

@@ -172,6 +172,24 @@ def conv_bwd(l_in, l_sh, l_out, row_ptr, src, x, Y, W, G, want=("dx", "dW", "dY"
     return dx, dW, dY
 
 
+def conv_fwd_shared(l_in, l_sh, l_out, row_ptr, src, x, Y, Ws):
+    """Forward with path-weight sharing: Ws [E][C] is every path's weight, so
+    this is conv_fwd with W[e][p][u] = Ws[e][u] (TDN rebuttal to oXft: one
+    weight matrix shared across paths)."""
+    P = paths(l_in, l_sh, l_out).shape[0]
+    Ws = _f64(Ws)
+    return conv_fwd(l_in, l_sh, l_out, row_ptr, src, x, Y, np.repeat(Ws[:, None, :], P, axis=1))
+
+
+def conv_bwd_shared(l_in, l_sh, l_out, row_ptr, src, x, Y, Ws, G, want=("dx", "dW", "dY")):
+    """Backward with path-weight sharing: by the chain rule through
+    W[e][p][u] = Ws[e][u], dWs[e][u] = sum over p of dW[e][p][u]."""
+    P = paths(l_in, l_sh, l_out).shape[0]
+    Ws = _f64(Ws)
+    dx, dW, dY = conv_bwd(l_in, l_sh, l_out, row_ptr, src, x, Y, np.repeat(Ws[:, None, :], P, axis=1), G, want)
+    return dx, (dW.sum(axis=1) if dW is not None else None), dY
+
+
 def graph_transpose(row_ptr, src):
     """(srow_ptr[N+1], perm[E], sdst[E]): edges stably grouped by sender."""
     row_ptr, src = _i64(row_ptr), _i64(src)

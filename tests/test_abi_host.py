@@ -47,14 +47,14 @@ def test_plan_create_arguments(L):
     assert L.lib().cgtp_plan_create(None, 2, 2, 2, 128, 0) == L.CGTP_ERR_INVALID_ARG
     assert _create(L, -1, 2, 2, 128, 0)[0] == L.CGTP_ERR_INVALID_ARG
     assert _create(L, 2, 2, 2, 0, 0)[0] == L.CGTP_ERR_INVALID_ARG
-    assert _create(L, 2, 2, 2, 128, 4)[0] == L.CGTP_ERR_INVALID_ARG      # unknown flag bit
+    assert _create(L, 2, 2, 2, 128, 8)[0] == L.CGTP_ERR_INVALID_ARG      # unknown flag bit
     assert _create(L, 4, 4, 4, 16, 0)[0] == L.CGTP_ERR_UNSUPPORTED
     assert _create(L, 1, 4, 1, 16, 0)[0] == L.CGTP_ERR_UNSUPPORTED
     assert _create(L, 2, 2, 2, 129, 0)[0] == L.CGTP_ERR_UNSUPPORTED     # more than 128 channels
     # every degree triple up to 3 and every channel count from 1 to 128
     for (a, b, c) in ((0, 0, 0), (1, 1, 1), (2, 3, 2), (3, 0, 3), (0, 2, 2), (3, 3, 3)):
         for C in (1, 7, 8, 24, 64, 65, 96, 127, 128):
-            for flags in (0, L.CGTP_FLAG_VALIDATE, L.CGTP_FLAG_LOCALITY):
+            for flags in (0, L.CGTP_FLAG_VALIDATE, L.CGTP_FLAG_LOCALITY, L.CGTP_FLAG_SHARED_WEIGHTS):
                 st, h = _create(L, a, b, c, C, flags)
                 assert st == L.CGTP_OK, (a, b, c, C, flags)
                 assert L.lib().cgtp_plan_destroy(h) == L.CGTP_OK

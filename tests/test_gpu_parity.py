@@ -527,3 +527,36 @@ def test_validate_flag_rejects_malformed_csr(torch_dev):
             plan.graph_prepare(torch.tensor(rp, dtype=torch.int32, device=dev),
                                torch.tensor(s, dtype=torch.int32, device=dev))
         assert ei.value.status == _lib.CGTP_ERR_GRAPH
+
+
+@pytest.mark.parametrize("li,ls,lo,C", [(1, 1, 1, 8), (2, 2, 2, 128), (2, 2, 2, 24), (3, 3, 3, 64), (2, 3, 2, 96),
+                                        (1, 2, 2, 16), (3, 3, 3, 128)])
+def test_conv_shared_path_weights(torch_dev, oracle, li, ls, lo, C):
+    """Path-weight sharing: W and grad_W are [E][C] (one weight per edge and
+    channel for every path); grad_W is the sum over the paths."""
+    torch, dev = torch_dev
+    from clebsch_gordan_tensor_cgtp_amd.ops import Plan
+    N = 70
+    rng = np.random.default_rng(li * 100 + ls * 10 + lo + C)
+    degs = rng.integers(0, 12, size=N)
+    degs[[0, 5]] = 0
+    degs[8] = N - 1
+    g = synth.random_graph(N, degs, seed=C + 5)
+    E = g.n_edges
+    x = rng.standard_normal((N, (li + 1) ** 2, C), dtype=np.float32)
+    Ws = rng.standard_normal((E, C), dtype=np.float32)
+    G = rng.standard_normal((N, (lo + 1) ** 2, C), dtype=np.float32)
+    Y = oracle.sh(ls, g.r).astype(np.float32)
+    _log(f"[shared] ({li},{ls},{lo}) C={C} N={N} E={E}")
+    plan = Plan(li, ls, lo, C, shared_weights=True)
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    rp, sr = T(g.row_ptr), T(g.src)
+    Wd = T(Ws[:, None, :])                 # [E][1][C]: one weight row per edge
+    out = plan.conv_fwd(rp, sr, T(x), T(Y), Wd).cpu().numpy()
+    dx, dW, dY = (t.cpu().numpy() for t in plan.conv_bwd(rp, sr, T(x), T(Y), Wd, T(G)))
+    assert dW.shape == (E, 1, C)
+    assert_parity(out, oracle.conv_fwd_shared(li, ls, lo, g.row_ptr, g.src, x, Y, Ws), "out")
+    rdx, rdW, rdY = oracle.conv_bwd_shared(li, ls, lo, g.row_ptr, g.src, x, Y, Ws, G)
+    assert_parity(dx, rdx, "dx")
+    assert_parity(dW[:, 0], rdW, "dW")
+    assert_parity(dY, rdY, "dY")

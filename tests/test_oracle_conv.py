@@ -244,3 +244,28 @@ def test_graph_transpose_is_stable_sort_by_sender(oracle):
         np.testing.assert_array_equal(srow, np.concatenate([[0], np.cumsum(np.bincount(g.src, minlength=N))]))
         recv = np.repeat(np.arange(N), np.diff(g.row_ptr))
         np.testing.assert_array_equal(sdst, recv[ref_perm])
+
+
+def test_shared_path_weights_gradient_is_the_path_sum(oracle):
+    """Path-weight sharing (TDN rebuttal to oXft): the forward is the uvu
+    forward with the same weight on every path, and the weight gradient is
+    the exact (linear) finite difference of <G, out> in the shared weights."""
+    from clebsch_gordan_tensor_cgtp_amd.synth import random_graph
+    rng = np.random.default_rng(21)
+    L, C, N = 2, 3, 9
+    g = random_graph(N, rng.integers(0, 5, size=N), seed=22)
+    E = g.n_edges
+    x = rng.normal(size=(N, 9, C))
+    Y = rng.normal(size=(E, 9))
+    Ws = rng.normal(size=(E, C))
+    G = rng.normal(size=(N, 9, C))
+    out = oracle.conv_fwd_shared(L, L, L, g.row_ptr, g.src, x, Y, Ws)
+    # by hand: the same weight on each of the 15 paths
+    np.testing.assert_allclose(out, oracle.conv_fwd(L, L, L, g.row_ptr, g.src, x, Y, np.repeat(Ws[:, None], 15, 1)),
+                               rtol=0, atol=0)
+    _, dWs, _ = oracle.conv_bwd_shared(L, L, L, g.row_ptr, g.src, x, Y, Ws, G)
+    d = rng.normal(size=Ws.shape)
+    h = 1e-3
+    Lp = (G * oracle.conv_fwd_shared(L, L, L, g.row_ptr, g.src, x, Y, Ws + h * d)).sum()
+    Lm = (G * oracle.conv_fwd_shared(L, L, L, g.row_ptr, g.src, x, Y, Ws - h * d)).sum()
+    assert (Lp - Lm) / (2 * h) == pytest.approx((dWs * d).sum(), rel=1e-10)
