@@ -53,6 +53,8 @@ def _load():
     lib.orc_conv_fwd.argtypes = [ctypes.c_int] * 4 + [ctypes.c_int64] * 2 + [_i64p, _i64p] + [_dp] * 4
     lib.orc_conv_bwd.restype = ctypes.c_int
     lib.orc_conv_bwd.argtypes = [ctypes.c_int] * 4 + [ctypes.c_int64] * 2 + [_i64p, _i64p] + [_dp] * 7
+    lib.orc_conv_bwd_bwd.restype = ctypes.c_int
+    lib.orc_conv_bwd_bwd.argtypes = [ctypes.c_int] * 4 + [ctypes.c_int64] * 2 + [_i64p, _i64p] + [_dp] * 11
     lib.orc_graph_transpose.restype = None
     lib.orc_graph_transpose.argtypes = [ctypes.c_int64, ctypes.c_int64, _i64p, _i64p, _i64p, _i64p, _i64p]
     lib.orc_num_threads.restype = ctypes.c_int
@@ -170,6 +172,28 @@ def conv_bwd(l_in, l_sh, l_out, row_ptr, src, x, Y, W, G, want=("dx", "dW", "dY"
     if rc != 0:
         raise ValueError("oracle: unsupported degrees")
     return dx, dW, dY
+
+
+def conv_bwd_bwd(l_in, l_sh, l_out, row_ptr, src, x, Y, W, G, ggx=None, ggY=None, ggW=None,
+                 want=("dx", "dY", "dW", "dG")):
+    """Gradients (dx, dY, dW, dG) of S = <ggx, dx> + <ggW, dW> + <ggY, dY>
+    with respect to x, Y, W and G, where (dx, dW, dY) = conv_bwd(x, Y, W, G);
+    a cotangent given as None is zero, an output not in ``want`` is None."""
+    row_ptr, src = _i64(row_ptr), _i64(src)
+    x, Y, W, G = _f64(x), _f64(Y), _f64(W), _f64(G)
+    cot = [_f64(a) if a is not None else None for a in (ggx, ggY, ggW)]
+    N, C = x.shape[0], x.shape[2]
+    E = src.shape[0]
+    dx = np.zeros_like(x) if "dx" in want else None
+    dY = np.zeros_like(Y) if "dY" in want else None
+    dW = np.zeros_like(W) if "dW" in want else None
+    dG = np.zeros_like(G) if "dG" in want else None
+    opt = lambda a: _p(a) if a is not None else None
+    rc = _load().orc_conv_bwd_bwd(l_in, l_sh, l_out, C, N, E, _p(row_ptr, _i64p), _p(src, _i64p), _p(x), _p(Y),
+                                  _p(W), _p(G), *(opt(a) for a in cot), opt(dx), opt(dY), opt(dW), opt(dG))
+    if rc != 0:
+        raise ValueError("oracle: unsupported degrees")
+    return dx, dY, dW, dG
 
 
 def conv_fwd_shared(l_in, l_sh, l_out, row_ptr, src, x, Y, Ws):

@@ -447,6 +447,138 @@ int orc_conv_bwd(int lin, int lsh, int lout, int C, int64_t N, int64_t E,
     return 0;
 }
 
+/* Double backward: the gradients of
+ *   S = <ggx, dx> + <ggW, dW> + <ggY, dY>,   (dx, dW, dY) = orc_conv_bwd(x, Y, W, G),
+ * with respect to x, Y, W and G (the higher-order derivatives LunaTP's
+ * abstract names; force training differentiates the backward again).  The
+ * loss L(x, Y, W, G) = <G, out(x, Y, W)> is linear in each argument, so
+ * S = L(ggx, Y, W, G) + L(x, Y, ggW, G) + L(x, ggY, W, G) and every term of
+ * its gradients is read off the single coupling c = T_p[m1][m2][m3] of one
+ * edge, path, channel and (m1, m2, m3):
+ *   dG[i][k3][u] += c (ggx Y W + x ggY W + x Y ggW)
+ *   dx[j][k1][u] += c (ggY W G + Y ggW G)
+ *   dW[e][p][u]  += c (ggx Y G + x ggY G)
+ *   dY[e][k2]    += sum_u c (ggx W G + x ggW G)
+ * (x, ggx at the sender j, G at the receiver i).  A NULL cotangent counts as
+ * zero; a NULL output is skipped; outputs are overwritten. */
+int orc_conv_bwd_bwd(int lin, int lsh, int lout, int C, int64_t N, int64_t E, const int64_t* row_ptr,
+                     const int64_t* src, const double* x, const double* Y, const double* W, const double* G,
+                     const double* ggx, const double* ggY, const double* ggW, double* dx, double* dY,
+                     double* dW, double* dG)
+{
+    orc_tables t;
+    if (orc_tables_make(lin, lsh, lout, &t)) return -1;
+    const int Din = (lin + 1) * (lin + 1), Dsh = (lsh + 1) * (lsh + 1);
+    const int Dout = (lout + 1) * (lout + 1);
+    const int P = t.P;
+    int64_t* dst = (int64_t*)malloc(sizeof(int64_t) * (E > 0 ? E : 1));
+    for (int64_t i = 0; i < N; ++i)
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) dst[e] = i;
+#define ORC_X(a) x[(j * Din + (a)) * C + u]
+#define ORC_GX(a) (ggx ? ggx[(j * Din + (a)) * C + u] : 0.0)
+#define ORC_Y(b) Y[e * Dsh + (b)]
+#define ORC_GY(b) (ggY ? ggY[e * Dsh + (b)] : 0.0)
+#define ORC_W W[(e * P + p) * C + u]
+#define ORC_GW (ggW ? ggW[(e * P + p) * C + u] : 0.0)
+#define ORC_G(c3) G[(i * Dout + (c3)) * C + u]
+    /* dG: per receiver */
+    if (dG) {
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t i = 0; i < N; ++i) {
+            double* o = dG + i * Dout * C;
+            for (int q = 0; q < Dout * C; ++q) o[q] = 0.0;
+            for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+                const int64_t j = src[e];
+                for (int p = 0; p < P; ++p) {
+                    const int l1 = t.paths[3 * p], l2 = t.paths[3 * p + 1], l3 = t.paths[3 * p + 2];
+                    for (int u = 0; u < C; ++u)
+                        for (int m1 = -l1; m1 <= l1; ++m1)
+                            for (int m2 = -l2; m2 <= l2; ++m2)
+                                for (int m3 = -l3; m3 <= l3; ++m3) {
+                                    double c = t.T[p][((m1 + l1) * (2 * l2 + 1) + (m2 + l2)) * (2 * l3 + 1) + (m3 + l3)];
+                                    if (c == 0.0) continue;
+                                    int a = l1 * l1 + l1 + m1, b = l2 * l2 + l2 + m2;
+                                    o[(l3 * l3 + l3 + m3) * C + u] +=
+                                        c * (ORC_GX(a) * ORC_Y(b) * ORC_W + ORC_X(a) * ORC_GY(b) * ORC_W +
+                                             ORC_X(a) * ORC_Y(b) * ORC_GW);
+                                }
+                }
+            }
+        }
+    }
+    /* dW, dY: per edge */
+    if (dW || dY) {
+#pragma omp parallel for schedule(dynamic, 64)
+        for (int64_t e = 0; e < E; ++e) {
+            const int64_t j = src[e], i = dst[e];
+            if (dY)
+                for (int q = 0; q < Dsh; ++q) dY[e * Dsh + q] = 0.0;
+            for (int p = 0; p < P; ++p) {
+                const int l1 = t.paths[3 * p], l2 = t.paths[3 * p + 1], l3 = t.paths[3 * p + 2];
+                for (int u = 0; u < C; ++u) {
+                    double acc = 0.0;
+                    for (int m1 = -l1; m1 <= l1; ++m1)
+                        for (int m2 = -l2; m2 <= l2; ++m2)
+                            for (int m3 = -l3; m3 <= l3; ++m3) {
+                                double c = t.T[p][((m1 + l1) * (2 * l2 + 1) + (m2 + l2)) * (2 * l3 + 1) + (m3 + l3)];
+                                if (c == 0.0) continue;
+                                int a = l1 * l1 + l1 + m1, b = l2 * l2 + l2 + m2, k3 = l3 * l3 + l3 + m3;
+                                acc += c * (ORC_GX(a) * ORC_Y(b) + ORC_X(a) * ORC_GY(b)) * ORC_G(k3);
+                                if (dY) dY[e * Dsh + b] += c * (ORC_GX(a) * ORC_W + ORC_X(a) * ORC_GW) * ORC_G(k3);
+                            }
+                    if (dW) dW[(e * P + p) * C + u] = acc;
+                }
+            }
+        }
+    }
+    /* dx: scattered over edges into per-thread buffers, then summed */
+    if (dx) {
+        const int64_t rowlen = (int64_t)Din * C;
+        for (int64_t q = 0; q < N * rowlen; ++q) dx[q] = 0.0;
+#pragma omp parallel
+        {
+            double* mine = dx;
+            int nthr = 1;
+#ifdef _OPENMP
+            nthr = omp_get_num_threads();
+#endif
+            if (nthr > 1) mine = (double*)calloc((size_t)(N * rowlen > 0 ? N * rowlen : 1), sizeof(double));
+#pragma omp for schedule(static)
+            for (int64_t e = 0; e < E; ++e) {
+                const int64_t j = src[e], i = dst[e];
+                for (int p = 0; p < P; ++p) {
+                    const int l1 = t.paths[3 * p], l2 = t.paths[3 * p + 1], l3 = t.paths[3 * p + 2];
+                    for (int u = 0; u < C; ++u)
+                        for (int m1 = -l1; m1 <= l1; ++m1)
+                            for (int m2 = -l2; m2 <= l2; ++m2)
+                                for (int m3 = -l3; m3 <= l3; ++m3) {
+                                    double c = t.T[p][((m1 + l1) * (2 * l2 + 1) + (m2 + l2)) * (2 * l3 + 1) + (m3 + l3)];
+                                    if (c == 0.0) continue;
+                                    int a = l1 * l1 + l1 + m1, b = l2 * l2 + l2 + m2, k3 = l3 * l3 + l3 + m3;
+                                    mine[(j * Din + a) * C + u] +=
+                                        c * (ORC_GY(b) * ORC_W + ORC_Y(b) * ORC_GW) * ORC_G(k3);
+                                }
+                }
+            }
+            if (nthr > 1) {
+#pragma omp critical
+                for (int64_t q = 0; q < N * rowlen; ++q) dx[q] += mine[q];
+                free(mine);
+            }
+        }
+    }
+#undef ORC_X
+#undef ORC_GX
+#undef ORC_Y
+#undef ORC_GY
+#undef ORC_W
+#undef ORC_GW
+#undef ORC_G
+    free(dst);
+    orc_tables_free(&t);
+    return 0;
+}
+
 /* Sender-sorted view of a receiver-sorted CSR (the graph preparation the
  * backward needs): a stable counting sort of the edges by sender.
  *   srow_ptr[N+1]  offsets of each sender's out-edges

@@ -269,3 +269,61 @@ def test_shared_path_weights_gradient_is_the_path_sum(oracle):
     Lp = (G * oracle.conv_fwd_shared(L, L, L, g.row_ptr, g.src, x, Y, Ws + h * d)).sum()
     Lm = (G * oracle.conv_fwd_shared(L, L, L, g.row_ptr, g.src, x, Y, Ws - h * d)).sum()
     assert (Lp - Lm) / (2 * h) == pytest.approx((dWs * d).sum(), rel=1e-10)
+
+
+def _dbl_case(oracle, Ls, seed, C=3, N=9):
+    from clebsch_gordan_tensor_cgtp_amd.synth import random_graph
+    li, ls, lo = Ls
+    rng = np.random.default_rng(seed)
+    g = random_graph(N, rng.integers(0, 5, size=N), seed=seed + 1)
+    E = g.n_edges
+    P = oracle.paths(li, ls, lo).shape[0]
+    arrs = dict(x=rng.normal(size=(N, (li + 1) ** 2, C)), Y=rng.normal(size=(E, (ls + 1) ** 2)),
+                W=rng.normal(size=(E, P, C)), G=rng.normal(size=(N, (lo + 1) ** 2, C)))
+    cot = dict(ggx=rng.normal(size=arrs["x"].shape), ggY=rng.normal(size=arrs["Y"].shape),
+               ggW=rng.normal(size=arrs["W"].shape))
+    return g, arrs, cot, rng
+
+
+def _S(oracle, Ls, g, a, cot):
+    dx, dW, dY = oracle.conv_bwd(*Ls, g.row_ptr, g.src, a["x"], a["Y"], a["W"], a["G"])
+    return (cot["ggx"] * dx).sum() + (cot["ggW"] * dW).sum() + (cot["ggY"] * dY).sum()
+
+
+@pytest.mark.parametrize("Ls", [(1, 1, 1), (2, 2, 2), (2, 1, 3), (3, 2, 1)])
+def test_double_backward_exact_finite_differences(oracle, Ls):
+    """The double backward is the gradient of S = <ggx,dx> + <ggW,dW> + <ggY,dY>
+    (dx, dW, dY from the pinned conv_bwd); S is linear in each of x, Y, W, G,
+    so central differences along any one of them are exact up to roundoff."""
+    g, a, cot, rng = _dbl_case(oracle, Ls, seed=sum(Ls) * 7)
+    got = dict(zip(("x", "Y", "W", "G"), oracle.conv_bwd_bwd(*Ls, g.row_ptr, g.src, a["x"], a["Y"], a["W"], a["G"],
+                                                             **cot)))
+    h = 1e-3
+    for name in ("x", "Y", "W", "G"):
+        d = rng.normal(size=a[name].shape)
+        ap, am = dict(a), dict(a)
+        ap[name] = a[name] + h * d
+        am[name] = a[name] - h * d
+        fd = (_S(oracle, Ls, g, ap, cot) - _S(oracle, Ls, g, am, cot)) / (2 * h)
+        assert fd == pytest.approx((got[name] * d).sum(), rel=1e-9, abs=1e-9), (Ls, name)
+
+
+def test_double_backward_identities_and_missing_cotangents(oracle):
+    Ls = (2, 2, 2)
+    g, a, cot, _ = _dbl_case(oracle, Ls, seed=3)
+    dx, dY, dW, dG = oracle.conv_bwd_bwd(*Ls, g.row_ptr, g.src, a["x"], a["Y"], a["W"], a["G"], **cot)
+    S = _S(oracle, Ls, g, a, cot)
+    # S is homogeneous of degree 1 in G, and grad_x does not depend on x
+    assert (dG * a["G"]).sum() == pytest.approx(S, rel=1e-12)
+    dx0, dW0, dY0 = oracle.conv_bwd(*Ls, g.row_ptr, g.src, a["x"], a["Y"], a["W"], a["G"])
+    assert (dx * a["x"]).sum() == pytest.approx((cot["ggW"] * dW0).sum() + (cot["ggY"] * dY0).sum(), rel=1e-12)
+    # a missing cotangent is zero
+    z = {k: np.zeros_like(v) for k, v in cot.items()}
+    for k in cot:
+        part = dict(z)
+        part[k] = cot[k]
+        with_none = {kk: (cot[kk] if kk == k else None) for kk in cot}
+        r1 = oracle.conv_bwd_bwd(*Ls, g.row_ptr, g.src, a["x"], a["Y"], a["W"], a["G"], **part)
+        r2 = oracle.conv_bwd_bwd(*Ls, g.row_ptr, g.src, a["x"], a["Y"], a["W"], a["G"], **with_none)
+        for u, v in zip(r1, r2):
+            np.testing.assert_array_equal(u, v)
