@@ -45,6 +45,7 @@ SIGNATURES = {
                                      _vp]),
     "cgtp_conv_bwd": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, ctypes.c_size_t, _vp]),
+    "cgtp_conv_bwd_bwd": (ctypes.c_int, [_vp, _c_i64, _c_i64] + [_vp] * 14 + [ctypes.c_size_t, _vp]),
     "cgtp_conv_bwd_noalloc": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                              _vp]),
     "cgtp_status_string": (ctypes.c_char_p, [ctypes.c_int]),

@@ -375,6 +375,63 @@ cgtp_status_t cgtp_conv_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
     return hip_status(plan->ks->bwd[plan->sub ? 1 : 0](a, stream));
 }
 
+cgtp_status_t cgtp_conv_bwd_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
+                                const int32_t* src, const float* x, const float* Y, const float* W,
+                                const float* grad_out, const float* gg_x, const float* gg_Y, const float* gg_W,
+                                float* dd_x, float* dd_Y, float* dd_W, float* dd_out, void* ws, size_t ws_bytes,
+                                hipStream_t stream)
+{
+    cgtp_status_t st = check_graph_args(plan, n_nodes, n_edges, row_ptr, src);
+    if (st != CGTP_OK) return st;
+    st = check_ws(n_nodes, n_edges, ws, ws_bytes);
+    if (st != CGTP_OK) return st;
+    if ((!dd_x && !dd_Y && !dd_W && !dd_out) || n_nodes == 0) return CGTP_OK;
+    if (!x || !aligned16(x) || !grad_out || !aligned16(grad_out)) return CGTP_ERR_INVALID_ARG;
+    if (n_edges > 0 && (!Y || !W || !aligned16(W) || !aligned16(Y))) return CGTP_ERR_INVALID_ARG;
+    for (const void* p : {(const void*)gg_x, (const void*)gg_Y, (const void*)gg_W, (const void*)dd_x,
+                          (const void*)dd_Y, (const void*)dd_W, (const void*)dd_out})
+        if (p && !aligned16(p)) return CGTP_ERR_INVALID_ARG;
+    st = ensure_prepared(plan, n_nodes, n_edges, row_ptr, src, ws, stream);
+    if (st != CGTP_OK) return st;
+    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges);
+    const char* base = (const char*)ws;
+    if (dd_out) {
+        cgtp::FwdArgs a{};
+        a.sh = launch_shape(plan, n_nodes, n_edges);
+        a.row_ptr = row_ptr;
+        a.src = src;
+        a.rorder = (const int32_t*)(base + L.rorder);
+        a.x = x;
+        a.Y = Y;
+        a.W = W;
+        a.out = dd_out;
+        a.ggx = gg_x;
+        a.ggY = gg_Y;
+        a.ggW = gg_W;
+        st = hip_status(plan->ks->fwd_dbl(a, stream));
+        if (st != CGTP_OK) return st;
+    }
+    if (dd_x || dd_Y || dd_W) {
+        cgtp::BwdArgs a{};
+        a.sh = launch_shape(plan, n_nodes, n_edges);
+        a.g = cgtp::GraphView{(const int32_t*)(base + L.srow), (const int32_t*)(base + L.perm),
+                              (const int32_t*)(base + L.sdst), (const int32_t*)(base + L.rorder),
+                              (const int32_t*)(base + L.sorder)};
+        a.x = x;
+        a.Y = Y;
+        a.W = W;
+        a.G = grad_out;
+        a.dx = dd_x;
+        a.dW = dd_W;
+        a.dY = dd_Y;
+        a.ggx = gg_x;
+        a.ggY = gg_Y;
+        a.ggW = gg_W;
+        st = hip_status(plan->ks->bwd_dbl(a, stream));
+    }
+    return st;
+}
+
 cgtp_status_t cgtp_conv_bwd_noalloc(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
                                     const int32_t* src, const float* x, const float* Y, const float* W,
                                     const float* grad_out, float* grad_x, float* grad_W, float* grad_Y,

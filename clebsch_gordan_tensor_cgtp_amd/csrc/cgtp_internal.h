@@ -87,6 +87,8 @@ struct Shape {
 
 enum GradMask : int { kGradX = 1, kGradW = 2, kGradY = 4 };
 
+// The double-backward launches read the cotangents ggx, ggY, ggW as well
+// (nullptr: zero); the others leave them unset.
 struct FwdArgs {
     Shape sh;
     const int32_t* row_ptr;
@@ -96,6 +98,9 @@ struct FwdArgs {
     const float* Y;
     const float* W;
     float* out;
+    const float* ggx;
+    const float* ggY;
+    const float* ggW;
 };
 
 struct BwdArgs {
@@ -108,6 +113,9 @@ struct BwdArgs {
     float* dx;
     float* dW;
     float* dY;
+    const float* ggx;
+    const float* ggY;
+    const float* ggW;
 };
 
 using ShLaunch = hipError_t (*)(int64_t E, const float* r, float* Y, hipStream_t s);
@@ -121,6 +129,11 @@ struct KernelSet {
     int lm, lpe, h;
     FwdLaunch fwd[2];  // [0]: complete degree set; [1]: SUB (smaller or mixed degrees)
     BwdLaunch bwd[2];
+    // double backward (every degree set, SUB form): fwd_dbl writes the
+    // gradient for grad_out into `out`, bwd_dbl those for x, W and Y into
+    // dx, dW and dY
+    FwdLaunch fwd_dbl;
+    BwdLaunch bwd_dbl;
 };
 
 // Kernels for compiled degree lm and channel count C, or nullptr.

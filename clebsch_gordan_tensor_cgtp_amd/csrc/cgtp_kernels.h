@@ -242,11 +242,14 @@ struct Pos {
 // and the copies that rotate a prefetched edge into place cost more than the
 // latency they hide (measured: 4% slower on the 50,000-atom layer), so only
 // degree 1 prefetches.
+// The double-backward kernels carry a second set of operands (the
+// cotangents) and run at half the occupancy.
 template <int LM, int LPE>
 struct Tune {
     static constexpr int fwd_occ = LM <= 2 ? 4 : 2;
     static constexpr int bwd_occ = LM == 1 || (LM == 2 && LPE == 64) ? 4 : (LM == 2 ? 3 : 2);
     static constexpr bool fwd_prefetch = LM == 1;
+    static constexpr int dbl_occ = LM == 1 ? 4 : (LM == 2 ? 2 : 1);
 };
 
 // acc += a*b, where the first term of a sum (`started` false, known at
@@ -384,13 +387,104 @@ __device__ __forceinline__ void fwd_slice(const float (&w)[Tb::P], const float (
     });
 }
 
-template <int LM, int LPE, int H, bool SUB>
-__global__ void __launch_bounds__(256, (Tune<LM, LPE>::fwd_occ)) k_conv_fwd(FwdArgs a)
+// ---- double backward, receiver side ----------------------------------------
+// The gradient of S = <ggx, grad_x> + <ggW, grad_W> + <ggY, grad_Y> with
+// respect to grad_out is the forward applied to the three products that are
+// linear in one cotangent each:
+//   d_out[i] = sum_e W (ggx_j (x) Y) + W (x_j (x) ggY) + ggW (x_j (x) Y).
+// It runs on the forward's work decomposition with these operands added.
+template <class Tb>
+struct FwdEdgeD : FwdEdge<Tb> {
+    float gw[Tb::P], gx[Tb::DIN], gy[Tb::DSH];
+};
+
+// the cotangent rows of edge e (zero where the caller passed none)
+template <class Tb, bool SUB, bool UNI>
+__device__ __forceinline__ void fwd_load_dbl(FwdEdgeD<Tb>& d, int32_t e, uint32_t chl, const FwdArgs& a,
+                                             const Dims<Tb, SUB>& dm)
+{
+    fwd_load<Tb, SUB, UNI>(d, e, chl, a, dm);
+    constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH;
+    const int32_t C = edge_stride(a.sh.C);
+    chl = lane_offset(chl);
+    int32_t j = UNI ? scalar_load(a.src + e) : a.src[e];
+    j = (uint32_t)j < (uint32_t)a.sh.N ? j : 0;
+    if (a.ggW) {
+        const float* wrow = a.ggW + (int64_t)e * (dm.P * C);
+        static_for<0, P>([&](auto PI) {
+            constexpr int p = decltype(PI)::value;
+            if constexpr (SUB) {
+                const float v = __builtin_nontemporal_load(at_lane(wrow + a.sh.woff[p], chl));
+                d.gw[p] = ((a.sh.active >> p) & 1) ? v : 0.0f;
+            } else {
+                d.gw[p] = __builtin_nontemporal_load(at_lane(wrow + p * C, chl));
+            }
+        });
+    } else {
+#pragma unroll
+        for (int p = 0; p < P; ++p) d.gw[p] = 0.0f;
+    }
+    if (a.ggx) {
+        const float* xrow = a.ggx + (int64_t)j * (dm.d_in * C);
+        static_for<0, DIN>([&](auto K) { d.gx[K] = *at_lane(xrow + Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_in) * C, chl); });
+    } else {
+#pragma unroll
+        for (int k = 0; k < DIN; ++k) d.gx[k] = 0.0f;
+    }
+    if (a.ggY) {
+        const float* yp = a.ggY + (int64_t)e * dm.d_sh;
+        static_for<0, DSH>([&](auto K) { d.gy[K] = yp[Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_sh)]; });
+    } else {
+#pragma unroll
+        for (int k = 0; k < DSH; ++k) d.gy[k] = 0.0f;
+    }
+}
+
+// acc[l3,m3] += sum_p sum_{a,b} T_p[a][b][m3] (W_p (ggx[a] y[b] + x[a] ggy[b]) + ggW_p x[a] y[b])
+template <class Tb>
+__device__ __forceinline__ void fwd_slice_dbl(const FwdEdgeD<Tb>& d, const double (&yv)[Tb::DSH],
+                                              const double (&gyv)[Tb::DSH], double (&acc)[Tb::DOUT])
+{
+    double xv[Tb::DIN], gxv[Tb::DIN];
+#pragma unroll
+    for (int k = 0; k < Tb::DIN; ++k) {
+        xv[k] = (double)d.x[k];
+        gxv[k] = (double)d.gx[k];
+    }
+    static_for<0, Tb::P>([&](auto PI) {
+        constexpr int p = decltype(PI)::value;
+        using K = PathK<Tb, p>;
+        const double wd = (double)d.w[p], gwd = (double)d.gw[p];
+        static_for<0, K::d3>([&](auto M3) {
+            constexpr int m3 = decltype(M3)::value;
+            double z1 = 0.0, z2 = 0.0;
+            bool any1 = false, any2 = false;
+            static_for<0, K::d1>([&](auto A) {
+                static_for<0, K::d2>([&](auto B) {
+                    constexpr int a = decltype(A)::value, b = decltype(B)::value;
+                    constexpr double t = K::T(a, b, m3);
+                    if constexpr (t != 0.0) {
+                        const double x = xv[K::k1 + a], y = yv[K::k2 + b];
+                        mac(z1, t, __builtin_fma(x, gyv[K::k2 + b], gxv[K::k1 + a] * y), any1);
+                        mac(z2, t, x * y, any2);
+                    }
+                });
+            });
+            if (any1) acc[K::k3 + m3] = __builtin_fma(wd, z1, __builtin_fma(gwd, z2, acc[K::k3 + m3]));
+        });
+        static_for<0, K::d3>([&](auto M3) { opaque(acc[K::k3 + decltype(M3)::value]); });
+    });
+}
+
+template <int LM, int LPE, int H, bool SUB, bool DBL = false>
+__global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_occ : Tune<LM, LPE>::fwd_occ))
+    k_conv_fwd(FwdArgs a)
 {
     using Tb = cgmath::Tables<LM, LM, LM>;
     using Gm = Geo<LPE, H>;
     constexpr int DSH = Tb::DSH, DOUT = Tb::DOUT, S = Gm::S, CP = Gm::CP;
-    constexpr bool kPf = Tune<LM, LPE>::fwd_prefetch;
+    constexpr bool kPf = Tune<LM, LPE>::fwd_prefetch && !DBL;
+    using Edge = std::conditional_t<DBL, FwdEdgeD<Tb>, FwdEdge<Tb>>;
     // LDS: the streams' partial sums [stream][k][channel]
     __shared__ double red[S * DOUT * CP];
 
@@ -414,19 +508,27 @@ __global__ void __launch_bounds__(256, (Tune<LM, LPE>::fwd_occ)) k_conv_fwd(FwdA
     // is computed (the copy `cur = nxt` costs fewer registers than
     // alternating two named buffers, which would spill at this occupancy)
     int32_t e = e0 + ps.s;
-    FwdEdge<Tb> cur;
+    Edge cur;
     if (kPf && e < end) fwd_load<Tb, SUB, LPE == 64>(cur, e, chl, a, dm);
     while (e < end) {
         const int32_t en = e + S;
-        FwdEdge<Tb> nxt;
+        Edge nxt;
         if constexpr (kPf) {
             if (en < end) fwd_load<Tb, SUB, LPE == 64>(nxt, en, chl, a, dm);
+        } else if constexpr (DBL) {
+            fwd_load_dbl<Tb, SUB, LPE == 64>(cur, e, chl, a, dm);
         } else {
             fwd_load<Tb, SUB, LPE == 64>(cur, e, chl, a, dm);
         }
         double yv[DSH];
         edge_sh<DSH, LPE>(cur.y, yv);
-        fwd_slice<Tb>(cur.w, cur.x, yv, acc);
+        if constexpr (DBL) {
+            double gyv[DSH];
+            edge_sh<DSH, LPE>(cur.gy, gyv);
+            fwd_slice_dbl<Tb>(cur, yv, gyv, acc);
+        } else {
+            fwd_slice<Tb>(cur.w, cur.x, yv, acc);
+        }
         if constexpr (kPf) cur = nxt;
         e = en;
     }
@@ -447,11 +549,11 @@ __global__ void __launch_bounds__(256, (Tune<LM, LPE>::fwd_occ)) k_conv_fwd(FwdA
     }
 }
 
-template <int LM, int LPE, int H, bool SUB>
+template <int LM, int LPE, int H, bool SUB, bool DBL = false>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s)
 {
     if (a.sh.N == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_conv_fwd<LM, LPE, H, SUB>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_conv_fwd<LM, LPE, H, SUB, DBL>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -588,6 +690,138 @@ __device__ __forceinline__ void bwd_slice(const float (&w)[Tb::P], const float (
     });
 }
 
+// ---- double backward, sender side -------------------------------------------
+// The gradients of S = <ggx, grad_x> + <ggW, grad_W> + <ggY, grad_Y> with
+// respect to x, W and Y, for one edge and channel, with R_p as in bwd_slice:
+//   h_p = R_p y,  k_p = R_p ggy
+//   d_x[l1,a] += W_p k_p[a] + ggW_p h_p[a]
+//   d_W_p      = sum_a ggx[l1,a] h_p[a] + x[l1,a] k_p[a]
+//   d_y[l2,b] += sum_a R_p[a][b] (W_p ggx[l1,a] + ggW_p x[l1,a])
+// They run on the backward's work decomposition with these operands added.
+template <class Tb>
+struct BwdEdgeD : BwdEdge<Tb> {
+    float gw[Tb::P], gy[Tb::DSH];
+};
+
+template <class Tb, bool SUB, bool UNI>
+__device__ __forceinline__ void bwd_load_dbl(BwdEdgeD<Tb>& d, int32_t q, uint32_t chl, const BwdArgs& a,
+                                             const Dims<Tb, SUB>& dm)
+{
+    bwd_load<Tb, SUB, UNI>(d, q, chl, a, dm);
+    constexpr int P = Tb::P, DSH = Tb::DSH;
+    const int32_t C = edge_stride(a.sh.C);
+    chl = lane_offset(chl);
+    const int32_t e = d.e;
+    if (a.ggW) {
+        const float* wrow = a.ggW + (int64_t)e * (dm.P * C);
+        static_for<0, P>([&](auto PI) {
+            constexpr int p = decltype(PI)::value;
+            if constexpr (SUB) {
+                const float v = __builtin_nontemporal_load(at_lane(wrow + a.sh.woff[p], chl));
+                d.gw[p] = ((a.sh.active >> p) & 1) ? v : 0.0f;
+            } else {
+                d.gw[p] = __builtin_nontemporal_load(at_lane(wrow + p * C, chl));
+            }
+        });
+    } else {
+#pragma unroll
+        for (int p = 0; p < P; ++p) d.gw[p] = 0.0f;
+    }
+    if (a.ggY) {
+        const float* yp = a.ggY + (int64_t)e * dm.d_sh;
+        static_for<0, DSH>([&](auto K) {
+            const float* p = yp + Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_sh);
+            d.gy[K] = UNI ? scalar_load(p) : *p;
+        });
+    } else {
+#pragma unroll
+        for (int k = 0; k < DSH; ++k) d.gy[k] = 0.0f;
+    }
+}
+
+template <class Tb, class StoreW, class FlushY>
+__device__ __forceinline__ void bwd_slice_dbl(const BwdEdgeD<Tb>& d, const double (&yv)[Tb::DSH],
+                                              const double (&gyv)[Tb::DSH], const double (&xv)[Tb::DIN],
+                                              const double (&gxv)[Tb::DIN], double (&dxa)[Tb::DIN],
+                                              StoreW&& store_w, FlushY&& flush_y)
+{
+    constexpr int DOUT = Tb::DOUT;
+    double gv[DOUT];
+#pragma unroll
+    for (int k = 0; k < DOUT; ++k) gv[k] = (double)d.g[k];
+    static_for<0, 4>([&](auto L2I) {
+        constexpr int l2 = decltype(L2I)::value;
+        constexpr int d2 = 2 * l2 + 1, k2 = l2 * l2;
+        if constexpr ((l2 + 1) * (l2 + 1) <= Tb::DSH) {
+            double dyb[d2];
+            bool dys[d2];
+#pragma unroll
+            for (int b = 0; b < d2; ++b) {
+                dyb[b] = 0.0;
+                dys[b] = false;
+            }
+            static_for<0, Tb::P>([&](auto PI) {
+                constexpr int p = decltype(PI)::value;
+                using K = PathK<Tb, p>;
+                if constexpr (K::l2 == l2) {
+                    const double wd = (double)d.w[p], gwd = (double)d.gw[p];
+                    static_for<0, K::d3>([&](auto M3) { opaque(gv[K::k3 + decltype(M3)::value]); });
+                    double v[d2];
+                    bool vs[d2];
+                    static_for<0, d2>([&](auto B) {
+                        v[decltype(B)::value] = 0.0;
+                        vs[decltype(B)::value] = false;
+                    });
+                    double dw = 0.0;
+                    bool dws = false;
+                    static_for<0, K::d1>([&](auto A) {
+                        constexpr int a = decltype(A)::value;
+                        if constexpr (K::ROW(a)) {
+                            const double xm = __builtin_fma(gwd, xv[K::k1 + a], wd * gxv[K::k1 + a]);
+                            double h = 0.0, k = 0.0;
+                            bool hs = false, ks = false;
+                            static_for<0, d2>([&](auto B) {
+                                constexpr int b = decltype(B)::value;
+                                double r = 0.0;
+                                bool any = false;
+                                static_for<0, K::d3>([&](auto M3) {
+                                    constexpr int m3 = decltype(M3)::value;
+                                    constexpr double t = K::T(a, b, m3);
+                                    if constexpr (t != 0.0) mac(r, t, gv[K::k3 + m3], any);
+                                });
+                                if (any) {
+                                    mac(h, r, yv[k2 + b], hs);
+                                    mac(k, r, gyv[k2 + b], ks);
+                                    mac(v[b], r, xm, vs[b]);
+                                }
+                            });
+                            dxa[K::k1 + a] = __builtin_fma(wd, k, __builtin_fma(gwd, h, dxa[K::k1 + a]));
+                            mac(dw, gxv[K::k1 + a], h, dws);
+                            dw = __builtin_fma(xv[K::k1 + a], k, dw);
+                        }
+                    });
+                    store_w(std::integral_constant<int, p>{}, dw);
+                    static_for<0, d2>([&](auto B) {
+                        constexpr int b = decltype(B)::value;
+                        if constexpr (K::COL2(b)) {
+                            dyb[b] = dys[b] ? dyb[b] + v[b] : v[b];
+                            dys[b] = true;
+                        }
+                    });
+                    static_for<0, K::d1>([&](auto A) {
+                        if constexpr (K::ROW(decltype(A)::value)) opaque(dxa[K::k1 + decltype(A)::value]);
+                    });
+                    static_for<0, d2>([&](auto B) {
+                        if constexpr (K::COL2(decltype(B)::value)) opaque(dyb[decltype(B)::value]);
+                    });
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            });
+            flush_y(std::integral_constant<int, k2>{}, dyb);
+        }
+    });
+}
+
 // quad_perm DPP move of a double (both halves), CTRL a quad_perm selector
 template <int CTRL>
 __device__ __forceinline__ double dpp_quad(double v)
@@ -636,8 +870,9 @@ __device__ __forceinline__ double wave_sum_tile(const double* __restrict__ red, 
 // a C > 64 backward block.
 constexpr int kDyChunk = 64;
 
-template <int LM, int LPE, int H, bool SUB>
-__global__ void __launch_bounds__(256, (Tune<LM, LPE>::bwd_occ)) k_conv_bwd(BwdArgs a)
+template <int LM, int LPE, int H, bool SUB, bool DBL = false>
+__global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_occ : Tune<LM, LPE>::bwd_occ))
+    k_conv_bwd(BwdArgs a)
 {
     using Tb = cgmath::Tables<LM, LM, LM>;
     using Gm = Geo<LPE, H>;
@@ -669,13 +904,22 @@ __global__ void __launch_bounds__(256, (Tune<LM, LPE>::bwd_occ)) k_conv_bwd(BwdA
     const int32_t j = a.g.sorder[blockIdx.x];
     if ((uint32_t)j >= (uint32_t)N) return;  // idle block (or an unprepared schedule)
 
+    using Edge = std::conditional_t<DBL, BwdEdgeD<Tb>, BwdEdge<Tb>>;
     double xv[DIN], dxa[DIN];
+    double gxv[DBL ? DIN : 1];  // the sender's cotangent row ggx[j] (double backward)
     {
         const float* xrow = a.x + (int64_t)j * (dm.d_in * C);
         static_for<0, DIN>([&](auto Kc) {
             xv[Kc] = (double)*at_lane(xrow + Dims<Tb, SUB>::template comp<decltype(Kc)::value>(dm.d_in) * C, chl);
             dxa[Kc] = 0.0;
         });
+        if constexpr (DBL) {
+            const float* grow = a.ggx ? a.ggx + (int64_t)j * (dm.d_in * C) : nullptr;
+            static_for<0, DIN>([&](auto Kc) {
+                gxv[Kc] = grow ? (double)*at_lane(grow + Dims<Tb, SUB>::template comp<decltype(Kc)::value>(dm.d_in) * C, chl)
+                               : 0.0;
+            });
+        }
     }
     // the sender's range of the view, clamped to the view's bounds
     const int32_t q0 = clampi(a.g.srow[j], 0, E);
@@ -689,13 +933,21 @@ __global__ void __launch_bounds__(256, (Tune<LM, LPE>::bwd_occ)) k_conv_bwd(BwdA
         for (int32_t t = t0; t < t1; ++t) {
             const int32_t q = q0 + ps.s + S * t;
             if (q >= end) continue;  // uniform over the lanes of one edge
-            BwdEdge<Tb> cur;
-            bwd_load<Tb, SUB, LPE == 64>(cur, q, chl, a, dm);
+            Edge cur;
+            if constexpr (DBL) bwd_load_dbl<Tb, SUB, LPE == 64>(cur, q, chl, a, dm);
+            else bwd_load<Tb, SUB, LPE == 64>(cur, q, chl, a, dm);
             if constexpr (H == 2)
                 if (ps.h == 0 && lane == 0) eslot[ps.s * K + (t - t0)] = cur.ok ? cur.e : -1;
             if (!cur.ok) continue;
             double yv[DSH];
             edge_sh<DSH, LPE>(cur.y, yv);
+            double gyv[DBL ? DSH : 1];
+            if constexpr (DBL) edge_sh<DSH, LPE>(cur.gy, gyv);
+            // the edge's contraction (the backward's, or the double backward's)
+            auto slice = [&](auto&& store_w, auto&& flush_y) {
+                if constexpr (DBL) bwd_slice_dbl<Tb>(cur, yv, gyv, xv, gxv, dxa, store_w, flush_y);
+                else bwd_slice<Tb>(cur.w, cur.g, yv, xv, dxa, store_w, flush_y);
+            };
             const int32_t Ce = edge_stride(C);
             float* dwrow = a.dW + (int64_t)cur.e * (dm.P * Ce);
             const uint32_t chs = lane_offset(chl);
@@ -719,7 +971,7 @@ __global__ void __launch_bounds__(256, (Tune<LM, LPE>::bwd_occ)) k_conv_bwd(BwdA
             };
             if constexpr (kTile) {
                 // grad_Y partials go to this wave's LDS tile degree by degree
-                bwd_slice<Tb>(cur.w, cur.g, yv, xv, dxa, store_w, [&](auto K2, const auto& dyb) {
+                slice(store_w, [&](auto K2, const auto& dyb) {
                     constexpr int k2 = decltype(K2)::value;
 #pragma unroll
                     for (int b = 0; b < (int)(sizeof(dyb) / sizeof(double)); ++b)
@@ -742,7 +994,7 @@ __global__ void __launch_bounds__(256, (Tune<LM, LPE>::bwd_occ)) k_conv_bwd(BwdA
             } else {
                 // an edge spans LPE < 64 lanes: reduce each degree's partials over them
                 float* yp = a.dY + (int64_t)cur.e * dm.d_sh;
-                bwd_slice<Tb>(cur.w, cur.g, yv, xv, dxa, store_w, [&](auto K2, const auto& dyb) {
+                slice(store_w, [&](auto K2, const auto& dyb) {
                     constexpr int k2 = decltype(K2)::value;
 #pragma unroll
                     for (int b = 0; b < (int)(sizeof(dyb) / sizeof(double)); ++b) {
@@ -790,11 +1042,11 @@ __global__ void __launch_bounds__(256, (Tune<LM, LPE>::bwd_occ)) k_conv_bwd(BwdA
     }
 }
 
-template <int LM, int LPE, int H, bool SUB>
+template <int LM, int LPE, int H, bool SUB, bool DBL = false>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s)
 {
     if (a.sh.N == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_conv_bwd<LM, LPE, H, SUB>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_conv_bwd<LM, LPE, H, SUB, DBL>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -805,7 +1057,9 @@ constexpr KernelSet make_set()
                      LPE,
                      H,
                      {&launch_fwd<LM, LPE, H, false>, &launch_fwd<LM, LPE, H, true>},
-                     {&launch_bwd<LM, LPE, H, false>, &launch_bwd<LM, LPE, H, true>}};
+                     {&launch_bwd<LM, LPE, H, false>, &launch_bwd<LM, LPE, H, true>},
+                     &launch_fwd<LM, LPE, H, true, true>,
+                     &launch_bwd<LM, LPE, H, true, true>};
 }
 
 template <int LM>

@@ -105,7 +105,7 @@ class Plan:
         _need(row_ptr, "row_ptr", torch.int32)
         _need(src, "src", torch.int32, (E,), dev)
         _need(grad_r, "grad_r", torch.float32, (E, 3), dev)
-        ws = self._workspace(ws, N, E, dev)
+        ws = self._workspace(ws, row_ptr, src)
         if grad_pos is None:
             grad_pos = torch.empty((N, 3), dtype=torch.float32, device=dev)
         _need(grad_pos, "grad_pos", torch.float32, (N, 3), dev)
@@ -126,22 +126,28 @@ class Plan:
             self._h, N, E, _ptr(row_ptr), _ptr(src), _ptr(ws), ws.numel(), _stream(row_ptr.device)))
         return ws
 
-    def _workspace(self, ws, N, E, dev):
+    def _workspace(self, ws, row_ptr, src):
+        # A workspace allocated here is prepared here: the library knows a
+        # prepared workspace by its address, and a fresh allocation can land
+        # where an earlier, since freed, workspace of the same graph was.
         if ws is None:
-            ws = torch.empty(self.workspace_size(N, E), dtype=torch.uint8, device=dev)
-        _need(ws, "ws", torch.uint8, device=dev)
+            return self.graph_prepare(row_ptr, src)
+        _need(ws, "ws", torch.uint8, device=row_ptr.device)
         return ws
 
     def conv_fwd(self, row_ptr, src, x, Y, W, ws=None, out=None) -> torch.Tensor:
         """out[N][D_out][C].  ``ws``: the graph's workspace (from graph_prepare,
-        or any buffer of workspace_size bytes, which the call then prepares)."""
+        or any buffer of workspace_size bytes, which the call then prepares
+        unless it already holds this graph's view; a buffer whose memory
+        served anything else since its preparation must be prepared again).
+        Without ``ws`` a workspace is allocated and prepared for this call."""
         N, E, C, dev = row_ptr.shape[0] - 1, src.shape[0], self.channels, row_ptr.device
         _need(row_ptr, "row_ptr", torch.int32)
         _need(src, "src", torch.int32, (E,), dev)
         _need(x, "x", torch.float32, (N, self.dim_in, C), dev)
         _need(Y, "Y", torch.float32, (E, self.dim_sh), dev)
         _need(W, "W", torch.float32, (E, self.weight_rows, C), dev)
-        ws = self._workspace(ws, N, E, dev)
+        ws = self._workspace(ws, row_ptr, src)
         if out is None:
             out = torch.empty((N, self.dim_out, C), dtype=torch.float32, device=dev)
         _need(out, "out", torch.float32, (N, self.dim_out, C), dev)
@@ -160,7 +166,7 @@ class Plan:
         _need(Y, "Y", torch.float32, (E, self.dim_sh), dev)
         _need(W, "W", torch.float32, (E, self.weight_rows, C), dev)
         _need(grad_out, "grad_out", torch.float32, (N, self.dim_out, C), dev)
-        ws = self._workspace(ws, N, E, dev)
+        ws = self._workspace(ws, row_ptr, src)
         if "dx" in want and grad_x is None:
             grad_x = torch.empty((N, self.dim_in, C), dtype=torch.float32, device=dev)
         if "dW" in want and grad_W is None:
@@ -181,3 +187,30 @@ class Plan:
             self._h, N, E, _ptr(row_ptr), _ptr(src), _ptr(x), _ptr(Y), _ptr(W), _ptr(grad_out),
             _ptr(grad_x), _ptr(grad_W), _ptr(grad_Y), _ptr(ws), ws.numel(), _stream(dev)))
         return grad_x, grad_W, grad_Y
+
+    def conv_bwd_bwd(self, row_ptr, src, x, Y, W, grad_out, gg_x=None, gg_Y=None, gg_W=None, ws=None,
+                     want=("x", "Y", "W", "grad_out")):
+        """Double backward: the gradients (dd_x, dd_Y, dd_W, dd_out) of
+        S = <gg_x, grad_x> + <gg_W, grad_W> + <gg_Y, grad_Y>, where
+        (grad_x, grad_W, grad_Y) = conv_bwd(x, Y, W, grad_out), with respect to
+        x, Y, W and grad_out.  A cotangent left as None is zero; a result not
+        in ``want`` comes back as None."""
+        N, E, C, dev = row_ptr.shape[0] - 1, src.shape[0], self.channels, row_ptr.device
+        _need(row_ptr, "row_ptr", torch.int32)
+        _need(src, "src", torch.int32, (E,), dev)
+        sx, sy, sw, so = (N, self.dim_in, C), (E, self.dim_sh), (E, self.weight_rows, C), (N, self.dim_out, C)
+        _need(x, "x", torch.float32, sx, dev)
+        _need(Y, "Y", torch.float32, sy, dev)
+        _need(W, "W", torch.float32, sw, dev)
+        _need(grad_out, "grad_out", torch.float32, so, dev)
+        for t, n, s in ((gg_x, "gg_x", sx), (gg_Y, "gg_Y", sy), (gg_W, "gg_W", sw)):
+            if t is not None:
+                _need(t, n, torch.float32, s, dev)
+        ws = self._workspace(ws, row_ptr, src)
+        new = lambda shape, key: torch.empty(shape, dtype=torch.float32, device=dev) if key in want else None
+        dd_x, dd_Y, dd_W, dd_out = new(sx, "x"), new(sy, "Y"), new(sw, "W"), new(so, "grad_out")
+        L.check("cgtp_conv_bwd_bwd", L.lib().cgtp_conv_bwd_bwd(
+            self._h, N, E, _ptr(row_ptr), _ptr(src), _ptr(x), _ptr(Y), _ptr(W), _ptr(grad_out), _ptr(gg_x),
+            _ptr(gg_Y), _ptr(gg_W), _ptr(dd_x), _ptr(dd_Y), _ptr(dd_W), _ptr(dd_out), _ptr(ws), ws.numel(),
+            _stream(dev)))
+        return dd_x, dd_Y, dd_W, dd_out

@@ -152,7 +152,9 @@ cgtp_status_t cgtp_node_grad(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges,
  * row_ptr, src); cgtp_conv_fwd / cgtp_conv_bwd called with the same four
  * values and `ws` use it as it is, and otherwise run this preparation
  * themselves first.  The record is by pointer: after rewriting the contents
- * of row_ptr or src in place, call cgtp_graph_prepare again.  ws must be
+ * of row_ptr or src in place, or when the workspace memory has held anything
+ * else since it was prepared (for instance freed and allocated again at the
+ * same address), call cgtp_graph_prepare again.  ws must be
  * 256-byte aligned and at least cgtp_workspace_size bytes. */
 cgtp_status_t cgtp_graph_prepare(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges,
                                  const int32_t* row_ptr, const int32_t* src, void* ws, size_t ws_bytes,
@@ -180,6 +182,31 @@ cgtp_status_t cgtp_conv_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
                             const int32_t* src, const float* x, const float* Y, const float* W,
                             const float* grad_out, float* grad_x, float* grad_W, float* grad_Y,
                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Double backward (the higher-order derivatives LunaTP's abstract names;
+ * training on forces differentiates the backward once more).  With
+ * (grad_x, grad_W, grad_Y) = cgtp_conv_bwd(x, Y, W, grad_out) and cotangents
+ * gg_x [N][(l_in+1)^2][C], gg_W [E][P][C], gg_Y [E][(l_sh+1)^2] of those
+ * three results, this computes the gradients of
+ *   S = <gg_x, grad_x> + <gg_W, grad_W> + <gg_Y, grad_Y>
+ * with respect to each input of the backward:
+ *   dd_x   [N][(l_in+1)^2][C]   (with respect to x)
+ *   dd_Y   [E][(l_sh+1)^2]      (with respect to Y, summed over the channels)
+ *   dd_W   [E][P][C]            (with respect to W)
+ *   dd_out [N][(l_out+1)^2][C]  (with respect to grad_out)
+ * A NULL cotangent counts as zero; a NULL result is skipped; results are
+ * overwritten.  With CGTP_FLAG_SHARED_WEIGHTS, W, gg_W and dd_W are [E][1][C].
+ * S is linear in each input, so every result is a sum of three (dd_out) or
+ * two (the others) backward- or forward-like contractions, formed in one pass
+ * per side: dd_out on the receiver side as the forward is, the others on the
+ * sender side over the view in `ws` as the backward is (prepared here first
+ * unless cgtp_graph_prepare already did).  Same alignment rules as the other
+ * calls. */
+cgtp_status_t cgtp_conv_bwd_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
+                                const int32_t* src, const float* x, const float* Y, const float* W,
+                                const float* grad_out, const float* gg_x, const float* gg_Y, const float* gg_W,
+                                float* dd_x, float* dd_Y, float* dd_W, float* dd_out, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the

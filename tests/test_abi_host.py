@@ -25,10 +25,18 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(L.lib(), n), n
         assert n in L.SIGNATURES, n
+
+
+def test_binding_argument_counts_match_header(L):
+    """Every ctypes signature takes as many arguments as its declaration."""
+    text = open(os.path.join(ROOT, "include", "cgtp.h")).read()
+    for name, params in re.findall(r"^(?:cgtp_status_t|const char\*)\s+(cgtp_\w+)\(([^)]*)\);", text, re.M):
+        n = len([p for p in params.split(",") if p.strip()])
+        assert len(L.SIGNATURES[name][1]) == n, name
 
 
 def test_status_strings(L):
@@ -136,6 +144,14 @@ def test_calls_reject_bad_arguments_without_a_gpu(L):
     assert lib.cgtp_conv_bwd(h, 4, 4, fake, fake, fake, fake, fake, fake, None, None, None, ws, big,
                              None) == L.CGTP_OK
     assert lib.cgtp_sh_fwd(h, 0, None, None, None) == L.CGTP_OK
+    # double backward: (x, Y, W, grad_out, gg_x, gg_Y, gg_W, dd_x, dd_Y, dd_W, dd_out)
+    dbl = lambda *p, ws_=ws, n=big: lib.cgtp_conv_bwd_bwd(h, 4, 4, fake, fake, *p, ws_, n, None)
+    assert dbl(fake, fake, fake, fake, None, None, None, fake, None, None, None, ws_=ws, n=16) == L.CGTP_ERR_WORKSPACE
+    assert dbl(None, fake, fake, fake, None, None, None, fake, None, None, None) == L.CGTP_ERR_INVALID_ARG
+    assert dbl(fake, fake, fake, None, None, None, None, fake, None, None, None) == L.CGTP_ERR_INVALID_ARG
+    assert dbl(fake, fake, fake, fake, odd, None, None, fake, None, None, None) == L.CGTP_ERR_INVALID_ARG
+    assert dbl(fake, fake, fake, fake, None, None, None, None, None, None, odd) == L.CGTP_ERR_INVALID_ARG
+    assert dbl(fake, fake, fake, fake, fake, fake, fake, None, None, None, None) == L.CGTP_OK
     lib.cgtp_plan_destroy(h)
 
 

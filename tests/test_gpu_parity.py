@@ -560,3 +560,30 @@ def test_conv_shared_path_weights(torch_dev, oracle, li, ls, lo, C):
     assert_parity(dx, rdx, "dx")
     assert_parity(dW[:, 0], rdW, "dW")
     assert_parity(dY, rdY, "dY")
+
+
+def test_binding_prepares_the_workspaces_it_allocates(torch_dev, oracle):
+    """A workspace freed after preparation and the same memory handed out
+    again (torch's caching allocator returns the block at the same address)
+    for other data: a call without ``ws`` must not take the library's record
+    of that address for a prepared view."""
+    torch, dev = torch_dev
+    from clebsch_gordan_tensor_cgtp_amd.ops import Plan
+    L, C = 2, 64
+    plan = Plan(L, L, L, C)
+    g = _small_case(L, C, seed=6)
+    N, E = g.n_nodes, g.n_edges
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    rp, sr = T(g.row_ptr), T(g.src)
+    x, W, G = synth.make_tensors_numpy(N, E, L, C, seed=7)
+    Y = oracle.sh(L, g.r).astype(np.float32)
+    ref = oracle.conv_fwd(L, L, L, g.row_ptr, g.src, x, Y, W)
+    xd, Yd, Wd = T(x), T(Y), T(W)
+    for _ in range(3):
+        ws = plan.graph_prepare(rp, sr)
+        nbytes = ws.numel()
+        del ws
+        junk = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=dev)   # likely the same block
+        del junk
+        out = plan.conv_fwd(rp, sr, xd, Yd, Wd).cpu().numpy()
+        assert_parity(out, ref, "out")

@@ -327,3 +327,30 @@ def test_double_backward_identities_and_missing_cotangents(oracle):
         r2 = oracle.conv_bwd_bwd(*Ls, g.row_ptr, g.src, a["x"], a["Y"], a["W"], a["G"], **with_none)
         for u, v in zip(r1, r2):
             np.testing.assert_array_equal(u, v)
+
+
+def test_double_backward_shared_weights_finite_differences(oracle):
+    """With path-weight sharing S = <ggx,dx> + <ggWs,dWs> + <ggY,dY> over the
+    shared backward; its gradients by exact central differences."""
+    from clebsch_gordan_tensor_cgtp_amd.synth import random_graph
+    li, ls, lo, C, N = 2, 1, 2, 3, 8
+    rng = np.random.default_rng(12)
+    g = random_graph(N, rng.integers(0, 5, size=N), seed=4)
+    E = g.n_edges
+    a = dict(x=rng.normal(size=(N, (li + 1) ** 2, C)), Y=rng.normal(size=(E, (ls + 1) ** 2)),
+             Ws=rng.normal(size=(E, C)), G=rng.normal(size=(N, (lo + 1) ** 2, C)))
+    cot = dict(ggx=rng.normal(size=a["x"].shape), ggY=rng.normal(size=a["Y"].shape), ggWs=rng.normal(size=(E, C)))
+
+    def S(v):
+        dx, dWs, dY = oracle.conv_bwd_shared(li, ls, lo, g.row_ptr, g.src, v["x"], v["Y"], v["Ws"], v["G"])
+        return (cot["ggx"] * dx).sum() + (cot["ggWs"] * dWs).sum() + (cot["ggY"] * dY).sum()
+
+    got = dict(zip(("x", "Y", "Ws", "G"), oracle.conv_bwd_bwd_shared(li, ls, lo, g.row_ptr, g.src, a["x"], a["Y"],
+                                                                       a["Ws"], a["G"], **cot)))
+    for name in a:
+        d = rng.normal(size=a[name].shape)
+        ap, am = dict(a), dict(a)
+        ap[name] = a[name] + 1e-3 * d
+        am[name] = a[name] - 1e-3 * d
+        fd = (S(ap) - S(am)) / 2e-3
+        assert fd == pytest.approx((got[name] * d).sum(), rel=1e-9, abs=1e-9), name
