@@ -214,6 +214,17 @@ def conv_bwd_shared(l_in, l_sh, l_out, row_ptr, src, x, Y, Ws, G, want=("dx", "d
     return dx, (dW.sum(axis=1) if dW is not None else None), dY
 
 
+def conv_bwd_bwd_shared(l_in, l_sh, l_out, row_ptr, src, x, Y, Ws, G, ggx=None, ggY=None, ggWs=None,
+                        want=("dx", "dY", "dW", "dG")):
+    """Double backward with path-weight sharing.  The shared backward returns
+    dWs = sum over p of dW_p, so <ggWs, dWs> = <ggW, dW> with ggW[e][p][u] =
+    ggWs[e][u] for every p; the gradient for Ws sums over the paths again."""
+    P = paths(l_in, l_sh, l_out).shape[0]
+    rep = lambda a: np.repeat(_f64(a)[:, None, :], P, axis=1) if a is not None else None
+    dx, dY, dW, dG = conv_bwd_bwd(l_in, l_sh, l_out, row_ptr, src, x, Y, rep(Ws), G, ggx, ggY, rep(ggWs), want)
+    return dx, dY, (dW.sum(axis=1) if dW is not None else None), dG
+
+
 def graph_transpose(row_ptr, src):
     """(srow_ptr[N+1], perm[E], sdst[E]): edges stably grouped by sender."""
     row_ptr, src = _i64(row_ptr), _i64(src)
