@@ -60,7 +60,12 @@ def algorithmic_bytes(N, E, P, C, d_in, d_sh, d_out):
     bwd = E * (8 * P * C + 8 * d_sh + 8) + N * (4 * C * (2 * d_in + d_out) + 4)
     sh = E * (12 + 4 * d_sh)
     prep = E * 4 * 6 + N * 4 * 4
-    return {"fwd": fwd, "bwd": bwd, "sh": sh, "prep": prep}
+    # double backward: the receiver side reads W, ggW, Y, ggY per edge and
+    # x, ggx per sender row and writes dd_out; the sender side reads W, ggW,
+    # Y, ggY, the view and x, ggx, grad_out rows and writes dd_W, dd_Y, dd_x
+    dbl_fwd = E * (8 * P * C + 8 * d_sh + 4) + N * (4 * C * (2 * d_in + d_out) + 4)
+    dbl_bwd = E * (12 * P * C + 12 * d_sh + 8) + N * (4 * C * (3 * d_in + d_out) + 4)
+    return {"fwd": fwd, "bwd": bwd, "sh": sh, "prep": prep, "dbl_fwd": dbl_fwd, "dbl_bwd": dbl_bwd}
 
 
 def conv_flops(L, C, E):
@@ -206,12 +211,41 @@ def run_workload(torch, dev, key, steps, warmup, settle, locality=False):
     }
     log(f"{key}: step {ms_step:.3f} ms | sh+prep {prep_ms:.3f} | fwd {fwd_ms:.3f} ms "
         f"({res['fwd_alg_gbs']:.0f} GB/s alg) | bwd {bwd_ms:.3f} ms ({res['bwd_alg_gbs']:.0f} GB/s alg)")
+    res["double_backward"] = time_double_backward(torch, plan, stream, rp, src, x, Y, W, G, ws, ab, steps)
     host = None
     if key == HEADLINE:
         host = (w, g, x.cpu().numpy(), W.cpu().numpy(), G.cpu().numpy())
     del Y, out, dx, dW, dY, ws, x, W, G
     torch.cuda.empty_cache()
     return res, host
+
+
+def time_double_backward(torch, plan, stream, rp, src, x, Y, W, G, ws, ab, steps):
+    """Median launch times of the double backward's two kernels (all three
+    cotangents given): the receiver side (dd_out) and the sender side
+    (dd_x, dd_Y, dd_W), each timed alone with HIP events on its stream."""
+    gx, gY, gW = torch.randn_like(x), torch.randn_like(Y), torch.randn_like(W)
+    legs = {"dd_out": ("grad_out",), "dd_x_Y_W": ("x", "Y", "W")}
+    res = {}
+    for name, want in legs.items():
+        for _ in range(3):
+            plan.conv_bwd_bwd(rp, src, x, Y, W, G, gx, gY, gW, ws, want=want)
+        ts = []
+        for _ in range(max(5, steps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            plan.conv_bwd_bwd(rp, src, x, Y, W, G, gx, gY, gW, ws, want=want)
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = statistics.median(a.elapsed_time(b) for a, b in ts)
+        nbytes = ab["dbl_fwd" if name == "dd_out" else "dbl_bwd"]
+        res[name] = {"ms": ms, "alg_bytes": nbytes, "alg_gbs": nbytes / (ms * 1e-3) / 1e9,
+                     "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del gx, gY, gW
+    log(f"  double backward: dd_out {res['dd_out']['ms']:.3f} ms ({res['dd_out']['alg_gbs']:.0f} GB/s alg) | "
+        f"dd_x,dd_Y,dd_W {res['dd_x_Y_W']['ms']:.3f} ms ({res['dd_x_Y_W']['alg_gbs']:.0f} GB/s alg)")
+    return res
 
 
 def cpu_model():
