@@ -55,6 +55,10 @@ def _load():
     lib.orc_conv_bwd.argtypes = [ctypes.c_int] * 4 + [ctypes.c_int64] * 2 + [_i64p, _i64p] + [_dp] * 7
     lib.orc_conv_bwd_bwd.restype = ctypes.c_int
     lib.orc_conv_bwd_bwd.argtypes = [ctypes.c_int] * 4 + [ctypes.c_int64] * 2 + [_i64p, _i64p] + [_dp] * 11
+    lib.orc_cp_conv_fwd.restype = None
+    lib.orc_cp_conv_fwd.argtypes = [ctypes.c_int] * 5 + [ctypes.c_int64, _i64p, _i64p] + [_dp] * 7
+    lib.orc_cp_conv_bwd.restype = None
+    lib.orc_cp_conv_bwd.argtypes = [ctypes.c_int] * 5 + [ctypes.c_int64] * 2 + [_i64p, _i64p] + [_dp] * 10
     lib.orc_graph_transpose.restype = None
     lib.orc_graph_transpose.argtypes = [ctypes.c_int64, ctypes.c_int64, _i64p, _i64p, _i64p, _i64p, _i64p]
     lib.orc_num_threads.restype = ctypes.c_int
@@ -223,6 +227,118 @@ def conv_bwd_bwd_shared(l_in, l_sh, l_out, row_ptr, src, x, Y, Ws, G, ggx=None, 
     rep = lambda a: np.repeat(_f64(a)[:, None, :], P, axis=1) if a is not None else None
     dx, dY, dW, dG = conv_bwd_bwd(l_in, l_sh, l_out, row_ptr, src, x, Y, rep(Ws), G, ggx, ggY, rep(ggWs), want)
     return dx, dY, (dW.sum(axis=1) if dW is not None else None), dG
+
+
+# ---------------------------------------------------------------------------
+# CP-decomposed tensor product ("Tensor Decomposition Networks ...", rebuttal
+# to S6y1: Equation (3), its gradients, and the data-free fit of the factors)
+# ---------------------------------------------------------------------------
+def cp_tensor(l_in, l_sh, l_out):
+    """The whole coupling tensor M [d1][d2][d3] of the degree set: every
+    path's real CG block T_p placed at the components of its degrees (a
+    component triple belongs to at most one path), so that with one weight for
+    every path the convolution couples x and y through M."""
+    d1, d2, d3 = (l_in + 1) ** 2, (l_sh + 1) ** 2, (l_out + 1) ** 2
+    M = np.zeros((d1, d2, d3))
+    for l1, l2, l3 in paths(l_in, l_sh, l_out):
+        M[l1 * l1:(l1 + 1) ** 2, l2 * l2:(l2 + 1) ** 2, l3 * l3:(l3 + 1) ** 2] = real_cg(l1, l2, l3)
+    return M
+
+
+def cp_exact_factors(M):
+    """Factors of rank d1*d2 that reproduce M exactly: column r = (a, b) has
+    B[:, r] = e_a, C[:, r] = e_b and A[:, r] = M[a, b, :]."""
+    d1, d2, d3 = M.shape
+    R = d1 * d2
+    A, B, Cf = np.zeros((d3, R)), np.zeros((d1, R)), np.zeros((d2, R))
+    for a in range(d1):
+        for b in range(d2):
+            r = a * d2 + b
+            B[a, r] = 1.0
+            Cf[b, r] = 1.0
+            A[:, r] = M[a, b, :]
+    return A, B, Cf
+
+
+def cp_reconstruct(A, B, Cf):
+    """The rank-R tensor sum_r B[:,r] (x) Cf[:,r] (x) A[:,r] as [d1][d2][d3]."""
+    return np.einsum("ar,br,cr->abc", _f64(B), _f64(Cf), _f64(A))
+
+
+def cp_objective(M, A, B, Cf):
+    """Squared Frobenius error ||M - [[A, B, Cf]]||^2: the expected squared
+    error of the approximate product over independent standard-normal x, y."""
+    return float(((_f64(M) - cp_reconstruct(A, B, Cf)) ** 2).sum())
+
+
+def cp_als_step(M, A, B, Cf, which, ridge=1e-12):
+    """One ALS update: the factor `which` ("B", "C" or "A") replaced by the
+    exact minimiser of the Frobenius error with the other two held fixed,
+    K V^-1 with K the tensor contracted with the other two factors and V the
+    Hadamard product of their Gram matrices (ridge * trace(V) / R added to
+    V's diagonal).  Returns the new (A, B, Cf)."""
+    M = _f64(M)
+    R = A.shape[1]
+
+    def solve(K, V):
+        V = V + np.eye(R) * (ridge * np.trace(V) / R)
+        return np.linalg.solve(V, K.T).T          # K V^-1 (V symmetric)
+
+    if which == "B":
+        B = solve(np.einsum("abc,br,cr->ar", M, Cf, A), (Cf.T @ Cf) * (A.T @ A))
+    elif which == "C":
+        Cf = solve(np.einsum("abc,ar,cr->br", M, B, A), (B.T @ B) * (A.T @ A))
+    else:
+        A = solve(np.einsum("abc,ar,br->cr", M, B, Cf), (B.T @ B) * (Cf.T @ Cf))
+    return A, B, Cf
+
+
+def cp_als(M, A, B, Cf, sweeps, ridge=1e-12):
+    """Alternating least squares for the CP factors of M (the data-free fit:
+    the Frobenius norm between exact and approximate product is minimised one
+    factor at a time, each step an exact linear least-squares solve, see
+    cp_als_step).  Order per sweep: B, then Cf, then A.  Returns (A, B, Cf,
+    [relative error after each sweep])."""
+    M = _f64(M)
+    A, B, Cf = (np.array(_f64(v), copy=True) for v in (A, B, Cf))
+    nrm = np.sqrt((M ** 2).sum())
+    hist = []
+    for _ in range(sweeps):
+        for which in ("B", "C", "A"):
+            A, B, Cf = cp_als_step(M, A, B, Cf, which, ridge)
+        hist.append(np.sqrt(cp_objective(M, A, B, Cf)) / nrm)
+    return A, B, Cf, hist
+
+
+def cp_conv_fwd(row_ptr, src, x, Y, W, A, B, Cf):
+    """out[N][d3][C] of the CP convolution: W [E][C] one weight per edge and
+    channel, factors A [d3][R], B [d1][R], Cf [d2][R]."""
+    row_ptr, src = _i64(row_ptr), _i64(src)
+    x, Y, W, A, B, Cf = (_f64(v) for v in (x, Y, W, A, B, Cf))
+    N, d1, C = x.shape
+    d3, R = A.shape
+    d2 = Cf.shape[0]
+    out = np.zeros((N, d3, C))
+    _load().orc_cp_conv_fwd(d1, d2, d3, R, C, N, _p(row_ptr, _i64p), _p(src, _i64p), _p(x), _p(Y), _p(W), _p(A),
+                            _p(B), _p(Cf), _p(out))
+    return out
+
+
+def cp_conv_bwd(row_ptr, src, x, Y, W, A, B, Cf, G, want=("dx", "dY", "dW")):
+    """(dx, dY, dW) of <G, cp_conv_fwd(...)>; a gradient not in ``want`` is None."""
+    row_ptr, src = _i64(row_ptr), _i64(src)
+    x, Y, W, A, B, Cf, G = (_f64(v) for v in (x, Y, W, A, B, Cf, G))
+    N, d1, C = x.shape
+    d3, R = A.shape
+    d2 = Cf.shape[0]
+    E = src.shape[0]
+    dx = np.zeros_like(x) if "dx" in want else None
+    dY = np.zeros((E, d2)) if "dY" in want else None
+    dW = np.zeros((E, C)) if "dW" in want else None
+    opt = lambda a: _p(a) if a is not None else None
+    _load().orc_cp_conv_bwd(d1, d2, d3, R, C, N, E, _p(row_ptr, _i64p), _p(src, _i64p), _p(x), _p(Y), _p(W),
+                            _p(A), _p(B), _p(Cf), _p(G), opt(dx), opt(dY), opt(dW))
+    return dx, dY, dW
 
 
 def graph_transpose(row_ptr, src):

@@ -579,6 +579,128 @@ int orc_conv_bwd_bwd(int lin, int lsh, int lout, int C, int64_t N, int64_t E, co
     return 0;
 }
 
+/* CP-decomposed tensor-product convolution ("Tensor Decomposition Networks
+ * ...", rebuttal to S6y1: Equation (3) and the gradients derived after it).
+ * The coupling of x (d1 components) and y (d2) into z (d3) is approximated by
+ * rank-R factors A [d3][R], B [d1][R], Cf [d2][R] (row-major):
+ *   z = A (B^T x  (.)  Cf^T y).
+ * Per edge e = j->i and channel u, with one weight W[e][u]:
+ *   out[i][:,u] += W[e][u] * A (B^T x[j][:,u] (.) Cf^T Y[e]).
+ * out is overwritten. */
+void orc_cp_conv_fwd(int d1, int d2, int d3, int R, int C, int64_t N, const int64_t* row_ptr,
+                     const int64_t* src, const double* x, const double* Y, const double* W, const double* A,
+                     const double* B, const double* Cf, double* out)
+{
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (R > 0 ? R : 1));
+        double* t = (double*)malloc(sizeof(double) * (R > 0 ? R : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < N; ++i) {
+            double* o = out + i * d3 * C;
+            for (int q = 0; q < d3 * C; ++q) o[q] = 0.0;
+            for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+                const int64_t j = src[e];
+                for (int r = 0; r < R; ++r) {
+                    t[r] = 0.0;
+                    for (int b = 0; b < d2; ++b) t[r] += Cf[b * R + r] * Y[e * d2 + b];
+                }
+                for (int u = 0; u < C; ++u) {
+                    for (int r = 0; r < R; ++r) {
+                        s[r] = 0.0;
+                        for (int a = 0; a < d1; ++a) s[r] += B[a * R + r] * x[(j * d1 + a) * C + u];
+                    }
+                    const double w = W[e * C + u];
+                    for (int c = 0; c < d3; ++c) {
+                        double z = 0.0;
+                        for (int r = 0; r < R; ++r) z += A[c * R + r] * s[r] * t[r];
+                        o[c * C + u] += w * z;
+                    }
+                }
+            }
+        }
+        free(s);
+        free(t);
+    }
+}
+
+/* Its backward for L = <G, out>, by the closed forms after Equation (3)
+ * (g_x = (g_z A (.) Cf^T y) B^T and g_y = (g_z A (.) B^T x) Cf^T, here with
+ * the edge weight and the channel sum): with g = G[i][:,u] for edge e = j->i,
+ *   dx[j][:,u] += W[e][u] B (A^T g (.) Cf^T Y[e])
+ *   dY[e]      += sum_u W[e][u] Cf (A^T g (.) B^T x[j][:,u])
+ *   dW[e][u]    = <g, A (B^T x[j][:,u] (.) Cf^T Y[e])>
+ * A NULL output is skipped; outputs are overwritten. */
+void orc_cp_conv_bwd(int d1, int d2, int d3, int R, int C, int64_t N, int64_t E, const int64_t* row_ptr,
+                     const int64_t* src, const double* x, const double* Y, const double* W, const double* A,
+                     const double* B, const double* Cf, const double* G, double* dx, double* dY, double* dW)
+{
+    int64_t* dst = (int64_t*)malloc(sizeof(int64_t) * (E > 0 ? E : 1));
+    for (int64_t i = 0; i < N; ++i)
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) dst[e] = i;
+    const int64_t rowlen = (int64_t)d1 * C;
+    if (dx)
+        for (int64_t q = 0; q < N * rowlen; ++q) dx[q] = 0.0;
+#pragma omp parallel
+    {
+        const int Rm = R > 0 ? R : 1;
+        double* s = (double*)malloc(sizeof(double) * Rm);
+        double* t = (double*)malloc(sizeof(double) * Rm);
+        double* ga = (double*)malloc(sizeof(double) * Rm);
+        double* mine = dx;
+        int nthr = 1;
+#ifdef _OPENMP
+        nthr = omp_get_num_threads();
+#endif
+        if (dx && nthr > 1) mine = (double*)calloc((size_t)(N * rowlen > 0 ? N * rowlen : 1), sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t e = 0; e < E; ++e) {
+            const int64_t j = src[e], i = dst[e];
+            for (int r = 0; r < R; ++r) {
+                t[r] = 0.0;
+                for (int b = 0; b < d2; ++b) t[r] += Cf[b * R + r] * Y[e * d2 + b];
+            }
+            if (dY)
+                for (int b = 0; b < d2; ++b) dY[e * d2 + b] = 0.0;
+            for (int u = 0; u < C; ++u) {
+                const double w = W[e * C + u];
+                for (int r = 0; r < R; ++r) {
+                    s[r] = 0.0;
+                    for (int a = 0; a < d1; ++a) s[r] += B[a * R + r] * x[(j * d1 + a) * C + u];
+                    ga[r] = 0.0;
+                    for (int c = 0; c < d3; ++c) ga[r] += A[c * R + r] * G[(i * d3 + c) * C + u];
+                }
+                if (dx)
+                    for (int a = 0; a < d1; ++a) {
+                        double v = 0.0;
+                        for (int r = 0; r < R; ++r) v += B[a * R + r] * ga[r] * t[r];
+                        mine[(j * d1 + a) * C + u] += w * v;
+                    }
+                if (dY)
+                    for (int b = 0; b < d2; ++b) {
+                        double v = 0.0;
+                        for (int r = 0; r < R; ++r) v += Cf[b * R + r] * ga[r] * s[r];
+                        dY[e * d2 + b] += w * v;
+                    }
+                if (dW) {
+                    double v = 0.0;
+                    for (int r = 0; r < R; ++r) v += ga[r] * s[r] * t[r];
+                    dW[e * C + u] = v;
+                }
+            }
+        }
+        if (dx && nthr > 1) {
+#pragma omp critical
+            for (int64_t q = 0; q < N * rowlen; ++q) dx[q] += mine[q];
+            free(mine);
+        }
+        free(s);
+        free(t);
+        free(ga);
+    }
+    free(dst);
+}
+
 /* Sender-sorted view of a receiver-sorted CSR (the graph preparation the
  * backward needs): a stable counting sort of the edges by sender.
  *   srow_ptr[N+1]  offsets of each sender's out-edges
