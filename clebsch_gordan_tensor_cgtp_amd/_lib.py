@@ -21,6 +21,7 @@ CGTP_ERR_WORKSPACE = -3
 CGTP_ERR_HIP = -4
 CGTP_ERR_ALLOC = -5
 CGTP_ERR_GRAPH = -6
+CGTP_ERR_NUMERIC = -7
 CGTP_FLAG_VALIDATE = 1
 CGTP_FLAG_LOCALITY = 2
 CGTP_FLAG_SHARED_WEIGHTS = 4
@@ -46,6 +47,10 @@ SIGNATURES = {
     "cgtp_conv_bwd": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, ctypes.c_size_t, _vp]),
     "cgtp_conv_bwd_bwd": (ctypes.c_int, [_vp, _c_i64, _c_i64] + [_vp] * 14 + [ctypes.c_size_t, _vp]),
+    "cgtp_cp_workspace_size": (ctypes.c_int, [_vp, ctypes.c_int, _c_i64, _c_i64, ctypes.POINTER(ctypes.c_size_t)]),
+    "cgtp_cp_fit": (ctypes.c_int, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_double] + [_vp] * 4),
+    "cgtp_cp_conv_fwd": (ctypes.c_int, [_vp, ctypes.c_int, _c_i64, _c_i64] + [_vp] * 10 + [ctypes.c_size_t, _vp]),
+    "cgtp_cp_conv_bwd": (ctypes.c_int, [_vp, ctypes.c_int, _c_i64, _c_i64] + [_vp] * 13 + [ctypes.c_size_t, _vp]),
     "cgtp_conv_bwd_noalloc": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                              _vp]),
     "cgtp_status_string": (ctypes.c_char_p, [ctypes.c_int]),

@@ -14,6 +14,7 @@
 #include <unordered_map>
 #include <vector>
 
+#include "cgtp_cp.h"
 #include "cgtp_internal.h"
 #include "cgtp_math.h"
 
@@ -432,6 +433,156 @@ cgtp_status_t cgtp_conv_bwd_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edg
     return st;
 }
 
+// ---- CP-decomposed tensor product ------------------------------------------
+cgtp_status_t cgtp_cp_workspace_size(cgtp_plan_t plan, int rank, int64_t n_nodes, int64_t n_edges, size_t* bytes)
+{
+    if (!plan || !bytes || n_nodes < 0 || n_edges < 0 || rank < 1) return CGTP_ERR_INVALID_ARG;
+    if (rank > cgtp::kMaxCpRank) return CGTP_ERR_UNSUPPORTED;
+    *bytes = cgtp::cp_ws_layout(n_nodes, n_edges, cgtp::cp_padded_rank(rank), plan->channels).total;
+    return CGTP_OK;
+}
+
+cgtp_status_t cgtp_cp_fit(cgtp_plan_t plan, int rank, int sweeps, double ridge, double* A, double* B, double* C,
+                          double* rel_err)
+{
+    if (!plan || rank < 1 || sweeps < 0 || !(ridge >= 0.0) || !A || !B || !C) return CGTP_ERR_INVALID_ARG;
+    const int d1 = plan->d_in, d2 = plan->d_sh, d3 = plan->d_out;
+    std::vector<double> M((size_t)d1 * d2 * d3, 0.0), T;
+    for (int p = 0; p < plan->P; ++p) {
+        const int l1 = plan->paths[3 * p], l2 = plan->paths[3 * p + 1], l3 = plan->paths[3 * p + 2];
+        const int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
+        T.assign((size_t)n1 * n2 * n3, 0.0);
+        if (!cgtp::host_cg_table(plan->lm, plan->super_index[(size_t)p], T.data())) return CGTP_ERR_UNSUPPORTED;
+        for (int a = 0; a < n1; ++a)
+            for (int b = 0; b < n2; ++b)
+                for (int c = 0; c < n3; ++c)
+                    M[((size_t)(l1 * l1 + a) * d2 + (l2 * l2 + b)) * d3 + (l3 * l3 + c)] =
+                        T[((size_t)a * n2 + b) * n3 + c];
+    }
+    return cgtp::cp_als_fit(M.data(), d1, d2, d3, rank, sweeps, ridge, A, B, C, rel_err) ? CGTP_OK
+                                                                                          : CGTP_ERR_NUMERIC;
+}
+
+namespace {
+
+// shared checks of the two CP convolution calls
+cgtp_status_t cp_prepare(const cgtp_plan_s* plan, int rank, int64_t n_nodes, int64_t n_edges,
+                         const int32_t* row_ptr, const int32_t* src, void* ws, size_t ws_bytes,
+                         const cgtp::CpKernelSet** ks, cgtp::CpWsLayout* CL)
+{
+    cgtp_status_t st = check_graph_args(plan, n_nodes, n_edges, row_ptr, src);
+    if (st != CGTP_OK) return st;
+    if (rank < 1) return CGTP_ERR_INVALID_ARG;
+    *ks = cgtp::find_cp_kernels(rank, plan->channels);
+    if (!*ks) return CGTP_ERR_UNSUPPORTED;
+    *CL = cgtp::cp_ws_layout(n_nodes, n_edges, (*ks)->rp, plan->channels);
+    if (!ws || ws_bytes < CL->total) return CGTP_ERR_WORKSPACE;
+    if (((uintptr_t)ws & 255u) != 0) return CGTP_ERR_INVALID_ARG;
+    return CGTP_OK;
+}
+
+bool all_aligned(std::initializer_list<const void*> ps)
+{
+    for (const void* p : ps)
+        if (!p || !aligned16(p)) return false;
+    return true;
+}
+
+}  // namespace
+
+cgtp_status_t cgtp_cp_conv_fwd(cgtp_plan_t plan, int rank, int64_t n_nodes, int64_t n_edges,
+                               const int32_t* row_ptr, const int32_t* src, const float* x, const float* Y,
+                               const float* W, const float* A, const float* B, const float* C, float* out,
+                               void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    const cgtp::CpKernelSet* ks = nullptr;
+    cgtp::CpWsLayout CL{};
+    cgtp_status_t st = cp_prepare(plan, rank, n_nodes, n_edges, row_ptr, src, ws, ws_bytes, &ks, &CL);
+    if (st != CGTP_OK) return st;
+    if (n_nodes == 0) return CGTP_OK;
+    if (!all_aligned({x, out, A, B})) return CGTP_ERR_INVALID_ARG;
+    if (n_edges > 0 && !all_aligned({Y, W, C})) return CGTP_ERR_INVALID_ARG;
+    st = ensure_prepared(plan, n_nodes, n_edges, row_ptr, src, ws, stream);
+    if (st != CGTP_OK) return st;
+    char* base = (char*)ws;
+    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges);
+    const int Cn = plan->channels;
+    double* xb = (double*)(base + CL.xb);
+    double* yc = (double*)(base + CL.yc);
+    st = hip_status(ks->proj_rows(n_nodes, plan->d_in, rank, Cn, B, x, xb, stream));
+    if (st == CGTP_OK) st = hip_status(ks->proj_edge(n_edges, plan->d_sh, rank, C, Y, yc, stream));
+    if (st != CGTP_OK) return st;
+    cgtp::CpFwdArgs a{};
+    a.N = (int32_t)n_nodes;
+    a.E = (int32_t)n_edges;
+    a.C = Cn;
+    a.R = rank;
+    a.d3 = plan->d_out;
+    a.n_order = cgtp::conv_grid(n_nodes);
+    a.order = (const int32_t*)(base + L.rorder);
+    a.row_ptr = row_ptr;
+    a.src = src;
+    a.W = W;
+    a.A = A;
+    a.xb = xb;
+    a.yc = yc;
+    a.out = out;
+    return hip_status(ks->fwd(a, stream));
+}
+
+cgtp_status_t cgtp_cp_conv_bwd(cgtp_plan_t plan, int rank, int64_t n_nodes, int64_t n_edges,
+                               const int32_t* row_ptr, const int32_t* src, const float* x, const float* Y,
+                               const float* W, const float* A, const float* B, const float* C,
+                               const float* grad_out, float* grad_x, float* grad_W, float* grad_Y, void* ws,
+                               size_t ws_bytes, hipStream_t stream)
+{
+    const cgtp::CpKernelSet* ks = nullptr;
+    cgtp::CpWsLayout CL{};
+    cgtp_status_t st = cp_prepare(plan, rank, n_nodes, n_edges, row_ptr, src, ws, ws_bytes, &ks, &CL);
+    if (st != CGTP_OK) return st;
+    if ((!grad_x && !grad_W && !grad_Y) || n_nodes == 0) return CGTP_OK;
+    if (!all_aligned({x, grad_out, A, B})) return CGTP_ERR_INVALID_ARG;
+    if (n_edges > 0 && !all_aligned({Y, W, C})) return CGTP_ERR_INVALID_ARG;
+    for (const void* p : {(const void*)grad_x, (const void*)grad_W, (const void*)grad_Y})
+        if (p && !aligned16(p)) return CGTP_ERR_INVALID_ARG;
+    st = ensure_prepared(plan, n_nodes, n_edges, row_ptr, src, ws, stream);
+    if (st != CGTP_OK) return st;
+    char* base = (char*)ws;
+    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges);
+    const int Cn = plan->channels;
+    double* xb = (double*)(base + CL.xb);
+    double* ga = (double*)(base + CL.ga);
+    double* yc = (double*)(base + CL.yc);
+    double* dyc = (double*)(base + CL.dyc);
+    st = hip_status(ks->proj_rows(n_nodes, plan->d_in, rank, Cn, B, x, xb, stream));
+    if (st == CGTP_OK) st = hip_status(ks->proj_rows(n_nodes, plan->d_out, rank, Cn, A, grad_out, ga, stream));
+    if (st == CGTP_OK) st = hip_status(ks->proj_edge(n_edges, plan->d_sh, rank, C, Y, yc, stream));
+    if (st != CGTP_OK) return st;
+    cgtp::CpBwdArgs a{};
+    a.N = (int32_t)n_nodes;
+    a.E = (int32_t)n_edges;
+    a.C = Cn;
+    a.R = rank;
+    a.d1 = plan->d_in;
+    a.n_order = cgtp::conv_grid(n_nodes);
+    a.order = (const int32_t*)(base + L.sorder);
+    a.srow = (const int32_t*)(base + L.srow);
+    a.perm = (const int32_t*)(base + L.perm);
+    a.sdst = (const int32_t*)(base + L.sdst);
+    a.W = W;
+    a.B = B;
+    a.xb = xb;
+    a.ga = ga;
+    a.yc = yc;
+    a.dx = grad_x;
+    a.dW = grad_W;
+    a.dyc = grad_Y ? dyc : nullptr;
+    a.dwa = (double*)(base + CL.dwa);
+    st = hip_status(ks->bwd(a, stream));
+    if (st != CGTP_OK || !grad_Y) return st;
+    return hip_status(ks->edge_back(n_edges, plan->d_sh, rank, ks->h, C, dyc, grad_Y, stream));
+}
+
 cgtp_status_t cgtp_conv_bwd_noalloc(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
                                     const int32_t* src, const float* x, const float* Y, const float* W,
                                     const float* grad_out, float* grad_x, float* grad_W, float* grad_Y,
@@ -493,6 +644,7 @@ const char* cgtp_status_string(cgtp_status_t status)
         case CGTP_ERR_HIP: return "HIP error";
         case CGTP_ERR_ALLOC: return "host allocation failed";
         case CGTP_ERR_GRAPH: return "malformed CSR graph";
+        case CGTP_ERR_NUMERIC: return "CP fit: normal matrix not positive definite";
     }
     return "unknown status";
 }

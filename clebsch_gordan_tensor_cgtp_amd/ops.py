@@ -214,3 +214,64 @@ class Plan:
             _ptr(gg_Y), _ptr(gg_W), _ptr(dd_x), _ptr(dd_Y), _ptr(dd_W), _ptr(dd_out), _ptr(ws), ws.numel(),
             _stream(dev)))
         return dd_x, dd_Y, dd_W, dd_out
+
+    # -- CP-decomposed tensor product -------------------------------------------
+    def cp_workspace_size(self, rank: int, n_nodes: int, n_edges: int) -> int:
+        b = ctypes.c_size_t()
+        L.check("cgtp_cp_workspace_size", L.lib().cgtp_cp_workspace_size(self._h, rank, n_nodes, n_edges,
+                                                                          ctypes.byref(b)))
+        return b.value
+
+    def cp_fit(self, A0, B0, C0, sweeps: int, ridge: float = 1e-12):
+        """Data-free ALS fit of the rank-R factors of the plan's coupling
+        tensor from the start (A0 [d3][R], B0 [d1][R], C0 [d2][R]); host
+        computation.  Returns (A, B, C, relative Frobenius error)."""
+        R = A0.shape[1]
+        A, B, C = (np.ascontiguousarray(v, dtype=np.float64).copy() for v in (A0, B0, C0))
+        if A.shape != (self.dim_out, R) or B.shape != (self.dim_in, R) or C.shape != (self.dim_sh, R):
+            raise ValueError("factor shapes must be [d_out][R], [d_in][R], [d_sh][R]")
+        err = ctypes.c_double()
+        dp = lambda a: ctypes.c_void_p(a.ctypes.data)
+        L.check("cgtp_cp_fit", L.lib().cgtp_cp_fit(self._h, R, sweeps, ridge, dp(A), dp(B), dp(C), ctypes.byref(err)))
+        return A, B, C, err.value
+
+    def _cp_common(self, row_ptr, src, x, Y, W, A, B, C, ws):
+        N, E, Ch, dev = row_ptr.shape[0] - 1, src.shape[0], self.channels, row_ptr.device
+        R = A.shape[1]
+        _need(row_ptr, "row_ptr", torch.int32)
+        _need(src, "src", torch.int32, (E,), dev)
+        _need(x, "x", torch.float32, (N, self.dim_in, Ch), dev)
+        _need(Y, "Y", torch.float32, (E, self.dim_sh), dev)
+        _need(W, "W", torch.float32, (E, Ch), dev)
+        _need(A, "A", torch.float32, (self.dim_out, R), dev)
+        _need(B, "B", torch.float32, (self.dim_in, R), dev)
+        _need(C, "C", torch.float32, (self.dim_sh, R), dev)
+        if ws is None:
+            ws = torch.empty(self.cp_workspace_size(R, N, E), dtype=torch.uint8, device=dev)
+            self.graph_prepare(row_ptr, src, ws)   # see _workspace
+        _need(ws, "ws", torch.uint8, device=dev)
+        return N, E, Ch, dev, R, ws
+
+    def cp_conv_fwd(self, row_ptr, src, x, Y, W, A, B, C, ws=None, out=None) -> torch.Tensor:
+        """CP convolution out[N][D_out][C]: W [E][C]; factors A [D_out][R],
+        B [D_in][R], C [D_sh][R] (fp32, on the device)."""
+        N, E, Ch, dev, R, ws = self._cp_common(row_ptr, src, x, Y, W, A, B, C, ws)
+        if out is None:
+            out = torch.empty((N, self.dim_out, Ch), dtype=torch.float32, device=dev)
+        _need(out, "out", torch.float32, (N, self.dim_out, Ch), dev)
+        L.check("cgtp_cp_conv_fwd", L.lib().cgtp_cp_conv_fwd(
+            self._h, R, N, E, _ptr(row_ptr), _ptr(src), _ptr(x), _ptr(Y), _ptr(W), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(out), _ptr(ws), ws.numel(), _stream(dev)))
+        return out
+
+    def cp_conv_bwd(self, row_ptr, src, x, Y, W, A, B, C, grad_out, ws=None, want=("dx", "dW", "dY")):
+        """(grad_x [N][D_in][C], grad_W [E][C], grad_Y [E][D_sh]) of the CP
+        convolution; a gradient not in ``want`` comes back as None."""
+        N, E, Ch, dev, R, ws = self._cp_common(row_ptr, src, x, Y, W, A, B, C, ws)
+        _need(grad_out, "grad_out", torch.float32, (N, self.dim_out, Ch), dev)
+        new = lambda shape, key: torch.empty(shape, dtype=torch.float32, device=dev) if key in want else None
+        dx, dW, dY = new((N, self.dim_in, Ch), "dx"), new((E, Ch), "dW"), new((E, self.dim_sh), "dY")
+        L.check("cgtp_cp_conv_bwd", L.lib().cgtp_cp_conv_bwd(
+            self._h, R, N, E, _ptr(row_ptr), _ptr(src), _ptr(x), _ptr(Y), _ptr(W), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(grad_out), _ptr(dx), _ptr(dW), _ptr(dY), _ptr(ws), ws.numel(), _stream(dev)))
+        return dx, dW, dY

@@ -72,7 +72,8 @@ typedef enum {
     CGTP_ERR_WORKSPACE = -3,    /* workspace missing or smaller than cgtp_workspace_size */
     CGTP_ERR_HIP = -4,          /* a HIP call or kernel launch failed */
     CGTP_ERR_ALLOC = -5,        /* host allocation failed */
-    CGTP_ERR_GRAPH = -6         /* CGTP_FLAG_VALIDATE found a malformed CSR */
+    CGTP_ERR_GRAPH = -6,        /* CGTP_FLAG_VALIDATE found a malformed CSR */
+    CGTP_ERR_NUMERIC = -7       /* the CP fit met a normal matrix that is not positive definite */
 } cgtp_status_t;
 
 /* Validate the CSR (on a host copy, synchronously) in every call taking a graph. */
@@ -207,6 +208,61 @@ cgtp_status_t cgtp_conv_bwd_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edg
                                 const float* grad_out, const float* gg_x, const float* gg_Y, const float* gg_W,
                                 float* dd_x, float* dd_Y, float* dd_W, float* dd_out, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
+
+/* ---- CP-decomposed tensor product ----------------------------------------
+ * The approximate product of "Tensor Decomposition Networks for Accelerating
+ * Machine Learning Force Field Computations" (authors' rebuttal to S6y1,
+ * Equation (3)): the coupling of x (d1 = (l_in+1)^2 components) and y
+ * (d2 = (l_sh+1)^2) into z (d3 = (l_out+1)^2) is z = A (B^T x (.) C^T y)
+ * with rank-R factors A [d3][R], B [d1][R], C [d2][R] (row-major), which
+ * approximate the whole coupling tensor M of the plan's degrees (every
+ * path's real CG block at its components).  Over the graph, with one weight
+ * per edge and channel:
+ *   out[i][:,u] = sum_{e = j->i} W[e][u] A (B^T x[j][:,u] (.) C^T Y[e])
+ * W is [E][C] whatever the plan's weight flags.  Ranks 1..64; the plan's
+ * degrees and channel count (1..128) apply. */
+
+/* Workspace of the CP calls: the graph view of cgtp_workspace_size followed
+ * by the projected rows (B^T x and A^T grad_out per node, C^T Y and its
+ * gradient per edge).  One such workspace serves cgtp_graph_prepare and the
+ * CP calls of one graph. */
+cgtp_status_t cgtp_cp_workspace_size(cgtp_plan_t plan, int rank, int64_t n_nodes, int64_t n_edges,
+                                     size_t* bytes);
+
+/* Data-free fit of the factors (same rebuttal, reply on Figure 3: minimise
+ * the Frobenius norm between the exact and the approximate product over
+ * standard-normal inputs, once, before training).  Over independent
+ * standard-normal x, y the expected squared error equals ||M - [[A,B,C]]||_F^2,
+ * so this runs alternating least squares on M: per sweep B, then C, then A
+ * is replaced by its exact least-squares solution with the other two fixed
+ * (normal matrix plus ridge * trace / R on its diagonal; ridge 0 is allowed).
+ * A [d3][rank], B [d1][rank], C [d2][rank] are host fp64 arrays: the starting
+ * point on entry (the caller draws it, e.g. standard normal), the fit on
+ * return.  *rel_err (may be NULL) = ||M - [[A,B,C]]||_F / ||M||_F.  Host
+ * computation, no GPU.  CGTP_ERR_NUMERIC if a normal matrix is not positive
+ * definite (raise ridge). */
+cgtp_status_t cgtp_cp_fit(cgtp_plan_t plan, int rank, int sweeps, double ridge, double* A, double* B, double* C,
+                          double* rel_err);
+
+/* Forward of the CP convolution: out [N][d3][C] (a receiver without in-edges
+ * gets zeros).  A, B, C: the factors as fp32 device arrays.  Node-centric and
+ * atomic-free; B^T x is formed once per node and A applied once per receiver
+ * (inside `ws`, prepared here first unless cgtp_graph_prepare already did). */
+cgtp_status_t cgtp_cp_conv_fwd(cgtp_plan_t plan, int rank, int64_t n_nodes, int64_t n_edges,
+                               const int32_t* row_ptr, const int32_t* src, const float* x, const float* Y,
+                               const float* W, const float* A, const float* B, const float* C, float* out,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward of L = <grad_out, out> for the CP convolution, by the closed forms
+ * after Equation (3) (g_x = (g_z A (.) C^T y) B^T, g_y = (g_z A (.) B^T x) C^T,
+ * here with the edge weight and the sum over channels):
+ *   grad_x [N][d1][C], grad_W [E][C], grad_Y [E][d2]; each may be NULL.
+ * Sender-centric and atomic-free over the view in `ws`. */
+cgtp_status_t cgtp_cp_conv_bwd(cgtp_plan_t plan, int rank, int64_t n_nodes, int64_t n_edges,
+                               const int32_t* row_ptr, const int32_t* src, const float* x, const float* Y,
+                               const float* W, const float* A, const float* B, const float* C,
+                               const float* grad_out, float* grad_x, float* grad_W, float* grad_Y, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the
