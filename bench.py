@@ -212,6 +212,7 @@ def run_workload(torch, dev, key, steps, warmup, settle, locality=False):
     log(f"{key}: step {ms_step:.3f} ms | sh+prep {prep_ms:.3f} | fwd {fwd_ms:.3f} ms "
         f"({res['fwd_alg_gbs']:.0f} GB/s alg) | bwd {bwd_ms:.3f} ms ({res['bwd_alg_gbs']:.0f} GB/s alg)")
     res["double_backward"] = time_double_backward(torch, plan, stream, rp, src, x, Y, W, G, ws, ab, steps)
+    res["cp"] = time_cp(torch, plan, stream, rp, src, x, Y, G, (16, 32, 64) if key == HEADLINE else (32,), steps)
     host = None
     if key == HEADLINE:
         host = (w, g, x.cpu().numpy(), W.cpu().numpy(), G.cpu().numpy())
@@ -246,6 +247,59 @@ def time_double_backward(torch, plan, stream, rp, src, x, Y, W, G, ws, ab, steps
     log(f"  double backward: dd_out {res['dd_out']['ms']:.3f} ms ({res['dd_out']['alg_gbs']:.0f} GB/s alg) | "
         f"dd_x,dd_Y,dd_W {res['dd_x_Y_W']['ms']:.3f} ms ({res['dd_x_Y_W']['alg_gbs']:.0f} GB/s alg)")
     return res
+
+
+def cp_alg_bytes(N, E, C, d_in, d_sh, d_out):
+    """Bytes the CP convolution must move: forward reads x, Y, one weight per
+    edge and channel, the CSR, and writes out; backward reads x, grad_out, Y,
+    W, the view and writes grad_x, grad_W, grad_Y (the projected rows are the
+    implementation's own traffic, not counted)."""
+    fwd = E * (4 * C + 4 * d_sh + 4) + N * (4 * C * (d_in + d_out) + 4)
+    bwd = E * (8 * C + 8 * d_sh + 8) + N * (4 * C * (2 * d_in + d_out) + 4)
+    return fwd, bwd
+
+
+def time_cp(torch, plan, stream, rp, src, x, Y, G, ranks, steps):
+    """The CP-decomposed convolution (one weight per edge and channel) with
+    factors from the library's data-free fit: median times of the whole
+    forward and backward calls (projections included), HIP events on their
+    stream."""
+    import numpy as np
+
+    N, E, C = x.shape[0], Y.shape[0], plan.channels
+    W = torch.randn((E, C), device=x.device) / math.sqrt(plan.num_paths)
+    fb, bb = cp_alg_bytes(N, E, C, plan.dim_in, plan.dim_sh, plan.dim_out)
+    out = {}
+    for R in ranks:
+        rng = np.random.default_rng(R)
+        A, B, Cf, err = plan.cp_fit(rng.standard_normal((plan.dim_out, R)), rng.standard_normal((plan.dim_in, R)),
+                                    rng.standard_normal((plan.dim_sh, R)), sweeps=200)
+        fA, fB, fC = (torch.from_numpy(v.astype(np.float32)).to(x.device) for v in (A, B, Cf))
+        ws = torch.empty(plan.cp_workspace_size(R, N, E), dtype=torch.uint8, device=x.device)
+        plan.graph_prepare(rp, src, ws)
+        o = torch.empty((N, plan.dim_out, C), device=x.device)
+        res = {"fit_rel_err": err}
+        for name, fn in (("fwd", lambda: plan.cp_conv_fwd(rp, src, x, Y, W, fA, fB, fC, ws, out=o)),
+                         ("bwd", lambda: plan.cp_conv_bwd(rp, src, x, Y, W, fA, fB, fC, G, ws))):
+            for _ in range(3):
+                fn()
+            ts = []
+            for _ in range(max(5, steps)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                ts.append((e0, e1))
+            torch.cuda.synchronize()
+            ms = statistics.median(a.elapsed_time(b) for a, b in ts)
+            nb = fb if name == "fwd" else bb
+            res[name + "_ms"] = ms
+            res[name + "_alg_gbs"] = nb / (ms * 1e-3) / 1e9
+        res["fwd_bwd_edges_per_s"] = E / ((res["fwd_ms"] + res["bwd_ms"]) * 1e-3)
+        out[str(R)] = res
+        log(f"  CP rank {R} (fit error {err:.1e}): fwd {res['fwd_ms']:.3f} ms | bwd {res['bwd_ms']:.3f} ms")
+        del ws, o
+    return out
 
 
 def cpu_model():
