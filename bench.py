@@ -25,6 +25,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import subprocess
 import sys
@@ -132,7 +133,7 @@ def make_inputs(torch, dev, key, seed=0):
     return w, g, T(g.row_ptr), T(g.src), T(g.r), x, W, G
 
 
-def run_workload(torch, dev, key, steps, warmup, settle, locality=False):
+def run_workload(torch, dev, key, steps, warmup, settle, locality=False, extras=True):
     """Time `steps` whole steps of workload `key`.  Returns the measurements
     and the host-side inputs (for the CPU baseline)."""
     from clebsch_gordan_tensor_cgtp_amd.ops import Plan
@@ -211,8 +212,10 @@ def run_workload(torch, dev, key, steps, warmup, settle, locality=False):
     }
     log(f"{key}: step {ms_step:.3f} ms | sh+prep {prep_ms:.3f} | fwd {fwd_ms:.3f} ms "
         f"({res['fwd_alg_gbs']:.0f} GB/s alg) | bwd {bwd_ms:.3f} ms ({res['bwd_alg_gbs']:.0f} GB/s alg)")
-    res["double_backward"] = time_double_backward(torch, plan, stream, rp, src, x, Y, W, G, ws, ab, steps)
-    res["cp"] = time_cp(torch, plan, stream, rp, src, x, Y, G, (16, 32, 64) if key == HEADLINE else (32,), steps)
+    if extras:
+        res["double_backward"] = time_double_backward(torch, plan, stream, rp, src, x, Y, W, G, ws, ab, steps)
+        res["cp"] = time_cp(torch, plan, stream, rp, src, x, Y, G, (16, 32, 64) if key == HEADLINE else (32,),
+                            steps)
     host = None
     if key == HEADLINE:
         host = (w, g, x.cpu().numpy(), W.cpu().numpy(), G.cpu().numpy())
@@ -419,7 +422,7 @@ def _pmc(path):
 
 
 def _short(name):
-    return name.replace("void ", "").replace("cgtp::", "").split("(")[0]
+    return name.replace("void ", "").replace("(anonymous namespace)::", "").replace("cgtp::", "").split("(")[0]
 
 
 def summarize(d, workload):
@@ -427,6 +430,7 @@ def summarize(d, workload):
     from the rocprofv3 output under `d` (subdirectories named as in the
     commands each summary lists)."""
     cmd = f"python3 bench.py --workloads {workload} --steps 10 --warmup 2 --settle 0.3 --no-cpu-baseline"
+    cmd_pmc = cmd + " --no-extras"
     def find(sub, f):
         # the copy calibration may sit beside the workload's directory
         for base in (d, os.path.dirname(os.path.normpath(d))):
@@ -459,14 +463,15 @@ def summarize(d, workload):
     D = (w.l_max + 1) ** 2
     alg_all = algorithmic_bytes(g.n_nodes, g.n_edges, w.num_paths, w.channels, D, D, D)
     for kern in ("conv_fwd", "conv_bwd"):
-        name = [k for k in fetch if f"k_{kern}<" in k][0]
+        # the step's kernel (the double backward instantiates the same template with DBL = true)
+        name = [k for k in fetch if re.search(rf"k_{kern}<\d+, \d+, \d+, (true|false), false>", k)][0]
         fk, wk = fetch[name]["FETCH_SIZE"], write[name]["WRITE_SIZE"]
         rd, wr = fk * 1024 * ff, wk * 1024 * wf
         alg = alg_all[kern.split("_")[1]]
         lines = [f"# HBM traffic of {_short(name)} on the {workload} workload ({w.name})",
                  "# commands (repo root; one counter per pass):",
-                 f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o run -- {cmd}",
-                 f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o run -- {cmd}",
+                 f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o run -- {cmd_pmc}",
+                 f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o run -- {cmd_pmc}",
                  "# calibration on a plain copy of known size (torch neg() over 1 GiB fp32: 1 GiB read + 1 GiB written):",
                  "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/cal_fetch -o run -- python3 bench.py --copy-calibration",
                  "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/cal_write -o run -- python3 bench.py --copy-calibration",
@@ -487,14 +492,14 @@ def summarize(d, workload):
     lines = [f"# SQ / GRBM counters of the convolution kernels on the {workload} workload (medians over launches)",
              "# commands (repo root):",
              f"#   rocprofv3 --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
-             f"SQ_ACTIVE_INST_VALU SQ_INSTS_VALU GRBM_GUI_ACTIVE GRBM_COUNT --output-format csv -d <dir>/sq1 -o run -- {cmd}",
+             f"SQ_ACTIVE_INST_VALU SQ_INSTS_VALU GRBM_GUI_ACTIVE GRBM_COUNT --output-format csv -d <dir>/sq1 -o run -- {cmd_pmc}",
              f"#   rocprofv3 --pmc SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_SCA SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR "
-             f"SQ_INSTS_SALU SQ_INST_CYCLES_VMEM_RD SQ_WAIT_INST_LDS --output-format csv -d <dir>/sq2 -o run -- {cmd}",
+             f"SQ_INSTS_SALU SQ_INST_CYCLES_VMEM_RD SQ_WAIT_INST_LDS --output-format csv -d <dir>/sq2 -o run -- {cmd_pmc}",
              "# derived (per launch): gpu_cycles = GRBM_GUI_ACTIVE / 8 (one count per XCD); VALU busy =",
              "# 4 * SQ_ACTIVE_INST_VALU / (gpu_cycles * 1024 SIMDs) (SQ cycle counters count 4-cycle units);",
              "# mean resident waves per SIMD = 4 * SQ_WAVE_CYCLES / (gpu_cycles * 1024)"]
     for name, c in sq.items():
-        if "k_conv" not in name:
+        if not re.search(r"k_conv_(fwd|bwd)<\d+, \d+, \d+, (true|false), false>", name):
             continue
         c = dict(c)
         c.update(sq2.get(name, {}))
@@ -521,6 +526,8 @@ def main():
     ap.add_argument("--workloads", default=",".join([HEADLINE] + OTHERS),
                     help="comma list; the first is the headline (value)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the step (skip the double-backward and CP legs)")
     ap.add_argument("--locality", action="store_true",
                     help="schedule blocks by graph-derived clusters per XCD instead of longest first")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -558,10 +565,11 @@ def main():
         print(json.dumps(copy_ceiling(torch, dev)), flush=True)
         return
 
-    head, host = run_workload(torch, dev, keys[0], args.steps, args.warmup, args.settle, args.locality)
+    extras = not args.no_extras
+    head, host = run_workload(torch, dev, keys[0], args.steps, args.warmup, args.settle, args.locality, extras)
     others = {}
     for k in keys[1:]:
-        others[k], _ = run_workload(torch, dev, k, max(5, args.steps // 2), 2, args.settle, args.locality)
+        others[k], _ = run_workload(torch, dev, k, max(5, args.steps // 2), 2, args.settle, args.locality, extras)
 
     kern, kms, kbytes = "conv_bwd", head["bwd_ms"], head["alg_bytes"]["bwd"]
     achieved = kbytes / (kms * 1e-3) / 1e9
