@@ -16,7 +16,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "cgtp_oracle.c")
 PINS = ["tests/test_oracle_cg.py", "tests/test_oracle_sh.py", "tests/test_oracle_conv.py",
-        "tests/test_oracle_forces.py"]
+        "tests/test_oracle_forces.py", "tests/test_oracle_cp.py"]
 
 # (name, text in the oracle source, replacement): each text occurs exactly once
 MUTATIONS = [
@@ -48,6 +48,19 @@ MUTATIONS = [
     ("SH backward: wrong l=3 derivative", "gx += w[15] * 3.0 * a * (x * x - y * y);",
      "gx += w[15] * 3.0 * a * (x * x + y * y);"),
     ("node gradient: receiver sign", "dpos[3 * i + a] -= dr[3 * e + a];", "dpos[3 * i + a] += dr[3 * e + a];"),
+    ("double backward: ggY term dropped from d_out",
+     "c * (ORC_GX(a) * ORC_Y(b) * ORC_W + ORC_X(a) * ORC_GY(b) * ORC_W +",
+     "c * (ORC_GX(a) * ORC_Y(b) * ORC_W + 0.0 * ORC_GY(b) * ORC_W +"),
+    ("double backward: weight and its cotangent swapped in d_Y",
+     "if (dY) dY[e * Dsh + b] += c * (ORC_GX(a) * ORC_W + ORC_X(a) * ORC_GW) * ORC_G(k3);",
+     "if (dY) dY[e * Dsh + b] += c * (ORC_GX(a) * ORC_GW + ORC_X(a) * ORC_W) * ORC_G(k3);"),
+    ("double backward: d_x without the ggW term",
+     "c * (ORC_GY(b) * ORC_W + ORC_Y(b) * ORC_GW) * ORC_G(k3);", "c * (ORC_GY(b) * ORC_W) * ORC_G(k3);"),
+    ("CP forward: C^T y factor dropped", "for (int r = 0; r < R; ++r) z += A[c * R + r] * s[r] * t[r];",
+     "for (int r = 0; r < R; ++r) z += A[c * R + r] * s[r];"),
+    ("CP backward: B^T x used in g_x", "for (int r = 0; r < R; ++r) v += B[a * R + r] * ga[r] * t[r];",
+     "for (int r = 0; r < R; ++r) v += B[a * R + r] * ga[r] * s[r];"),
+    ("CP backward: edge weight dropped in g_y", "dY[e * d2 + b] += w * v;", "dY[e * d2 + b] += v;"),
 ]
 
 
