@@ -213,6 +213,7 @@ def run_workload(torch, dev, key, steps, warmup, settle, locality=False, extras=
     log(f"{key}: step {ms_step:.3f} ms | sh+prep {prep_ms:.3f} | fwd {fwd_ms:.3f} ms "
         f"({res['fwd_alg_gbs']:.0f} GB/s alg) | bwd {bwd_ms:.3f} ms ({res['bwd_alg_gbs']:.0f} GB/s alg)")
     if extras:
+        res["forces"] = time_forces(torch, plan, stream, rp, src, r, Y, ws, steps)
         res["double_backward"] = time_double_backward(torch, plan, stream, rp, src, x, Y, W, G, ws, ab, steps)
         res["cp"] = time_cp(torch, plan, stream, rp, src, x, Y, G, (16, 32, 64) if key == HEADLINE else (32,),
                             steps)
@@ -222,6 +223,36 @@ def run_workload(torch, dev, key, steps, warmup, settle, locality=False, extras=
     del Y, out, dx, dW, dY, ws, x, W, G
     torch.cuda.empty_cache()
     return res, host
+
+
+def time_forces(torch, plan, stream, rp, src, r, Y, ws, steps):
+    """Median launch times of the path from grad_Y to the forces: the SH
+    backward (grad_Y -> grad_r) and the per-node gradient (grad_r ->
+    grad_pos), HIP events on their stream.  Algorithmic bytes: r, grad_Y read
+    and grad_r written per edge; grad_r and the view entry read per edge and
+    grad_pos, row_ptr, srow per node."""
+    N, E = rp.shape[0] - 1, r.shape[0]
+    gY = torch.randn_like(Y)
+    gr = torch.empty((E, 3), device=r.device)
+    gp = torch.empty((N, 3), device=r.device)
+    legs = {"sh_bwd": (lambda: plan.sh_bwd(r, gY, gr), E * (12 + 4 * plan.dim_sh + 12)),
+            "node_grad": (lambda: plan.node_grad(rp, src, gr, ws, gp), E * (12 + 4) + N * (12 + 8))}
+    res = {}
+    for name, (fn, nbytes) in legs.items():
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(max(5, steps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = statistics.median(a.elapsed_time(b) for a, b in ts)
+        res[name] = {"ms": ms, "alg_bytes": nbytes, "alg_gbs": nbytes / (ms * 1e-3) / 1e9}
+    log(f"  forces: sh_bwd {res['sh_bwd']['ms'] * 1e3:.1f} us | node_grad {res['node_grad']['ms'] * 1e3:.1f} us")
+    return res
 
 
 def time_double_backward(torch, plan, stream, rp, src, x, Y, W, G, ws, ab, steps):
