@@ -59,6 +59,10 @@ def _load():
     lib.orc_cp_conv_fwd.argtypes = [ctypes.c_int] * 5 + [ctypes.c_int64, _i64p, _i64p] + [_dp] * 7
     lib.orc_cp_conv_bwd.restype = None
     lib.orc_cp_conv_bwd.argtypes = [ctypes.c_int] * 5 + [ctypes.c_int64] * 2 + [_i64p, _i64p] + [_dp] * 10
+    lib.orc_conv_fwd_mid.restype = ctypes.c_int
+    lib.orc_conv_fwd_mid.argtypes = [ctypes.c_int] * 4 + [ctypes.c_int64, _i64p, _i64p] + [_dp] * 4
+    lib.orc_conv_bwd_mid.restype = ctypes.c_int
+    lib.orc_conv_bwd_mid.argtypes = [ctypes.c_int] * 4 + [ctypes.c_int64] * 2 + [_i64p, _i64p] + [_dp] * 7
     lib.orc_graph_transpose.restype = None
     lib.orc_graph_transpose.argtypes = [ctypes.c_int64, ctypes.c_int64, _i64p, _i64p, _i64p, _i64p, _i64p]
     lib.orc_num_threads.restype = ctypes.c_int
@@ -173,6 +177,41 @@ def conv_bwd(l_in, l_sh, l_out, row_ptr, src, x, Y, W, G, want=("dx", "dW", "dY"
                               _p(dx) if dx is not None else None,
                               _p(dW) if dW is not None else None,
                               _p(dY) if dY is not None else None)
+    if rc != 0:
+        raise ValueError("oracle: unsupported degrees")
+    return dx, dW, dY
+
+
+def mid_rows(l_in, l_sh, l_out):
+    """Row count of the per-path outputs: sum over the paths of 2*l3+1."""
+    return int(sum(2 * l3 + 1 for (_, _, l3) in paths(l_in, l_sh, l_out)))
+
+
+def conv_fwd_mid(l_in, l_sh, l_out, row_ptr, src, x, Y, W):
+    """Per-path outputs out_mid[N][D_mid][C] (path p owns 2*l3+1 rows, in path order)."""
+    row_ptr, src = _i64(row_ptr), _i64(src)
+    x, Y, W = _f64(x), _f64(Y), _f64(W)
+    N, C = x.shape[0], x.shape[2]
+    out = np.zeros((N, mid_rows(l_in, l_sh, l_out), C))
+    rc = _load().orc_conv_fwd_mid(l_in, l_sh, l_out, C, N, _p(row_ptr, _i64p), _p(src, _i64p), _p(x), _p(Y), _p(W),
+                                  _p(out))
+    if rc != 0:
+        raise ValueError("oracle: unsupported degrees")
+    return out
+
+
+def conv_bwd_mid(l_in, l_sh, l_out, row_ptr, src, x, Y, W, G, want=("dx", "dW", "dY")):
+    """(dx, dW, dY) of <G_mid, out_mid>; a gradient not in ``want`` is None."""
+    row_ptr, src = _i64(row_ptr), _i64(src)
+    x, Y, W, G = _f64(x), _f64(Y), _f64(W), _f64(G)
+    N, C = x.shape[0], x.shape[2]
+    E = src.shape[0]
+    dx = np.zeros_like(x) if "dx" in want else None
+    dW = np.zeros_like(W) if "dW" in want else None
+    dY = np.zeros_like(Y) if "dY" in want else None
+    opt = lambda a: _p(a) if a is not None else None
+    rc = _load().orc_conv_bwd_mid(l_in, l_sh, l_out, C, N, E, _p(row_ptr, _i64p), _p(src, _i64p), _p(x), _p(Y),
+                                  _p(W), _p(G), opt(dx), opt(dW), opt(dY))
     if rc != 0:
         raise ValueError("oracle: unsupported degrees")
     return dx, dW, dY

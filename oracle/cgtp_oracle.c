@@ -447,6 +447,100 @@ int orc_conv_bwd(int lin, int lsh, int lout, int C, int64_t N, int64_t E,
     return 0;
 }
 
+/* Per-path (concatenated) outputs: path p keeps its own 2*l3+1 rows,
+ * rows o_p .. o_p + 2*l3 with o_p = sum over earlier paths of (2*l3+1), so
+ * out_mid [N][D_mid][C], D_mid = sum_p (2*l3+1):
+ *   out_mid[i][o_p + l3 + m3][u] = sum_{e in seg(i)} W[e][p][u]
+ *       sum_{m1,m2} T_p[m1][m2][m3] x[src e][k(l1,m1)][u] Y[e][k(l2,m2)].
+ * Summing the blocks of the paths of each l3 gives orc_conv_fwd. */
+int orc_conv_fwd_mid(int lin, int lsh, int lout, int C, int64_t N, const int64_t* row_ptr, const int64_t* src,
+                     const double* x, const double* Y, const double* W, double* out)
+{
+    orc_tables t;
+    if (orc_tables_make(lin, lsh, lout, &t)) return -1;
+    const int Din = (lin + 1) * (lin + 1), Dsh = (lsh + 1) * (lsh + 1), P = t.P;
+    int o[64], Dmid = 0;
+    for (int p = 0; p < P; ++p) {
+        o[p] = Dmid;
+        Dmid += 2 * t.paths[3 * p + 2] + 1;
+    }
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < N; ++i) {
+        double* op = out + i * Dmid * C;
+        for (int q = 0; q < Dmid * C; ++q) op[q] = 0.0;
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+            const int64_t j = src[e];
+            for (int p = 0; p < P; ++p) {
+                const int l1 = t.paths[3 * p], l2 = t.paths[3 * p + 1], l3 = t.paths[3 * p + 2];
+                for (int u = 0; u < C; ++u) {
+                    const double w = W[(e * P + p) * C + u];
+                    for (int m1 = -l1; m1 <= l1; ++m1)
+                        for (int m2 = -l2; m2 <= l2; ++m2)
+                            for (int m3 = -l3; m3 <= l3; ++m3) {
+                                double c = t.T[p][((m1 + l1) * (2 * l2 + 1) + (m2 + l2)) * (2 * l3 + 1) + (m3 + l3)];
+                                if (c == 0.0) continue;
+                                op[(o[p] + l3 + m3) * C + u] += w * c * x[(j * Din + l1 * l1 + l1 + m1) * C + u] *
+                                                                Y[e * Dsh + l2 * l2 + l2 + m2];
+                            }
+                }
+            }
+        }
+    }
+    orc_tables_free(&t);
+    return 0;
+}
+
+/* Backward of L = <G_mid, out_mid> (G_mid [N][D_mid][C]): as orc_conv_bwd,
+ * with path p coupled to its own block G_mid[dst e][o_p + l3 + m3] instead
+ * of the l3 slot.  A NULL output is skipped; outputs are overwritten. */
+int orc_conv_bwd_mid(int lin, int lsh, int lout, int C, int64_t N, int64_t E, const int64_t* row_ptr,
+                     const int64_t* src, const double* x, const double* Y, const double* W, const double* G,
+                     double* dx, double* dW, double* dY)
+{
+    orc_tables t;
+    if (orc_tables_make(lin, lsh, lout, &t)) return -1;
+    const int Din = (lin + 1) * (lin + 1), Dsh = (lsh + 1) * (lsh + 1), P = t.P;
+    int o[64], Dmid = 0;
+    for (int p = 0; p < P; ++p) {
+        o[p] = Dmid;
+        Dmid += 2 * t.paths[3 * p + 2] + 1;
+    }
+    int64_t* dst = (int64_t*)malloc(sizeof(int64_t) * (E > 0 ? E : 1));
+    for (int64_t i = 0; i < N; ++i)
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) dst[e] = i;
+    if (dx)
+        for (int64_t q = 0; q < N * Din * C; ++q) dx[q] = 0.0;
+    /* per edge: dW, dY; dx scattered serially (plain and order-independent in exact arithmetic) */
+    for (int64_t e = 0; e < E; ++e) {
+        const int64_t j = src[e], i = dst[e];
+        if (dY)
+            for (int q = 0; q < Dsh; ++q) dY[e * Dsh + q] = 0.0;
+        for (int p = 0; p < P; ++p) {
+            const int l1 = t.paths[3 * p], l2 = t.paths[3 * p + 1], l3 = t.paths[3 * p + 2];
+            for (int u = 0; u < C; ++u) {
+                const double w = W[(e * P + p) * C + u];
+                double acc = 0.0;
+                for (int m1 = -l1; m1 <= l1; ++m1)
+                    for (int m2 = -l2; m2 <= l2; ++m2)
+                        for (int m3 = -l3; m3 <= l3; ++m3) {
+                            double c = t.T[p][((m1 + l1) * (2 * l2 + 1) + (m2 + l2)) * (2 * l3 + 1) + (m3 + l3)];
+                            if (c == 0.0) continue;
+                            const double xv = x[(j * Din + l1 * l1 + l1 + m1) * C + u];
+                            const double yv = Y[e * Dsh + l2 * l2 + l2 + m2];
+                            const double gv = G[(i * Dmid + o[p] + l3 + m3) * C + u];
+                            acc += c * xv * yv * gv;
+                            if (dx) dx[(j * Din + l1 * l1 + l1 + m1) * C + u] += w * c * yv * gv;
+                            if (dY) dY[e * Dsh + l2 * l2 + l2 + m2] += w * c * xv * gv;
+                        }
+                if (dW) dW[(e * P + p) * C + u] = acc;
+            }
+        }
+    }
+    free(dst);
+    orc_tables_free(&t);
+    return 0;
+}
+
 /* Double backward: the gradients of
  *   S = <ggx, dx> + <ggW, dW> + <ggY, dY>,   (dx, dW, dY) = orc_conv_bwd(x, Y, W, G),
  * with respect to x, Y, W and G (the higher-order derivatives LunaTP's

@@ -354,3 +354,62 @@ def test_double_backward_shared_weights_finite_differences(oracle):
         am[name] = a[name] - 1e-3 * d
         fd = (S(ap) - S(am)) / 2e-3
         assert fd == pytest.approx((got[name] * d).sum(), rel=1e-9, abs=1e-9), name
+
+
+@pytest.mark.parametrize("Ls", [(1, 1, 1), (2, 2, 2), (2, 1, 3), (3, 3, 3), (0, 2, 2)])
+def test_per_path_outputs_sum_to_the_convolution(oracle, Ls):
+    """The per-path blocks summed over the paths of each l3 are the pinned
+    (summed) convolution; the blocks sit in path order."""
+    from clebsch_gordan_tensor_cgtp_amd.synth import random_graph
+    rng = np.random.default_rng(sum(Ls) + 40)
+    N, C = 9, 3
+    g = random_graph(N, rng.integers(0, 5, size=N), seed=2)
+    P = oracle.paths(*Ls)
+    x = rng.normal(size=(N, (Ls[0] + 1) ** 2, C))
+    Y = rng.normal(size=(g.n_edges, (Ls[1] + 1) ** 2))
+    W = rng.normal(size=(g.n_edges, P.shape[0], C))
+    mid = oracle.conv_fwd_mid(*Ls, g.row_ptr, g.src, x, Y, W)
+    assert mid.shape[1] == oracle.mid_rows(*Ls) == sum(2 * l3 + 1 for (_, _, l3) in P)
+    summed = np.zeros((N, (Ls[2] + 1) ** 2, C))
+    o = 0
+    for (l1, l2, l3) in P:
+        summed[:, l3 * l3:(l3 + 1) ** 2] += mid[:, o:o + 2 * l3 + 1]
+        o += 2 * l3 + 1
+    np.testing.assert_allclose(summed, oracle.conv_fwd(*Ls, g.row_ptr, g.src, x, Y, W), rtol=1e-12, atol=1e-12)
+    # a single path's weights alone: its block is that path's part of the summed output
+    for q in (0, P.shape[0] - 1):
+        Wq = np.zeros_like(W)
+        Wq[:, q] = W[:, q]
+        l3 = P[q][2]
+        oq = sum(2 * P[k][2] + 1 for k in range(q))
+        np.testing.assert_allclose(mid[:, oq:oq + 2 * l3 + 1],
+                                   oracle.conv_fwd(*Ls, g.row_ptr, g.src, x, Y, Wq)[:, l3 * l3:(l3 + 1) ** 2],
+                                   rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("Ls", [(1, 1, 1), (2, 2, 2), (3, 2, 1)])
+def test_per_path_backward_finite_differences_and_replicated_grad(oracle, Ls):
+    """Exact central differences of <G_mid, out_mid>, and with every path's
+    block of G_mid set to the l3 slot of a summed G the per-path backward is
+    the pinned backward."""
+    from clebsch_gordan_tensor_cgtp_amd.synth import random_graph
+    rng = np.random.default_rng(sum(Ls) + 50)
+    N, C = 8, 2
+    g = random_graph(N, rng.integers(0, 5, size=N), seed=3)
+    P = oracle.paths(*Ls)
+    a = dict(x=rng.normal(size=(N, (Ls[0] + 1) ** 2, C)), Y=rng.normal(size=(g.n_edges, (Ls[1] + 1) ** 2)),
+             W=rng.normal(size=(g.n_edges, P.shape[0], C)))
+    Gm = rng.normal(size=(N, oracle.mid_rows(*Ls), C))
+    got = dict(zip(("x", "W", "Y"), oracle.conv_bwd_mid(*Ls, g.row_ptr, g.src, a["x"], a["Y"], a["W"], Gm)))
+    L = lambda v: (Gm * oracle.conv_fwd_mid(*Ls, g.row_ptr, g.src, v["x"], v["Y"], v["W"])).sum()
+    for name in ("x", "Y", "W"):
+        d = rng.normal(size=a[name].shape)
+        ap, am = dict(a), dict(a)
+        ap[name] = a[name] + 1e-3 * d
+        am[name] = a[name] - 1e-3 * d
+        assert (L(ap) - L(am)) / 2e-3 == pytest.approx((got[name] * d).sum(), rel=1e-9, abs=1e-9), name
+    Gs = rng.normal(size=(N, (Ls[2] + 1) ** 2, C))
+    Grep = np.concatenate([Gs[:, l3 * l3:(l3 + 1) ** 2] for (_, _, l3) in P], axis=1)
+    for u, v in zip(oracle.conv_bwd_mid(*Ls, g.row_ptr, g.src, a["x"], a["Y"], a["W"], Grep),
+                    oracle.conv_bwd(*Ls, g.row_ptr, g.src, a["x"], a["Y"], a["W"], Gs)):
+        np.testing.assert_allclose(u, v, rtol=1e-12, atol=1e-12)
