@@ -25,6 +25,7 @@ CGTP_ERR_NUMERIC = -7
 CGTP_FLAG_VALIDATE = 1
 CGTP_FLAG_LOCALITY = 2
 CGTP_FLAG_SHARED_WEIGHTS = 4
+CGTP_FLAG_PATH_OUTPUTS = 8
 
 _c_i64 = ctypes.c_int64
 _vp = ctypes.c_void_p

@@ -24,6 +24,8 @@ struct cgtp_plan_s {
     int P, d_in, d_sh, d_out;
     int lm;                         // compiled degree serving this plan
     bool sub;                       // degrees other than (lm, lm, lm)
+    bool mid;                       // per-path outputs
+    int d_mid;                      // their row count, sum of 2*l3+1
     std::vector<int> paths;         // [P][3]
     std::vector<int> super_index;   // [P]: index of each path in the compiled degree's path list
     cgtp::Shape shape;              // N and E filled in per call
@@ -34,7 +36,8 @@ struct cgtp_plan_s {
 
 namespace {
 
-constexpr unsigned kKnownFlags = CGTP_FLAG_VALIDATE | CGTP_FLAG_LOCALITY | CGTP_FLAG_SHARED_WEIGHTS;
+constexpr unsigned kKnownFlags =
+    CGTP_FLAG_VALIDATE | CGTP_FLAG_LOCALITY | CGTP_FLAG_SHARED_WEIGHTS | CGTP_FLAG_PATH_OUTPUTS;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -194,6 +197,7 @@ cgtp_status_t cgtp_plan_create(cgtp_plan_t* plan, int l_in, int l_sh, int l_out,
     p->flags = flags;
     p->lm = lm;
     const bool shared = (flags & CGTP_FLAG_SHARED_WEIGHTS) != 0;
+    p->mid = (flags & CGTP_FLAG_PATH_OUTPUTS) != 0;
     p->sub = shared || !(l_in == lm && l_sh == lm && l_out == lm);
     p->P = cgtp::cgmath::num_paths(l_in, l_sh, l_out);
     p->d_in = (l_in + 1) * (l_in + 1);
@@ -215,7 +219,7 @@ cgtp_status_t cgtp_plan_create(cgtp_plan_t* plan, int l_in, int l_sh, int l_out,
     s.P = shared ? 1 : p->P;
     s.shared = shared ? 1 : 0;
     const int Pm = cgtp::cgmath::num_paths(lm, lm, lm);
-    int q = 0;
+    int q = 0, rows = 0;
     for (int k = 0; k < Pm; ++k) {
         const cgtp::cgmath::Path t = cgtp::cgmath::path_at(lm, lm, lm, k);
         const bool mine = t.l1 <= l_in && t.l2 <= l_sh && t.l3 <= l_out;
@@ -225,7 +229,17 @@ cgtp_status_t cgtp_plan_create(cgtp_plan_t* plan, int l_in, int l_sh, int l_out,
         }
         // an inactive path reads a valid row (and gets weight 0)
         s.woff[k] = shared ? 0 : std::min(q, p->P - 1) * channels;
-        if (mine) ++q;
+        // per-path outputs: the path's first row, in the plan's path order
+        s.moff[k] = mine ? rows : -1;
+        if (mine) {
+            ++q;
+            rows += 2 * t.l3 + 1;
+        }
+    }
+    p->d_mid = rows;
+    if (p->mid) {
+        s.mid = 1;
+        s.d_out = rows;
     }
     p->shape = s;
     p->ks = ks;
@@ -249,7 +263,7 @@ cgtp_status_t cgtp_plan_info(cgtp_plan_t plan, int* num_paths, int* paths_l1l2l3
     if (paths_l1l2l3) memcpy(paths_l1l2l3, plan->paths.data(), sizeof(int) * plan->paths.size());
     if (dim_in) *dim_in = plan->d_in;
     if (dim_sh) *dim_sh = plan->d_sh;
-    if (dim_out) *dim_out = plan->d_out;
+    if (dim_out) *dim_out = plan->mid ? plan->d_mid : plan->d_out;
     return CGTP_OK;
 }
 
@@ -339,6 +353,7 @@ cgtp_status_t cgtp_conv_fwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
     a.Y = Y;
     a.W = W;
     a.out = out;
+    if (plan->mid) return hip_status(plan->ks->fwd_mid(a, stream));
     return hip_status(plan->ks->fwd[plan->sub ? 1 : 0](a, stream));
 }
 
@@ -373,6 +388,7 @@ cgtp_status_t cgtp_conv_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
     a.dx = grad_x;
     a.dW = grad_W;
     a.dY = grad_Y;
+    if (plan->mid) return hip_status(plan->ks->bwd_mid(a, stream));
     return hip_status(plan->ks->bwd[plan->sub ? 1 : 0](a, stream));
 }
 
@@ -384,6 +400,7 @@ cgtp_status_t cgtp_conv_bwd_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edg
 {
     cgtp_status_t st = check_graph_args(plan, n_nodes, n_edges, row_ptr, src);
     if (st != CGTP_OK) return st;
+    if (plan->mid) return CGTP_ERR_UNSUPPORTED;
     st = check_ws(n_nodes, n_edges, ws, ws_bytes);
     if (st != CGTP_OK) return st;
     if ((!dd_x && !dd_Y && !dd_W && !dd_out) || n_nodes == 0) return CGTP_OK;
@@ -631,6 +648,7 @@ cgtp_status_t cgtp_conv_bwd_noalloc(cgtp_plan_t plan, int64_t n_nodes, int64_t n
     a.dx = grad_x;
     a.dW = grad_W;
     a.dY = grad_Y;
+    if (plan->mid) return hip_status(plan->ks->bwd_mid(a, stream));
     return hip_status(plan->ks->bwd[plan->sub ? 1 : 0](a, stream));
 }
 

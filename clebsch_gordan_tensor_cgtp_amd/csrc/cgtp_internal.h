@@ -76,13 +76,19 @@ struct GraphView {
 // weights at element offset woff[p] (a multiple of C) inside the edge's
 // [P][C] weight row.  With path-weight sharing the row is [1][C]: every
 // woff[p] is 0 and the backward sums grad_W over the paths.
+//
+// With per-path outputs (mid = 1) the output and grad_out rows are not summed
+// per l3: path p owns rows moff[p] .. moff[p] + 2*l3 of a node's d_out =
+// sum_p (2*l3 + 1) rows (moff[p] = -1 for a compiled path the plan lacks).
 struct Shape {
     int32_t N, E, C;
-    int32_t d_in, d_sh, d_out;  // (l+1)^2 of the plan's degrees
+    int32_t d_in, d_sh, d_out;  // row widths: (l+1)^2 of the plan's degrees (d_out: per-path rows when mid)
     int32_t P;                  // weight rows per edge: the plan's path count, or 1 when shared
     int32_t shared;             // 1: one weight per edge and channel for every path
+    int32_t mid;                // 1: one output block per path
     uint64_t active;            // compiled paths the plan uses
     int32_t woff[kMaxPaths];    // weight offset of every compiled path (clamped for inactive ones)
+    int32_t moff[kMaxPaths];    // per-path outputs: first output row of every compiled path, or -1
 };
 
 enum GradMask : int { kGradX = 1, kGradW = 2, kGradY = 4 };
@@ -134,6 +140,11 @@ struct KernelSet {
     // dx, dW and dY
     FwdLaunch fwd_dbl;
     BwdLaunch bwd_dbl;
+    // per-path outputs (SUB form): fwd_mid writes every path's block of
+    // `out` (one launch per group of paths), bwd_mid reads every path's block
+    // of grad_out
+    FwdLaunch fwd_mid;
+    BwdLaunch bwd_mid;
 };
 
 // Kernels for compiled degree lm and channel count C, or nullptr.

@@ -558,12 +558,186 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s)
 }
 
 // ----------------------------------------------------------------------------
+// forward with per-path outputs
+// ----------------------------------------------------------------------------
+// Every path writes its own 2*l3+1 output rows instead of adding into the l3
+// slot (the summed output is the sum of these blocks over the paths of each
+// l3).  The compiled paths are cut into consecutive groups of at most kMidRows
+// output rows; one launch serves one group, so a lane's accumulators stay at
+// the summed forward's count at degree 3 (16) and the groups' outputs are
+// disjoint (no partial sums across launches).  Each launch gathers x_j and Y
+// again and reads only its paths' weights.
+constexpr int kMidRows = 16;
+
+template <class Tb>
+struct PathGroups {
+    struct Info {
+        int n;
+        int begin[kMaxPaths + 1];
+    };
+    static constexpr Info make()
+    {
+        Info r{};
+        int g = 0, rows = 0;
+        r.begin[0] = 0;
+        for (int p = 0; p < Tb::P; ++p) {
+            const int d3 = 2 * Tb::data.l3[p] + 1;
+            if (rows + d3 > kMidRows) {
+                r.begin[++g] = p;
+                rows = 0;
+            }
+            rows += d3;
+        }
+        r.n = g + 1;
+        r.begin[r.n] = Tb::P;
+        return r;
+    }
+    static constexpr Info info = make();
+    static constexpr int NG = info.n;
+    // rows of group g before path p (p inside the group), and the group's rows
+    static constexpr int row_of(int g, int p)
+    {
+        int r = 0;
+        for (int q = info.begin[g]; q < p; ++q) r += 2 * Tb::data.l3[q] + 1;
+        return r;
+    }
+    static constexpr int rows(int g) { return row_of(g, info.begin[g + 1]); }
+};
+
+template <class Tb, int G>
+struct MidEdge {
+    static constexpr int P0 = PathGroups<Tb>::info.begin[G], P1 = PathGroups<Tb>::info.begin[G + 1];
+    float w[P1 - P0], x[Tb::DIN], y[Tb::DSH];
+};
+
+template <class Tb, int G, bool UNI>
+__device__ __forceinline__ void fwd_load_mid(MidEdge<Tb, G>& d, int32_t e, uint32_t chl, const FwdArgs& a,
+                                             const Dims<Tb, true>& dm)
+{
+    using M = MidEdge<Tb, G>;
+    constexpr int DIN = Tb::DIN, DSH = Tb::DSH;
+    const int32_t C = edge_stride(a.sh.C);
+    chl = lane_offset(chl);
+    int32_t j = UNI ? scalar_load(a.src + e) : a.src[e];
+    j = (uint32_t)j < (uint32_t)a.sh.N ? j : 0;  // a sender outside [0, N) breaks the CSR contract
+    const float* wrow = a.W + (int64_t)e * (dm.P * C);
+    static_for<M::P0, M::P1>([&](auto PI) {
+        constexpr int p = decltype(PI)::value;
+        const float v = __builtin_nontemporal_load(at_lane(wrow + a.sh.woff[p], chl));
+        d.w[p - M::P0] = ((a.sh.active >> p) & 1) ? v : 0.0f;
+    });
+    const float* xrow = a.x + (int64_t)j * (dm.d_in * C);
+    static_for<0, DIN>([&](auto K) { d.x[K] = *at_lane(xrow + Dims<Tb, true>::template comp<decltype(K)::value>(dm.d_in) * C, chl); });
+    const float* yp = a.Y + (int64_t)e * dm.d_sh;
+    static_for<0, DSH>([&](auto K) { d.y[K] = yp[Dims<Tb, true>::template comp<decltype(K)::value>(dm.d_sh)]; });
+}
+
+template <int LM, int LPE, int H, int G>
+__global__ void __launch_bounds__(256, (Tune<LM, LPE>::fwd_occ)) k_conv_fwd_mid(FwdArgs a)
+{
+    using Tb = cgmath::Tables<LM, LM, LM>;
+    using Gm = Geo<LPE, H>;
+    using PG = PathGroups<Tb>;
+    using M = MidEdge<Tb, G>;
+    constexpr int DSH = Tb::DSH, S = Gm::S, CP = Gm::CP;
+    constexpr int DG = PG::rows(G);
+    __shared__ double red[S * DG * CP];
+
+    const int tid = threadIdx.x;
+    const Pos<LPE, H> ps(tid);
+    const int ch = ps.channel();
+    const int32_t C = a.sh.C;
+    const uint32_t chl = ch < C ? 4u * ch : 0u;
+    const Dims<Tb, true> dm(a.sh);
+    const int32_t i = a.rorder[blockIdx.x];
+    if ((uint32_t)i >= (uint32_t)a.sh.N) return;
+    const int32_t E = a.sh.E;
+    const int32_t e0 = clampi(a.row_ptr[i], 0, E);
+    const int32_t end = clampi(a.row_ptr[i + 1], e0, E);
+
+    double acc[DG];
+#pragma unroll
+    for (int k = 0; k < DG; ++k) acc[k] = 0.0;
+    for (int32_t e = e0 + ps.s; e < end; e += S) {
+        M cur;
+        fwd_load_mid<Tb, G, LPE == 64>(cur, e, chl, a, dm);
+        double yv[DSH], xv[Tb::DIN];
+        edge_sh<DSH, LPE>(cur.y, yv);
+#pragma unroll
+        for (int k = 0; k < Tb::DIN; ++k) xv[k] = (double)cur.x[k];
+        static_for<M::P0, M::P1>([&](auto PI) {
+            constexpr int p = decltype(PI)::value;
+            using K = PathK<Tb, p>;
+            constexpr int r0 = PG::row_of(G, p);
+            const double wd = (double)cur.w[p - M::P0];
+            static_for<0, K::d3>([&](auto M3) {
+                constexpr int m3 = decltype(M3)::value;
+                double z = 0.0;
+                bool any = false;
+                static_for<0, K::d1>([&](auto A) {
+                    static_for<0, K::d2>([&](auto B) {
+                        constexpr int a_ = decltype(A)::value, b = decltype(B)::value;
+                        constexpr double t = K::T(a_, b, m3);
+                        if constexpr (t != 0.0) mac(z, t, xv[K::k1 + a_] * yv[K::k2 + b], any);
+                    });
+                });
+                if (any) acc[r0 + m3] = __builtin_fma(wd, z, acc[r0 + m3]);
+            });
+            static_for<0, K::d3>([&](auto M3) { opaque(acc[r0 + decltype(M3)::value]); });
+        });
+    }
+
+    // combine the streams in a fixed order; each path's rows have this block as their only writer
+#pragma unroll
+    for (int k = 0; k < DG; ++k) red[(ps.s * DG + k) * CP + ch] = acc[k];
+    __syncthreads();
+    float* op = a.out + (int64_t)i * (dm.d_out * C);
+    for (int t = tid; t < DG * CP; t += 256) {
+        const int k = t / CP, c = t % CP;
+        // output row of local row k: the owning path's block
+        int32_t row = -1;
+        static_for<M::P0, M::P1>([&](auto PI) {
+            constexpr int p = decltype(PI)::value;
+            constexpr int r0 = PG::row_of(G, p), d3 = 2 * Tb::data.l3[p] + 1;
+            if (k >= r0 && k < r0 + d3 && a.sh.moff[p] >= 0) row = a.sh.moff[p] + (k - r0);
+        });
+        if (row >= 0 && row < dm.d_out && c < C) {
+            double v = 0.0;
+#pragma unroll
+            for (int q = 0; q < S; ++q) v += red[q * DG * CP + t];
+            op[row * C + c] = (float)v;
+        }
+    }
+}
+
+// launches of groups G, G+1, ... in order
+template <int LM, int LPE, int H, int G>
+hipError_t launch_fwd_mid_from(const FwdArgs& a, hipStream_t s)
+{
+    if constexpr (G < PathGroups<cgmath::Tables<LM, LM, LM>>::NG) {
+        hipLaunchKernelGGL((k_conv_fwd_mid<LM, LPE, H, G>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0, s, a);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        return launch_fwd_mid_from<LM, LPE, H, G + 1>(a, s);
+    } else {
+        return hipSuccess;
+    }
+}
+
+template <int LM, int LPE, int H>
+hipError_t launch_fwd_mid(const FwdArgs& a, hipStream_t s)
+{
+    if (a.sh.N == 0) return hipSuccess;
+    return launch_fwd_mid_from<LM, LPE, H, 0>(a, s);
+}
+
+// ----------------------------------------------------------------------------
 // backward
 // ----------------------------------------------------------------------------
 template <class Tb>
 struct BwdEdge {
     static constexpr int P = Tb::P, DSH = Tb::DSH, DOUT = Tb::DOUT;
-    int32_t e;
+    int32_t e, i;
     bool ok;  // the view entry names a valid edge and receiver
     float w[P], g[DOUT], y[DSH];
 };
@@ -572,7 +746,7 @@ struct BwdEdge {
 // offset chl; a
 // corrupt entry (possible only if the view was not prepared for this graph)
 // is read as edge 0 / receiver 0 and flagged, never used out of bounds
-template <class Tb, bool SUB, bool UNI>
+template <class Tb, bool SUB, bool UNI, bool LOADG = true>
 __device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, uint32_t chl, const BwdArgs& a,
                                          const Dims<Tb, SUB>& dm)
 {
@@ -584,6 +758,7 @@ __device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, uint32_t chl
     d.ok = (uint32_t)e < (uint32_t)a.sh.E && (uint32_t)i < (uint32_t)a.sh.N;
     if (!d.ok) e = i = 0;
     d.e = e;
+    d.i = i;
     const float* wrow = a.W + (int64_t)e * (dm.P * C);
     static_for<0, P>([&](auto PI) {
         constexpr int p = decltype(PI)::value;
@@ -594,8 +769,10 @@ __device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, uint32_t chl
             d.w[p] = __builtin_nontemporal_load(at_lane(wrow + p * C, chl));
         }
     });
-    const float* grow = a.G + (int64_t)i * (dm.d_out * C);
-    static_for<0, DOUT>([&](auto K) { d.g[K] = *at_lane(grow + Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_out) * C, chl); });
+    if constexpr (LOADG) {
+        const float* grow = a.G + (int64_t)i * (dm.d_out * C);
+        static_for<0, DOUT>([&](auto K) { d.g[K] = *at_lane(grow + Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_out) * C, chl); });
+    }
     const float* yp = a.Y + (int64_t)e * dm.d_sh;
     static_for<0, DSH>([&](auto K) {
         const float* p = yp + Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_sh);
@@ -822,6 +999,129 @@ __device__ __forceinline__ void bwd_slice_dbl(const BwdEdgeD<Tb>& d, const doubl
     });
 }
 
+// ---- per-path outputs, sender side ------------------------------------------
+// The backward of the per-path-output forward: as bwd_slice, with path p's
+// R_p formed from its own block of grad_out (rows moff[p] ..) instead of the
+// l3 slot.  Those rows are gathered per path; the next path's rows are loaded
+// before the current path is computed, so their latency overlaps its
+// arithmetic.
+template <class Tb>
+struct L2Order {
+    struct O {
+        int p[kMaxPaths];
+    };
+    static constexpr O make()
+    {
+        O o{};
+        int k = 0;
+        for (int l2 = 0; l2 < 4; ++l2)
+            for (int p = 0; p < Tb::P; ++p)
+                if (Tb::data.l2[p] == l2) o.p[k++] = p;
+        return o;
+    }
+    static constexpr O ord = make();
+};
+
+template <class Tb, int p>
+__device__ __forceinline__ void load_mid_rows(float (&g)[7], const float* grow, int32_t Cs, uint32_t chl,
+                                              const Shape& sh)
+{
+    constexpr int d3 = 2 * Tb::data.l3[p] + 1;
+    // a path the plan lacks reads the node's first rows (its weight is 0);
+    // every row index stays inside the node's d_out rows
+    const int32_t r0 = sh.moff[p] >= 0 ? sh.moff[p] : 0;
+#pragma unroll
+    for (int m = 0; m < d3; ++m) {
+        const int32_t r = r0 + m < sh.d_out ? r0 + m : sh.d_out - 1;
+        g[m] = *at_lane(grow + r * Cs, chl);
+    }
+}
+
+template <class Tb, class StoreW, class FlushY>
+__device__ __forceinline__ void bwd_slice_mid(const float (&w)[Tb::P], const float* grow, int32_t Cs, uint32_t chl,
+                                              const Shape& sh, const double (&yv)[Tb::DSH],
+                                              const double (&xv)[Tb::DIN], double (&dxa)[Tb::DIN],
+                                              StoreW&& store_w, FlushY&& flush_y)
+{
+    using Ord = L2Order<Tb>;
+    float gcur[7], gnext[7];
+    load_mid_rows<Tb, Ord::ord.p[0]>(gcur, grow, Cs, chl, sh);
+    double dyb[7];
+    bool dys[7];
+    static_for<0, Tb::P>([&](auto KI) {
+        constexpr int k = decltype(KI)::value;
+        constexpr int p = Ord::ord.p[k];
+        using K = PathK<Tb, p>;
+        constexpr int l2 = K::l2, d2 = 2 * l2 + 1, k2 = l2 * l2;
+        constexpr bool first = k == 0 || Tb::data.l2[Ord::ord.p[k > 0 ? k - 1 : 0]] != l2;
+        constexpr bool last = k + 1 == Tb::P || Tb::data.l2[Ord::ord.p[k + 1 < Tb::P ? k + 1 : k]] != l2;
+        if constexpr (first) {
+#pragma unroll
+            for (int b = 0; b < 7; ++b) {
+                dyb[b] = 0.0;
+                dys[b] = false;
+            }
+        }
+        if constexpr (k + 1 < Tb::P) load_mid_rows<Tb, Ord::ord.p[k + 1 < Tb::P ? k + 1 : k]>(gnext, grow, Cs, chl, sh);
+        const double wd = (double)w[p];
+        double gv[K::d3];
+#pragma unroll
+        for (int m = 0; m < K::d3; ++m) gv[m] = (double)gcur[m];
+        double v[d2];
+        bool vs[d2];
+        static_for<0, d2>([&](auto B) {
+            v[decltype(B)::value] = 0.0;
+            vs[decltype(B)::value] = false;
+        });
+        double dw = 0.0;
+        bool dws = false;
+        static_for<0, K::d1>([&](auto A) {
+            constexpr int a = decltype(A)::value;
+            if constexpr (K::ROW(a)) {
+                double h = 0.0;
+                bool hs = false;
+                static_for<0, d2>([&](auto B) {
+                    constexpr int b = decltype(B)::value;
+                    double r = 0.0;
+                    bool any = false;
+                    static_for<0, K::d3>([&](auto M3) {
+                        constexpr int m3 = decltype(M3)::value;
+                        constexpr double t = K::T(a, b, m3);
+                        if constexpr (t != 0.0) mac(r, t, gv[m3], any);
+                    });
+                    if (any) {
+                        mac(h, r, yv[k2 + b], hs);
+                        mac(v[b], r, xv[K::k1 + a], vs[b]);
+                    }
+                });
+                dxa[K::k1 + a] = __builtin_fma(wd, h, dxa[K::k1 + a]);
+                mac(dw, xv[K::k1 + a], h, dws);
+            }
+        });
+        store_w(std::integral_constant<int, p>{}, dw);
+        static_for<0, d2>([&](auto B) {
+            constexpr int b = decltype(B)::value;
+            if constexpr (K::COL2(b)) mac(dyb[b], wd, v[b], dys[b]);
+        });
+        static_for<0, K::d1>([&](auto A) {
+            if constexpr (K::ROW(decltype(A)::value)) opaque(dxa[K::k1 + decltype(A)::value]);
+        });
+        static_for<0, d2>([&](auto B) {
+            if constexpr (K::COL2(decltype(B)::value)) opaque(dyb[decltype(B)::value]);
+        });
+        if constexpr (last) {
+            double out[d2];
+#pragma unroll
+            for (int b = 0; b < d2; ++b) out[b] = dys[b] ? dyb[b] : 0.0;
+            flush_y(std::integral_constant<int, k2>{}, out);
+        }
+        if constexpr (k + 1 < Tb::P)
+#pragma unroll
+            for (int m = 0; m < 7; ++m) gcur[m] = gnext[m];
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
 // quad_perm DPP move of a double (both halves), CTRL a quad_perm selector
 template <int CTRL>
 __device__ __forceinline__ double dpp_quad(double v)
@@ -870,7 +1170,7 @@ __device__ __forceinline__ double wave_sum_tile(const double* __restrict__ red, 
 // a C > 64 backward block.
 constexpr int kDyChunk = 64;
 
-template <int LM, int LPE, int H, bool SUB, bool DBL = false>
+template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool MID = false>
 __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_occ : Tune<LM, LPE>::bwd_occ))
     k_conv_bwd(BwdArgs a)
 {
@@ -935,7 +1235,7 @@ __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_occ : Tune<LM, 
             if (q >= end) continue;  // uniform over the lanes of one edge
             Edge cur;
             if constexpr (DBL) bwd_load_dbl<Tb, SUB, LPE == 64>(cur, q, chl, a, dm);
-            else bwd_load<Tb, SUB, LPE == 64>(cur, q, chl, a, dm);
+            else bwd_load<Tb, SUB, LPE == 64, !MID>(cur, q, chl, a, dm);
             if constexpr (H == 2)
                 if (ps.h == 0 && lane == 0) eslot[ps.s * K + (t - t0)] = cur.ok ? cur.e : -1;
             if (!cur.ok) continue;
@@ -945,8 +1245,15 @@ __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_occ : Tune<LM, 
             if constexpr (DBL) edge_sh<DSH, LPE>(cur.gy, gyv);
             // the edge's contraction (the backward's, or the double backward's)
             auto slice = [&](auto&& store_w, auto&& flush_y) {
-                if constexpr (DBL) bwd_slice_dbl<Tb>(cur, yv, gyv, xv, gxv, dxa, store_w, flush_y);
-                else bwd_slice<Tb>(cur.w, cur.g, yv, xv, dxa, store_w, flush_y);
+                if constexpr (DBL) {
+                    bwd_slice_dbl<Tb>(cur, yv, gyv, xv, gxv, dxa, store_w, flush_y);
+                } else if constexpr (MID) {
+                    const int32_t Cg = edge_stride(C);
+                    bwd_slice_mid<Tb>(cur.w, a.G + (int64_t)cur.i * (dm.d_out * Cg), Cg, lane_offset(chl), a.sh, yv,
+                                      xv, dxa, store_w, flush_y);
+                } else {
+                    bwd_slice<Tb>(cur.w, cur.g, yv, xv, dxa, store_w, flush_y);
+                }
             };
             const int32_t Ce = edge_stride(C);
             float* dwrow = a.dW + (int64_t)cur.e * (dm.P * Ce);
@@ -1042,11 +1349,12 @@ __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_occ : Tune<LM, 
     }
 }
 
-template <int LM, int LPE, int H, bool SUB, bool DBL = false>
+template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool MID = false>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s)
 {
     if (a.sh.N == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_conv_bwd<LM, LPE, H, SUB, DBL>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_conv_bwd<LM, LPE, H, SUB, DBL, MID>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0, s,
+                       a);
     return hipGetLastError();
 }
 
@@ -1059,7 +1367,9 @@ constexpr KernelSet make_set()
                      {&launch_fwd<LM, LPE, H, false>, &launch_fwd<LM, LPE, H, true>},
                      {&launch_bwd<LM, LPE, H, false>, &launch_bwd<LM, LPE, H, true>},
                      &launch_fwd<LM, LPE, H, true, true>,
-                     &launch_bwd<LM, LPE, H, true, true>};
+                     &launch_bwd<LM, LPE, H, true, true>,
+                     &launch_fwd_mid<LM, LPE, H>,
+                     &launch_bwd<LM, LPE, H, true, false, true>};
 }
 
 template <int LM>

@@ -39,11 +39,14 @@ class Plan:
     """Compiled CGTP convolution for degrees (l_in, l_sh, l_out) and C channels."""
 
     def __init__(self, l_in: int, l_sh: int, l_out: int, channels: int, validate: bool = False,
-                 locality: bool = False, shared_weights: bool = False):
+                 locality: bool = False, shared_weights: bool = False, path_outputs: bool = False):
+        """path_outputs: every path keeps its own 2*l3+1 output rows (out and
+        grad_out are [N][dim_out][C] with dim_out = sum over paths of 2*l3+1)."""
         lib = L.lib()
         h = ctypes.c_void_p()
         flags = (L.CGTP_FLAG_VALIDATE if validate else 0) | (L.CGTP_FLAG_LOCALITY if locality else 0) | \
-            (L.CGTP_FLAG_SHARED_WEIGHTS if shared_weights else 0)
+            (L.CGTP_FLAG_SHARED_WEIGHTS if shared_weights else 0) | (L.CGTP_FLAG_PATH_OUTPUTS if path_outputs else 0)
+        self.path_outputs = path_outputs
         self.shared_weights = shared_weights
         L.check("cgtp_plan_create", lib.cgtp_plan_create(ctypes.byref(h), l_in, l_sh, l_out, channels, flags))
         self._h = h
@@ -53,6 +56,7 @@ class Plan:
                                                       ctypes.byref(ds), ctypes.byref(do)))
         self.num_paths = P.value
         self.dim_in, self.dim_sh, self.dim_out = di.value, ds.value, do.value
+        self.dim_z = (l_out + 1) ** 2   # the coupled output's width (the CP product's d3)
         arr = (ctypes.c_int * (3 * self.num_paths))()
         L.check("cgtp_plan_info", lib.cgtp_plan_info(h, None, arr, None, None, None))
         self.paths = [tuple(arr[3 * q:3 * q + 3]) for q in range(self.num_paths)]
@@ -228,7 +232,7 @@ class Plan:
         computation.  Returns (A, B, C, relative Frobenius error)."""
         R = A0.shape[1]
         A, B, C = (np.ascontiguousarray(v, dtype=np.float64).copy() for v in (A0, B0, C0))
-        if A.shape != (self.dim_out, R) or B.shape != (self.dim_in, R) or C.shape != (self.dim_sh, R):
+        if A.shape != (self.dim_z, R) or B.shape != (self.dim_in, R) or C.shape != (self.dim_sh, R):
             raise ValueError("factor shapes must be [d_out][R], [d_in][R], [d_sh][R]")
         err = ctypes.c_double()
         dp = lambda a: ctypes.c_void_p(a.ctypes.data)
@@ -243,7 +247,7 @@ class Plan:
         _need(x, "x", torch.float32, (N, self.dim_in, Ch), dev)
         _need(Y, "Y", torch.float32, (E, self.dim_sh), dev)
         _need(W, "W", torch.float32, (E, Ch), dev)
-        _need(A, "A", torch.float32, (self.dim_out, R), dev)
+        _need(A, "A", torch.float32, (self.dim_z, R), dev)
         _need(B, "B", torch.float32, (self.dim_in, R), dev)
         _need(C, "C", torch.float32, (self.dim_sh, R), dev)
         if ws is None:
@@ -257,8 +261,8 @@ class Plan:
         B [D_in][R], C [D_sh][R] (fp32, on the device)."""
         N, E, Ch, dev, R, ws = self._cp_common(row_ptr, src, x, Y, W, A, B, C, ws)
         if out is None:
-            out = torch.empty((N, self.dim_out, Ch), dtype=torch.float32, device=dev)
-        _need(out, "out", torch.float32, (N, self.dim_out, Ch), dev)
+            out = torch.empty((N, self.dim_z, Ch), dtype=torch.float32, device=dev)
+        _need(out, "out", torch.float32, (N, self.dim_z, Ch), dev)
         L.check("cgtp_cp_conv_fwd", L.lib().cgtp_cp_conv_fwd(
             self._h, R, N, E, _ptr(row_ptr), _ptr(src), _ptr(x), _ptr(Y), _ptr(W), _ptr(A), _ptr(B), _ptr(C),
             _ptr(out), _ptr(ws), ws.numel(), _stream(dev)))
@@ -268,7 +272,7 @@ class Plan:
         """(grad_x [N][D_in][C], grad_W [E][C], grad_Y [E][D_sh]) of the CP
         convolution; a gradient not in ``want`` comes back as None."""
         N, E, Ch, dev, R, ws = self._cp_common(row_ptr, src, x, Y, W, A, B, C, ws)
-        _need(grad_out, "grad_out", torch.float32, (N, self.dim_out, Ch), dev)
+        _need(grad_out, "grad_out", torch.float32, (N, self.dim_z, Ch), dev)
         new = lambda shape, key: torch.empty(shape, dtype=torch.float32, device=dev) if key in want else None
         dx, dW, dY = new((N, self.dim_in, Ch), "dx"), new((E, Ch), "dW"), new((E, self.dim_sh), "dY")
         L.check("cgtp_cp_conv_bwd", L.lib().cgtp_cp_conv_bwd(

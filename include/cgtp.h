@@ -87,6 +87,18 @@ typedef enum {
  * [E][C], one weight per edge and channel used by every path, and
  * grad_W[e][u] = sum over the paths of dL/dW[e][p][u]. */
 #define CGTP_FLAG_SHARED_WEIGHTS 4u
+/* Per-path (concatenated) outputs: every path keeps its own 2*l3+1 output
+ * rows instead of adding into the l3 slot ("irreps_mid").  out and grad_out
+ * are [N][D_mid][C] with D_mid = sum over the paths of (2*l3+1); path p owns
+ * rows o_p .. o_p + 2*l3_p with o_p = sum over earlier paths of (2*l3+1), in
+ * the path order of cgtp_plan_info (which reports D_mid as dim_out).  The
+ * summed output is the sum of these blocks over the paths of each l3.  The
+ * per-path blocks are what a fully connected ("uvw") product mixes over
+ * channels per path (TDN rebuttal to cmnz: the fully connected CG tensor
+ * product as the cost-dominating kernel).  Combines with
+ * CGTP_FLAG_SHARED_WEIGHTS; cgtp_conv_bwd_bwd returns CGTP_ERR_UNSUPPORTED
+ * for such plans. */
+#define CGTP_FLAG_PATH_OUTPUTS 8u
 
 /* Create a plan for degrees (l_in, l_sh, l_out) and C channels: the path list
  * under the selection rules (TDN rebuttal to S6y1, first answer) and the real
@@ -105,7 +117,7 @@ cgtp_status_t cgtp_plan_destroy(cgtp_plan_t plan);
 /* Path count and dimensions of a plan (TDN rebuttal to S6y1, first answer:
  * which (l1, l2, l3) couple).  paths_l1l2l3, if not NULL, receives [P][3]
  * (l1, l2, l3) in the order the weights use.  Any output pointer may be NULL.
- * dim_* = (l+1)^2 of each degree. */
+ * dim_* = (l+1)^2 of each degree (dim_out = D_mid with CGTP_FLAG_PATH_OUTPUTS). */
 cgtp_status_t cgtp_plan_info(cgtp_plan_t plan, int* num_paths, int* paths_l1l2l3, int* dim_in,
                              int* dim_sh, int* dim_out);
 
