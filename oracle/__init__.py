@@ -217,6 +217,38 @@ def conv_bwd_mid(l_in, l_sh, l_out, row_ptr, src, x, Y, W, G, want=("dx", "dW", 
     return dx, dW, dY
 
 
+def path_mix_fwd(l_in, l_sh, l_out, mid, Wmix):
+    """Fully connected ("uvw") mixing of the per-path outputs: path p's block
+    of 2*l3+1 rows is multiplied by its channel matrix Wmix[p] [C][C_out] and
+    the paths of each l3 are summed (TDN rebuttal to cmnz: the fully connected
+    CG tensor product).  mid [N][D_mid][C] -> out [N][(l_out+1)^2][C_out]."""
+    mid, Wmix = _f64(mid), _f64(Wmix)
+    N = mid.shape[0]
+    out = np.zeros((N, (l_out + 1) ** 2, Wmix.shape[2]))
+    o = 0
+    for p, (l1, l2, l3) in enumerate(paths(l_in, l_sh, l_out)):
+        d = 2 * l3 + 1
+        for m in range(d):
+            out[:, l3 * l3 + m, :] += mid[:, o + m, :] @ Wmix[p]
+        o += d
+    return out
+
+
+def path_mix_bwd(l_in, l_sh, l_out, mid, Wmix, G):
+    """(d_mid, d_Wmix) of <G, path_mix_fwd(mid, Wmix)>."""
+    mid, Wmix, G = _f64(mid), _f64(Wmix), _f64(G)
+    d_mid = np.zeros_like(mid)
+    d_W = np.zeros_like(Wmix)
+    o = 0
+    for p, (l1, l2, l3) in enumerate(paths(l_in, l_sh, l_out)):
+        d = 2 * l3 + 1
+        for m in range(d):
+            d_mid[:, o + m, :] = G[:, l3 * l3 + m, :] @ Wmix[p].T
+            d_W[p] += mid[:, o + m, :].T @ G[:, l3 * l3 + m, :]
+        o += d
+    return d_mid, d_W
+
+
 def conv_bwd_bwd(l_in, l_sh, l_out, row_ptr, src, x, Y, W, G, ggx=None, ggY=None, ggW=None,
                  want=("dx", "dY", "dW", "dG")):
     """Gradients (dx, dY, dW, dG) of S = <ggx, dx> + <ggW, dW> + <ggY, dY>

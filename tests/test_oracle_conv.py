@@ -413,3 +413,43 @@ def test_per_path_backward_finite_differences_and_replicated_grad(oracle, Ls):
     for u, v in zip(oracle.conv_bwd_mid(*Ls, g.row_ptr, g.src, a["x"], a["Y"], a["W"], Grep),
                     oracle.conv_bwd(*Ls, g.row_ptr, g.src, a["x"], a["Y"], a["W"], Gs)):
         np.testing.assert_allclose(u, v, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("Ls", [(1, 1, 1), (2, 2, 2), (2, 1, 3)])
+def test_path_mixing_reduces_to_the_pinned_convolutions(oracle, Ls):
+    """The uvw mixing of the per-path outputs: with every Wmix[p] the identity
+    it gives the summed convolution; with Wmix[p] = diag(s_p) the convolution
+    whose weights are scaled by s_p per path and channel."""
+    from clebsch_gordan_tensor_cgtp_amd.synth import random_graph
+    rng = np.random.default_rng(sum(Ls) + 60)
+    N, C = 9, 4
+    g = random_graph(N, rng.integers(0, 5, size=N), seed=5)
+    P = oracle.paths(*Ls).shape[0]
+    x = rng.normal(size=(N, (Ls[0] + 1) ** 2, C))
+    Y = rng.normal(size=(g.n_edges, (Ls[1] + 1) ** 2))
+    W = rng.normal(size=(g.n_edges, P, C))
+    mid = oracle.conv_fwd_mid(*Ls, g.row_ptr, g.src, x, Y, W)
+    eye = np.repeat(np.eye(C)[None], P, axis=0)
+    np.testing.assert_allclose(oracle.path_mix_fwd(*Ls, mid, eye), oracle.conv_fwd(*Ls, g.row_ptr, g.src, x, Y, W),
+                               rtol=1e-12, atol=1e-12)
+    sc = rng.normal(size=(P, C))
+    diag = np.stack([np.diag(v) for v in sc])
+    np.testing.assert_allclose(oracle.path_mix_fwd(*Ls, mid, diag),
+                               oracle.conv_fwd(*Ls, g.row_ptr, g.src, x, Y, W * sc[None]), rtol=1e-12, atol=1e-12)
+
+
+def test_path_mixing_backward_finite_differences(oracle):
+    Ls = (2, 1, 2)
+    rng = np.random.default_rng(61)
+    N, C, Co = 7, 3, 5
+    D = oracle.mid_rows(*Ls)
+    P = oracle.paths(*Ls).shape[0]
+    mid, Wm = rng.normal(size=(N, D, C)), rng.normal(size=(P, C, Co))
+    G = rng.normal(size=(N, (Ls[2] + 1) ** 2, Co))
+    dmid, dW = oracle.path_mix_bwd(*Ls, mid, Wm, G)
+    L = lambda m, w: (G * oracle.path_mix_fwd(*Ls, m, w)).sum()
+    for name, base, got in (("mid", mid, dmid), ("Wmix", Wm, dW)):
+        d = rng.normal(size=base.shape)
+        args_p = (mid + 1e-3 * d, Wm) if name == "mid" else (mid, Wm + 1e-3 * d)
+        args_m = (mid - 1e-3 * d, Wm) if name == "mid" else (mid, Wm - 1e-3 * d)
+        assert (L(*args_p) - L(*args_m)) / 2e-3 == pytest.approx((got * d).sum(), rel=1e-9, abs=1e-9), name
