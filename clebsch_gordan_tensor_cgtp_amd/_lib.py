@@ -48,6 +48,9 @@ SIGNATURES = {
     "cgtp_conv_bwd": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, ctypes.c_size_t, _vp]),
     "cgtp_conv_bwd_bwd": (ctypes.c_int, [_vp, _c_i64, _c_i64] + [_vp] * 14 + [ctypes.c_size_t, _vp]),
+    "cgtp_path_mix_workspace_size": (ctypes.c_int, [_vp, _c_i64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
+    "cgtp_path_mix_fwd": (ctypes.c_int, [_vp, _c_i64, ctypes.c_int, _vp, _vp, _vp, _vp]),
+    "cgtp_path_mix_bwd": (ctypes.c_int, [_vp, _c_i64, ctypes.c_int] + [_vp] * 6 + [ctypes.c_size_t, _vp]),
     "cgtp_cp_workspace_size": (ctypes.c_int, [_vp, ctypes.c_int, _c_i64, _c_i64, ctypes.POINTER(ctypes.c_size_t)]),
     "cgtp_cp_fit": (ctypes.c_int, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_double] + [_vp] * 4),
     "cgtp_cp_conv_fwd": (ctypes.c_int, [_vp, ctypes.c_int, _c_i64, _c_i64] + [_vp] * 10 + [ctypes.c_size_t, _vp]),

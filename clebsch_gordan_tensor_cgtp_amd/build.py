@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 # so the slowest compiles run in parallel (longest first)
 SOURCES = ["cgtp_kernels_l3_c128.hip", "cgtp_kernels_l3_c64.hip", "cgtp_kernels_l3_c32.hip",
            "cgtp_kernels_l3_c16.hip", "cgtp_kernels_l3_c8.hip", "cgtp_kernels_l2_wide.hip", "cgtp_kernels_l2.hip",
-           "cgtp_kernels_l1.hip", "cgtp_cp.hip", "cgtp_registry.hip", "cgtp_graph.hip", "cgtp_forces.hip",
+           "cgtp_kernels_l1.hip", "cgtp_cp.hip", "cgtp_mix.hip", "cgtp_registry.hip", "cgtp_graph.hip", "cgtp_forces.hip",
            "cgtp_cp_fit.cpp", "cgtp_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -17,6 +17,7 @@
 #include "cgtp_cp.h"
 #include "cgtp_internal.h"
 #include "cgtp_math.h"
+#include "cgtp_mix.h"
 
 struct cgtp_plan_s {
     int l_in, l_sh, l_out, channels;
@@ -448,6 +449,72 @@ cgtp_status_t cgtp_conv_bwd_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edg
         st = hip_status(plan->ks->bwd_dbl(a, stream));
     }
     return st;
+}
+
+// ---- fully connected mixing of the per-path outputs ----------------------------
+namespace {
+
+constexpr int kMaxMixOut = 1024;
+
+cgtp::MixShape mix_shape(const cgtp_plan_s* plan, int64_t n_nodes, int c_out)
+{
+    cgtp::MixShape m{};
+    m.N = (int32_t)n_nodes;
+    m.C = plan->channels;
+    m.Co = c_out;
+    m.P = plan->P;
+    m.Dmid = plan->d_mid;
+    m.Dout = plan->d_out;
+    int o = 0;
+    for (int p = 0; p < plan->P; ++p) {
+        m.l3[p] = plan->paths[3 * p + 2];
+        m.o[p] = o;
+        o += 2 * m.l3[p] + 1;
+    }
+    return m;
+}
+
+}  // namespace
+
+cgtp_status_t cgtp_path_mix_workspace_size(cgtp_plan_t plan, int64_t n_nodes, int c_out, size_t* bytes)
+{
+    if (!plan || !bytes || n_nodes < 0 || c_out < 1) return CGTP_ERR_INVALID_ARG;
+    if (c_out > kMaxMixOut) return CGTP_ERR_UNSUPPORTED;
+    *bytes = cgtp::mix_workspace_bytes(n_nodes, plan->P, plan->channels, c_out);
+    return CGTP_OK;
+}
+
+cgtp_status_t cgtp_path_mix_fwd(cgtp_plan_t plan, int64_t n_nodes, int c_out, const float* mid, const float* Wmix,
+                                float* out, hipStream_t stream)
+{
+    if (!plan || n_nodes < 0 || n_nodes >= (int64_t)INT32_MAX || c_out < 1) return CGTP_ERR_INVALID_ARG;
+    if (c_out > kMaxMixOut) return CGTP_ERR_UNSUPPORTED;
+    if (!Wmix || !aligned16(Wmix)) return CGTP_ERR_INVALID_ARG;
+    if (n_nodes == 0) return CGTP_OK;
+    if (!mid || !out || !aligned16(mid) || !aligned16(out)) return CGTP_ERR_INVALID_ARG;
+    return hip_status(cgtp::launch_mix_fwd(mix_shape(plan, n_nodes, c_out), mid, Wmix, out, stream));
+}
+
+cgtp_status_t cgtp_path_mix_bwd(cgtp_plan_t plan, int64_t n_nodes, int c_out, const float* mid, const float* Wmix,
+                                const float* grad_out, float* grad_mid, float* grad_Wmix, void* ws, size_t ws_bytes,
+                                hipStream_t stream)
+{
+    if (!plan || n_nodes < 0 || n_nodes >= (int64_t)INT32_MAX || c_out < 1) return CGTP_ERR_INVALID_ARG;
+    if (c_out > kMaxMixOut) return CGTP_ERR_UNSUPPORTED;
+    if (!grad_mid && !grad_Wmix) return CGTP_OK;
+    if (!Wmix || !aligned16(Wmix)) return CGTP_ERR_INVALID_ARG;
+    if (grad_Wmix) {
+        if (!aligned16(grad_Wmix)) return CGTP_ERR_INVALID_ARG;
+        if (!ws || ws_bytes < cgtp::mix_workspace_bytes(n_nodes, plan->P, plan->channels, c_out))
+            return CGTP_ERR_WORKSPACE;
+        if (((uintptr_t)ws & 255u) != 0) return CGTP_ERR_INVALID_ARG;
+    }
+    if (n_nodes > 0) {
+        if (!mid || !grad_out || !aligned16(mid) || !aligned16(grad_out)) return CGTP_ERR_INVALID_ARG;
+        if (grad_mid && !aligned16(grad_mid)) return CGTP_ERR_INVALID_ARG;
+    }
+    return hip_status(cgtp::launch_mix_bwd(mix_shape(plan, n_nodes, c_out), mid, Wmix, grad_out, grad_mid,
+                                           grad_Wmix, (double*)ws, stream));
 }
 
 // ---- CP-decomposed tensor product ------------------------------------------

@@ -219,6 +219,42 @@ class Plan:
             _stream(dev)))
         return dd_x, dd_Y, dd_W, dd_out
 
+    # -- fully connected ("uvw") mixing of the per-path outputs ----------------
+    @property
+    def mid_rows(self) -> int:
+        """Rows of the per-path outputs: sum over the paths of 2*l3+1."""
+        return sum(2 * l3 + 1 for (_, _, l3) in self.paths)
+
+    def path_mix_fwd(self, mid, Wmix, out=None) -> torch.Tensor:
+        """out[N][(l_out+1)^2][C_out] = per path, mid's block times Wmix[p]
+        [C][C_out], summed over the paths of each l3."""
+        N, C, dev = mid.shape[0], self.channels, mid.device
+        Co = Wmix.shape[2]
+        _need(mid, "mid", torch.float32, (N, self.mid_rows, C))
+        _need(Wmix, "Wmix", torch.float32, (self.num_paths, C, Co), dev)
+        if out is None:
+            out = torch.empty((N, self.dim_z, Co), dtype=torch.float32, device=dev)
+        _need(out, "out", torch.float32, (N, self.dim_z, Co), dev)
+        L.check("cgtp_path_mix_fwd", L.lib().cgtp_path_mix_fwd(self._h, N, Co, _ptr(mid), _ptr(Wmix), _ptr(out),
+                                                               _stream(dev)))
+        return out
+
+    def path_mix_bwd(self, mid, Wmix, grad_out, want=("mid", "Wmix")):
+        """(grad_mid, grad_Wmix) of <grad_out, path_mix_fwd(mid, Wmix)>."""
+        N, C, dev = mid.shape[0], self.channels, mid.device
+        Co = Wmix.shape[2]
+        _need(mid, "mid", torch.float32, (N, self.mid_rows, C))
+        _need(Wmix, "Wmix", torch.float32, (self.num_paths, C, Co), dev)
+        _need(grad_out, "grad_out", torch.float32, (N, self.dim_z, Co), dev)
+        gm = torch.empty_like(mid) if "mid" in want else None
+        gw = torch.empty_like(Wmix) if "Wmix" in want else None
+        b = ctypes.c_size_t()
+        L.check("cgtp_path_mix_workspace_size", L.lib().cgtp_path_mix_workspace_size(self._h, N, Co, ctypes.byref(b)))
+        ws = torch.empty(max(1, b.value), dtype=torch.uint8, device=dev)
+        L.check("cgtp_path_mix_bwd", L.lib().cgtp_path_mix_bwd(self._h, N, Co, _ptr(mid), _ptr(Wmix), _ptr(grad_out),
+                                                               _ptr(gm), _ptr(gw), _ptr(ws), ws.numel(), _stream(dev)))
+        return gm, gw
+
     # -- CP-decomposed tensor product -------------------------------------------
     def cp_workspace_size(self, rank: int, n_nodes: int, n_edges: int) -> int:
         b = ctypes.c_size_t()

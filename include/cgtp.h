@@ -221,6 +221,35 @@ cgtp_status_t cgtp_conv_bwd_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edg
                                 float* dd_x, float* dd_Y, float* dd_W, float* dd_out, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* ---- fully connected ("uvw") mixing ----------------------------------------
+ * The fully connected CG tensor product ("Tensor Decomposition Networks ...",
+ * rebuttal to cmnz: the cost-dominating kernel) couples every input channel
+ * with every output channel per path.  With its weights shared over the edges
+ * it is the per-path-output convolution (CGTP_FLAG_PATH_OUTPUTS) followed by
+ * one dense channel matrix per path, summed over the paths of each l3:
+ *   out[i][k(l3,m)][w] = sum_{p: l3_p = l3} sum_u mid[i][o_p + m][u] Wmix[p][u][w]
+ * mid [N][D_mid][C] (the per-path outputs, layout of CGTP_FLAG_PATH_OUTPUTS,
+ * C the plan's channels), Wmix [P][C][c_out], out [N][(l_out+1)^2][c_out];
+ * 1 <= c_out <= 1024.  Runs on the fp64 matrix cores; any plan of the degree
+ * set may be used (only its path list and C matter). */
+
+/* Workspace bytes of cgtp_path_mix_bwd (the weight gradient's per-block
+ * partial sums). */
+cgtp_status_t cgtp_path_mix_workspace_size(cgtp_plan_t plan, int64_t n_nodes, int c_out, size_t* bytes);
+
+/* out = the mixing above (overwritten). */
+cgtp_status_t cgtp_path_mix_fwd(cgtp_plan_t plan, int64_t n_nodes, int c_out, const float* mid, const float* Wmix,
+                                float* out, hipStream_t stream);
+
+/* Backward of L = <grad_out, out>:
+ *   grad_mid[i][o_p + m][u] = sum_w grad_out[i][k(l3_p,m)][w] Wmix[p][u][w]
+ *   grad_Wmix[p][u][w]      = sum_i sum_m mid[i][o_p + m][u] grad_out[i][k(l3_p,m)][w]
+ * Either output may be NULL.  The weight gradient sums over the nodes in a
+ * fixed order (node ranges per block, partials in ws, added in order). */
+cgtp_status_t cgtp_path_mix_bwd(cgtp_plan_t plan, int64_t n_nodes, int c_out, const float* mid, const float* Wmix,
+                                const float* grad_out, float* grad_mid, float* grad_Wmix, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
 /* ---- CP-decomposed tensor product ----------------------------------------
  * The approximate product of "Tensor Decomposition Networks for Accelerating
  * Machine Learning Force Field Computations" (authors' rebuttal to S6y1,

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 18
+    assert len(names) == 21
     for n in names:
         assert hasattr(L.lib(), n), n
         assert n in L.SIGNATURES, n
@@ -188,3 +188,21 @@ def test_path_outputs_plan_reports_the_per_path_width(L):
         rows = sum(2 * l3 + 1 for (_, _, l3) in plan.paths)
         assert plan.dim_out == rows and (want is None or rows == want)
         assert plan.dim_z == (c + 1) ** 2
+
+
+def test_path_mix_arguments_without_a_gpu(L):
+    from clebsch_gordan_tensor_cgtp_amd.ops import Plan
+    plan = Plan(2, 2, 2, 64)
+    lib = L.lib()
+    fake, odd, ws = ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 8), ctypes.c_void_p(1 << 20)
+    b = ctypes.c_size_t()
+    assert lib.cgtp_path_mix_workspace_size(plan._h, 1000, 0, ctypes.byref(b)) == L.CGTP_ERR_INVALID_ARG
+    assert lib.cgtp_path_mix_workspace_size(plan._h, 1000, 1025, ctypes.byref(b)) == L.CGTP_ERR_UNSUPPORTED
+    assert lib.cgtp_path_mix_workspace_size(plan._h, 1000, 128, ctypes.byref(b)) == L.CGTP_OK
+    assert b.value == 8 * 2 * 15 * 64 * 128          # 2 node-range splits of fp64 partials
+    assert lib.cgtp_path_mix_fwd(None, 10, 8, fake, fake, fake, None) == L.CGTP_ERR_INVALID_ARG
+    assert lib.cgtp_path_mix_fwd(plan._h, 10, 8, odd, fake, fake, None) == L.CGTP_ERR_INVALID_ARG
+    assert lib.cgtp_path_mix_fwd(plan._h, 10, 2000, fake, fake, fake, None) == L.CGTP_ERR_UNSUPPORTED
+    assert lib.cgtp_path_mix_bwd(plan._h, 10, 8, fake, fake, fake, None, None, None, 0, None) == L.CGTP_OK
+    assert lib.cgtp_path_mix_bwd(plan._h, 10, 8, fake, fake, fake, None, fake, ws, 16, None) == L.CGTP_ERR_WORKSPACE
+    assert lib.cgtp_path_mix_bwd(plan._h, 10, 8, fake, fake, None, fake, None, None, 0, None) == L.CGTP_ERR_INVALID_ARG
