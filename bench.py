@@ -217,6 +217,7 @@ def run_workload(torch, dev, key, steps, warmup, settle, locality=False, extras=
         res["double_backward"] = time_double_backward(torch, plan, stream, rp, src, x, Y, W, G, ws, ab, steps)
         res["cp"] = time_cp(torch, plan, stream, rp, src, x, Y, G, (16, 32, 64) if key == HEADLINE else (32,),
                             steps)
+        res["path_outputs"] = time_path_outputs(torch, stream, rp, src, x, Y, W, steps)
     host = None
     if key == HEADLINE:
         host = (w, g, x.cpu().numpy(), W.cpu().numpy(), G.cpu().numpy())
@@ -280,6 +281,57 @@ def time_double_backward(torch, plan, stream, rp, src, x, Y, W, G, ws, ab, steps
     del gx, gY, gW
     log(f"  double backward: dd_out {res['dd_out']['ms']:.3f} ms ({res['dd_out']['alg_gbs']:.0f} GB/s alg) | "
         f"dd_x,dd_Y,dd_W {res['dd_x_Y_W']['ms']:.3f} ms ({res['dd_x_Y_W']['alg_gbs']:.0f} GB/s alg)")
+    return res
+
+
+def _median_ms(torch, stream, fn, steps):
+    for _ in range(3):
+        fn()
+    ts = []
+    for _ in range(max(5, steps)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    return statistics.median(a.elapsed_time(b) for a, b in ts)
+
+
+def time_path_outputs(torch, stream, rp, src, x, Y, W, steps):
+    """The per-path (concatenated) outputs and their fully connected (uvw)
+    mixing with C_out = C: median times of the convolution forward and
+    backward (all launches of each call) and of the mixing forward and
+    backward, HIP events on their stream.  Algorithmic bytes as for the
+    summed convolution with D_mid output rows; the mixing is reported as fp64
+    matrix-core TFLOP/s (2 N D_mid C C_out flops forward, twice that backward)."""
+    from clebsch_gordan_tensor_cgtp_amd.ops import Plan
+
+    N, E, C = x.shape[0], Y.shape[0], x.shape[2]
+    L = int(round(math.sqrt(Y.shape[1]))) - 1
+    plan = Plan(L, L, L, C, path_outputs=True)
+    P, Dm = plan.num_paths, plan.dim_out
+    ws = plan.graph_prepare(rp, src)
+    G = torch.randn((N, Dm, C), device=x.device)
+    Wm = torch.randn((P, C, C), device=x.device) / math.sqrt(C)
+    mid = torch.empty((N, Dm, C), device=x.device)
+    res = {"d_mid": Dm}
+    res["fwd_ms"] = _median_ms(torch, stream, lambda: plan.conv_fwd(rp, src, x, Y, W, ws, out=mid), steps)
+    res["bwd_ms"] = _median_ms(torch, stream, lambda: plan.conv_bwd(rp, src, x, Y, W, G, ws), steps)
+    fwd_b = E * (4 * P * C + 4 * plan.dim_sh + 4) + N * (4 * C * (plan.dim_in + Dm) + 4)
+    bwd_b = E * (8 * P * C + 8 * plan.dim_sh + 8) + N * (4 * C * (2 * plan.dim_in + Dm) + 4)
+    res["fwd_alg_gbs"] = fwd_b / (res["fwd_ms"] * 1e-3) / 1e9
+    res["bwd_alg_gbs"] = bwd_b / (res["bwd_ms"] * 1e-3) / 1e9
+    Gz = torch.randn((N, plan.dim_z, C), device=x.device)
+    res["mix_fwd_ms"] = _median_ms(torch, stream, lambda: plan.path_mix_fwd(mid, Wm), steps)
+    res["mix_bwd_ms"] = _median_ms(torch, stream, lambda: plan.path_mix_bwd(mid, Wm, Gz), steps)
+    fl = 2.0 * N * Dm * C * C
+    res["mix_fwd_tflops"] = fl / (res["mix_fwd_ms"] * 1e-3) / 1e12
+    res["mix_bwd_tflops"] = 2 * fl / (res["mix_bwd_ms"] * 1e-3) / 1e12
+    log(f"  per-path outputs (D_mid {Dm}): fwd {res['fwd_ms']:.3f} ms | bwd {res['bwd_ms']:.3f} ms | uvw mixing fwd "
+        f"{res['mix_fwd_ms']:.3f} ms ({res['mix_fwd_tflops']:.1f} TFLOP/s) bwd {res['mix_bwd_ms']:.3f} ms "
+        f"({res['mix_bwd_tflops']:.1f} TFLOP/s)")
+    del ws, G, Wm, mid, Gz
     return res
 
 

@@ -20,7 +20,7 @@ struct MixShape {
 };
 
 // node-range splits of the weight gradient, and its workspace
-int32_t mix_splits(int64_t N);
+int32_t mix_splits(int64_t N, int32_t P, int32_t C, int32_t Co);
 size_t mix_workspace_bytes(int64_t N, int32_t P, int32_t C, int32_t Co);
 
 // out [N][Dout][Co] from mid [N][Dmid][C] and Wmix [P][C][Co]

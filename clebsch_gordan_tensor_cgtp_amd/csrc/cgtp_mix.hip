@@ -180,11 +180,23 @@ inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b);
 
 }  // namespace
 
-int32_t mix_splits(int64_t N) { return (int32_t)(N <= 512 ? 1 : (N / 512 < 64 ? (N + 511) / 512 : 64)); }
+// Node-range splits of the weight gradient: enough blocks to fill the chip
+// (about 4096 with the tiles of every path) and at most 512 nodes per split,
+// but at least 16 nodes per split and at most 256 splits.
+int32_t mix_splits(int64_t N, int32_t P, int32_t C, int32_t Co)
+{
+    const int64_t tiles = (int64_t)P * ((C + 63) / 64) * ((Co + 63) / 64);
+    int64_t n = (4096 + tiles - 1) / (tiles > 0 ? tiles : 1);
+    if (n < (N + 511) / 512) n = (N + 511) / 512;
+    const int64_t by_nodes = (N + 15) / 16;
+    if (n > by_nodes) n = by_nodes;
+    if (n > 256) n = 256;
+    return (int32_t)(n < 1 ? 1 : n);
+}
 
 size_t mix_workspace_bytes(int64_t N, int32_t P, int32_t C, int32_t Co)
 {
-    return sizeof(double) * (size_t)mix_splits(N) * (size_t)P * (size_t)C * (size_t)Co;
+    return sizeof(double) * (size_t)mix_splits(N, P, C, Co) * (size_t)P * (size_t)C * (size_t)Co;
 }
 
 hipError_t launch_mix_fwd(const MixShape& m, const float* mid, const float* Wmix, float* out, hipStream_t s)
@@ -214,7 +226,7 @@ hipError_t launch_mix_bwd(const MixShape& m, const float* mid, const float* Wmix
         if (e != hipSuccess) return e;
     }
     if (dW) {
-        const int32_t nsplit = mix_splits(m.N);
+        const int32_t nsplit = mix_splits(m.N, m.P, m.C, m.Co);
         const int32_t chunk = (int32_t)((m.N + nsplit - 1) / nsplit);
         hipLaunchKernelGGL(k_mix_bwd_weight, dim3(cdiv(m.C, kRows * kWaves), cdiv(m.Co, kCols), (unsigned)(m.P * nsplit)),
                            dim3(256), 0, s, m, nsplit, chunk > 0 ? chunk : 1, mid, G, part);

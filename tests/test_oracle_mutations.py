@@ -35,9 +35,12 @@ MUTATIONS = [
     ("forward: m1 index flipped",
      "double xv = x[(j * Din + l1 * l1 + l1 + m1) * C + u];\n                                double yv = Y[e * Dsh + l2 * l2 + l2 + m2];\n                                o[",
      "double xv = x[(j * Din + l1 * l1 + l1 - m1) * C + u];\n                                double yv = Y[e * Dsh + l2 * l2 + l2 + m2];\n                                o["),
-    ("backward: weight dropped in grad_Y", "if (dY) dY[e * Dsh + l2 * l2 + l2 + m2] += w * c * xv * gv;",
-     "if (dY) dY[e * Dsh + l2 * l2 + l2 + m2] += c * xv * gv;"),
-    ("backward: grad_W without grad_out", "acc += c * xv * yv * gv;", "acc += c * xv * yv;"),
+    ("backward: weight dropped in grad_Y",
+     "acc += c * xv * yv * gv;\n                                if (dY) dY[e * Dsh + l2 * l2 + l2 + m2] += w * c * xv * gv;",
+     "acc += c * xv * yv * gv;\n                                if (dY) dY[e * Dsh + l2 * l2 + l2 + m2] += c * xv * gv;"),
+    ("backward: grad_W without grad_out",
+     "acc += c * xv * yv * gv;\n                                if (dY) dY",
+     "acc += c * xv * yv;\n                                if (dY) dY"),
     ("backward: grad_x scattered to the receiver", "mine[(j * Din + l1 * l1 + l1 + m1) * C + u] += w * c * yv * gv;",
      "mine[(i * Din + l1 * l1 + l1 + m1) * C + u] += w * c * yv * gv;"),
     ("transpose: receivers walked backwards",
@@ -61,6 +64,9 @@ MUTATIONS = [
     ("CP backward: B^T x used in g_x", "for (int r = 0; r < R; ++r) v += B[a * R + r] * ga[r] * t[r];",
      "for (int r = 0; r < R; ++r) v += B[a * R + r] * ga[r] * s[r];"),
     ("CP backward: edge weight dropped in g_y", "dY[e * d2 + b] += w * v;", "dY[e * d2 + b] += v;"),
+    ("per-path outputs: m3 flipped", "op[(o[p] + l3 + m3) * C + u] += w * c *", "op[(o[p] + l3 - m3) * C + u] += w * c *"),
+    ("per-path backward: the summed slot read", "const double gv = G[(i * Dmid + o[p] + l3 + m3) * C + u];",
+     "const double gv = G[(i * Dmid + l3 * l3 + l3 + m3) * C + u];"),
 ]
 
 
