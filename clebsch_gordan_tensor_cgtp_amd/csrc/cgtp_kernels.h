@@ -243,13 +243,15 @@ struct Pos {
 // latency they hide (measured: 4% slower on the 50,000-atom layer), so only
 // degree 1 prefetches.
 // The double-backward kernels carry a second set of operands (the
-// cotangents) and run at half the occupancy.
+// cotangents) and run at lower occupancy (at degree 2 the receiver side fits
+// 3 waves per SIMD without spilling, the sender side 2).
 template <int LM, int LPE>
 struct Tune {
     static constexpr int fwd_occ = LM <= 2 ? 4 : 2;
     static constexpr int bwd_occ = LM == 1 || (LM == 2 && LPE == 64) ? 4 : (LM == 2 ? 3 : 2);
     static constexpr bool fwd_prefetch = LM == 1;
-    static constexpr int dbl_occ = LM == 1 ? 4 : (LM == 2 ? 2 : 1);
+    static constexpr int dbl_fwd_occ = LM == 1 ? 4 : (LM == 2 ? 3 : 1);
+    static constexpr int dbl_bwd_occ = LM == 1 ? 4 : (LM == 2 ? 2 : 1);
 };
 
 // acc += a*b, where the first term of a sum (`started` false, known at
@@ -477,7 +479,7 @@ __device__ __forceinline__ void fwd_slice_dbl(const FwdEdgeD<Tb>& d, const doubl
 }
 
 template <int LM, int LPE, int H, bool SUB, bool DBL = false>
-__global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_occ : Tune<LM, LPE>::fwd_occ))
+__global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_fwd_occ : Tune<LM, LPE>::fwd_occ))
     k_conv_fwd(FwdArgs a)
 {
     using Tb = cgmath::Tables<LM, LM, LM>;
@@ -1171,7 +1173,7 @@ __device__ __forceinline__ double wave_sum_tile(const double* __restrict__ red, 
 constexpr int kDyChunk = 64;
 
 template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool MID = false>
-__global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_occ : Tune<LM, LPE>::bwd_occ))
+__global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_bwd_occ : Tune<LM, LPE>::bwd_occ))
     k_conv_bwd(BwdArgs a)
 {
     using Tb = cgmath::Tables<LM, LM, LM>;

@@ -30,7 +30,7 @@
  *     Y_{l,m} = sqrt2 (-1)^m Im Y_l^|m| (m<0), Y_l^0, sqrt2 (-1)^m Re Y_l^m (m>0).
  *   - layouts, all row-major fp32, channels fastest:
  *       x, grad_x       [N][(l_in+1)^2][C]
- *       out, grad_out   [N][(l_out+1)^2][C]
+ *       out, grad_out   [N][(l_out+1)^2][C]   ([N][D_mid][C] with CGTP_FLAG_PATH_OUTPUTS)
  *       Y, grad_Y       [E][(l_sh+1)^2]
  *       W, grad_W       [E][P][C]   ([E][C] with CGTP_FLAG_SHARED_WEIGHTS)
  *       r               [E][3]
