@@ -546,8 +546,9 @@ def summarize(d, workload):
     D = (w.l_max + 1) ** 2
     alg_all = algorithmic_bytes(g.n_nodes, g.n_edges, w.num_paths, w.channels, D, D, D)
     for kern in ("conv_fwd", "conv_bwd"):
-        # the step's kernel (the double backward instantiates the same template with DBL = true)
-        name = [k for k in fetch if re.search(rf"k_{kern}<\d+, \d+, \d+, (true|false), false>", k)][0]
+        # the step's kernel (the double backward and the per-path outputs instantiate the
+        # same template with DBL or MID = true)
+        name = [k for k in fetch if re.search(rf"k_{kern}<\d+, \d+, \d+, (true|false), false(, false)?>", k)][0]
         fk, wk = fetch[name]["FETCH_SIZE"], write[name]["WRITE_SIZE"]
         rd, wr = fk * 1024 * ff, wk * 1024 * wf
         alg = alg_all[kern.split("_")[1]]
@@ -582,7 +583,7 @@ def summarize(d, workload):
              "# 4 * SQ_ACTIVE_INST_VALU / (gpu_cycles * 1024 SIMDs) (SQ cycle counters count 4-cycle units);",
              "# mean resident waves per SIMD = 4 * SQ_WAVE_CYCLES / (gpu_cycles * 1024)"]
     for name, c in sq.items():
-        if not re.search(r"k_conv_(fwd|bwd)<\d+, \d+, \d+, (true|false), false>", name):
+        if not re.search(r"k_conv_(fwd|bwd)<\d+, \d+, \d+, (true|false), false(, false)?>", name):
             continue
         c = dict(c)
         c.update(sq2.get(name, {}))
