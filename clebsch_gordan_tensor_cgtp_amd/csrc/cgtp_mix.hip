@@ -11,9 +11,9 @@
 //   d_mid[i][o_p + m][u] = sum_w G[i][k(l3_p,m)][w] Wmix[p][u][w]
 //   d_Wmix[p][u][w]      = sum_i sum_m mid[i][o_p + m][u] G[i][k(l3_p,m)][w]
 // All three are dense contractions, run as 16x16x4 fp64 MFMA tiles (fp32
-// operands widened on load, fp64 accumulation).  A 256-thread block holds four
-// waves; a wave owns 16 rows and 64 columns (four MFMA tiles sharing the row
-// operand).  The weight gradient sums over all nodes: the node range is split
+// operands staged through LDS, widened when read, fp64 accumulation).  A
+// 256-thread block computes a 64 x 64 output tile; each of its four waves owns
+// 16 rows (four MFMA tiles sharing the row operand).  The weight gradient sums over all nodes: the node range is split
 // over blocks, each writes its fp64 partial to the workspace, and a second
 // kernel adds the partials in a fixed order.
 //
@@ -32,8 +32,6 @@ namespace {
 
 typedef double v4d __attribute__((ext_vector_type(4)));
 
-constexpr int kRows = 16, kCols = 64, kWaves = 4;
-
 __device__ __forceinline__ int32_t clamp_idx(int32_t v, int32_t n) { return v < n ? v : n - 1; }
 
 // degree of output slot s (s in [l*l, (l+1)*(l+1)))
@@ -44,118 +42,218 @@ __device__ __forceinline__ int32_t slot_degree(int32_t s)
     return l;
 }
 
-// out[i][s][w] for the block's 64 nodes x 64 output channels of slot s
-__global__ void __launch_bounds__(256) k_mix_fwd(MixShape m, const float* __restrict__ mid,
-                                                 const float* __restrict__ Wmix, float* __restrict__ out)
+// ---- LDS-tiled MFMA GEMM ----------------------------------------------------
+// A block computes a 64 x 64 tile of D = sum over K-chunks of A (64 x 32) B
+// (32 x 64).  Every thread brings eight elements of each operand chunk from
+// global memory (runs of eight consecutive addresses, 16-byte loads where the
+// rows allow), the chunk goes to one of two LDS buffers, and each wave runs
+// its 16 x 64 strip as 8 k-steps x 4 MFMA tiles out of it.  The next chunk's
+// global loads are issued before the current chunk's MFMAs; with two buffers
+// one barrier per chunk keeps writers and readers apart.  Row strides of 36
+// and 80 words put the 64 lanes of each MFMA operand read on distinct banks.
+constexpr int kTM = 64, kTN = 64, kTK = 32;
+constexpr int kSA = kTK + 4, kSB = kTN + 16;
+
+struct Tile {
+    float a[kTM][kSA];  // [row][k]
+    float b[kTK][kSB];  // [k][col]
+};
+
+// one chunk: the thread's eight A and eight B elements
+struct Chunk {
+    float av[8], bv[8];
+};
+
+// v[0..7] = p[0..7] where idx0 + j < lim (else 0), 16-byte loads when the
+// whole run is in range and vec (rows of a multiple of four floats) holds
+__device__ __forceinline__ void load8(float (&v)[8], const float* __restrict__ p, int32_t idx0, int32_t lim, bool ok,
+                                      bool vec)
+{
+    if (ok && vec && idx0 + 8 <= lim) {
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        const float4 b = *reinterpret_cast<const float4*>(p + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (ok && idx0 + j < lim) ? p[j] : 0.0f;
+    }
+}
+
+// MFMAs of one staged chunk for this wave's 16 rows
+__device__ __forceinline__ void mfma_chunk(const Tile& T, int wave, int lane, v4d (&acc)[4])
+{
+    const int i = lane % 16, kk = lane / 16;
+#pragma unroll
+    for (int ks = 0; ks < kTK / 4; ++ks) {
+        const double a = (double)T.a[16 * wave + i][4 * ks + kk];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const double b = (double)T.b[4 * ks + kk][16 * t + i];
+            acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[t], 0, 0, 0);
+        }
+    }
+}
+
+// Runs chunks 0 .. n-1 through the two buffers starting at T[*buf]:
+// load(c, ch) fills the thread's elements of chunk c, put(ch, T) writes them
+// to LDS.  *buf tracks the buffer parity across calls.
+template <class Load, class Put>
+__device__ __forceinline__ void gemm_chunks(int32_t n, Tile (&T)[2], int& buf, Load&& load, Put&& put,
+                                            v4d (&acc)[4])
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int32_t n0 = (int32_t)blockIdx.x * (kRows * kWaves) + kRows * wave;
-    const int32_t c0 = (int32_t)blockIdx.y * kCols;
-    const int32_t s = (int32_t)blockIdx.z;
-    const int32_t l3 = slot_degree(s), mm = s - l3 * l3;
+    if (n <= 0) return;
+    Chunk cur;
+    load(0, cur);
+    for (int32_t c = 0; c < n; ++c) {
+        // T[buf] was last read two chunks ago; every wave has passed the
+        // barrier after that
+        put(cur, T[buf]);
+        __syncthreads();
+        if (c + 1 < n) load(c + 1, cur);
+        mfma_chunk(T[buf], wave, lane, acc);
+        buf ^= 1;
+    }
+}
+
+// store of D's 16 x 64 strip of this wave: row index r, column index col
+template <class Store>
+__device__ __forceinline__ void store_strip(const v4d (&acc)[4], Store&& store)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = lane % 16, kk = lane / 16;
-    const int32_t node = n0 + i, nodec = clamp_idx(node, m.N);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) store(16 * wave + 4 * r + kk, 16 * t + i, acc[t][r]);
+}
+
+// out[i][s][w]: rows = 64 nodes, cols = 64 output channels, K = (paths of
+// l3) x C.  The highest slots, whose degrees have the most paths, go first.
+__global__ void __launch_bounds__(256) k_mix_fwd(MixShape m, bool vec, const float* __restrict__ mid,
+                                                 const float* __restrict__ Wmix, float* __restrict__ out)
+{
+    __shared__ Tile T[2];
+    const int tid = threadIdx.x;
+    const int32_t n0 = (int32_t)blockIdx.x * kTM, c0 = (int32_t)blockIdx.y * kTN;
+    const int32_t s = m.Dout - 1 - (int32_t)blockIdx.z;
+    const int32_t l3 = slot_degree(s), mm = s - l3 * l3;
+    const int32_t kc = (m.C + kTK - 1) / kTK;  // chunks per path
     v4d acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = v4d{0.0, 0.0, 0.0, 0.0};
+    // A: row tid/4, k (tid%4)*8 + j; B: k tid/8, col (tid%8)*8 + j
+    const int ar = tid / 4, ak = (tid % 4) * 8, bk = tid / 8, bc = (tid % 8) * 8;
+    const int32_t node = n0 + ar, nodec = clamp_idx(node, m.N), col = c0 + bc;
+    int buf = 0;
     for (int32_t p = 0; p < m.P; ++p) {
         if (m.l3[p] != l3) continue;
         const float* arow = mid + ((int64_t)nodec * m.Dmid + m.o[p] + mm) * m.C;
         const float* wp = Wmix + (int64_t)p * m.C * m.Co;
-        for (int32_t u0 = 0; u0 < m.C; u0 += 4) {
-            const int32_t u = u0 + kk, uc = clamp_idx(u, m.C);
-            const double a = (node < m.N && u < m.C) ? (double)arow[uc] : 0.0;
+        auto load = [&](int32_t c, Chunk& ch) {
+            const int32_t u = c * kTK + ak, ub = c * kTK + bk;
+            load8(ch.av, arow + (u < m.C ? u : 0), u, m.C, node < m.N, vec);
+            load8(ch.bv, wp + (int64_t)clamp_idx(ub, m.C) * m.Co + (col < m.Co ? col : 0), col, m.Co, ub < m.C,
+                  vec);
+        };
+        auto put = [&](const Chunk& ch, Tile& t) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int32_t col = c0 + 16 * t + i;
-                const double b = (u < m.C && col < m.Co) ? (double)wp[(int64_t)uc * m.Co + clamp_idx(col, m.Co)] : 0.0;
-                acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[t], 0, 0, 0);
+            for (int j = 0; j < 8; ++j) {
+                t.a[ar][ak + j] = ch.av[j];
+                t.b[bk][bc + j] = ch.bv[j];
             }
-        }
+        };
+        gemm_chunks(kc, T, buf, load, put, acc);
     }
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int32_t nd = n0 + 4 * r + kk, col = c0 + 16 * t + i;
-            if (nd < m.N && col < m.Co) out[((int64_t)nd * m.Dout + s) * m.Co + col] = (float)acc[t][r];
-        }
+    store_strip(acc, [&](int r, int cidx, double v) {
+        const int32_t nd = n0 + r, cc = c0 + cidx;
+        if (nd < m.N && cc < m.Co) out[((int64_t)nd * m.Dout + s) * m.Co + cc] = (float)v;
+    });
 }
 
-// d_mid[i][row][u] for the block's 64 nodes x 64 input channels of per-path row `row`
-__global__ void __launch_bounds__(256) k_mix_bwd_data(MixShape m, const float* __restrict__ G,
+// d_mid[i][row][u]: rows = 64 nodes, cols = 64 input channels, K = C_out
+__global__ void __launch_bounds__(256) k_mix_bwd_data(MixShape m, bool vec, const float* __restrict__ G,
                                                       const float* __restrict__ Wmix, float* __restrict__ dmid)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int32_t n0 = (int32_t)blockIdx.x * (kRows * kWaves) + kRows * wave;
-    const int32_t c0 = (int32_t)blockIdx.y * kCols;
+    __shared__ Tile T[2];
+    const int tid = threadIdx.x;
+    const int32_t n0 = (int32_t)blockIdx.x * kTM, c0 = (int32_t)blockIdx.y * kTN;
     const int32_t row = (int32_t)blockIdx.z;
     int32_t p = 0;
     while (p + 1 < m.P && m.o[p + 1] <= row) ++p;
     const int32_t s = m.l3[p] * m.l3[p] + (row - m.o[p]);
-    const int i = lane % 16, kk = lane / 16;
-    const int32_t node = n0 + i, nodec = clamp_idx(node, m.N);
-    const float* grow = G + ((int64_t)nodec * m.Dout + s) * m.Co;
-    const float* wp = Wmix + (int64_t)p * m.C * m.Co;
     v4d acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = v4d{0.0, 0.0, 0.0, 0.0};
-    for (int32_t w0 = 0; w0 < m.Co; w0 += 4) {
-        const int32_t w = w0 + kk, wc = clamp_idx(w, m.Co);
-        const double a = (node < m.N && w < m.Co) ? (double)grow[wc] : 0.0;
+    // A (G rows, contiguous in w): row tid/4, k (tid%4)*8 + j; B (Wmix[p][u][w],
+    // contiguous in w): col u = tid/4, k (tid%4)*8 + j, stored transposed
+    const int ar = tid / 4, ak = (tid % 4) * 8;
+    const int32_t node = n0 + ar, nodec = clamp_idx(node, m.N);
+    const float* grow = G + ((int64_t)nodec * m.Dout + s) * m.Co;
+    const int32_t ucol = c0 + ar;
+    const float* wrow = Wmix + ((int64_t)p * m.C + clamp_idx(ucol, m.C)) * m.Co;
+    auto load = [&](int32_t c, Chunk& ch) {
+        const int32_t w = c * kTK + ak, wo = w < m.Co ? w : 0;
+        load8(ch.av, grow + wo, w, m.Co, node < m.N, vec);
+        load8(ch.bv, wrow + wo, w, m.Co, ucol < m.C, vec);
+    };
+    auto put = [&](const Chunk& ch, Tile& t) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int32_t u = c0 + 16 * t + i;
-            const double b = (w < m.Co && u < m.C) ? (double)wp[(int64_t)clamp_idx(u, m.C) * m.Co + wc] : 0.0;
-            acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[t], 0, 0, 0);
+        for (int j = 0; j < 8; ++j) {
+            t.a[ar][ak + j] = ch.av[j];
+            t.b[ak + j][ar] = ch.bv[j];
         }
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int32_t nd = n0 + 4 * r + kk, u = c0 + 16 * t + i;
-            if (nd < m.N && u < m.C) dmid[((int64_t)nd * m.Dmid + row) * m.C + u] = (float)acc[t][r];
-        }
+    };
+    int buf = 0;
+    gemm_chunks((m.Co + kTK - 1) / kTK, T, buf, load, put, acc);
+    store_strip(acc, [&](int r, int cidx, double v) {
+        const int32_t nd = n0 + r, u = c0 + cidx;
+        if (nd < m.N && u < m.C) dmid[((int64_t)nd * m.Dmid + row) * m.C + u] = (float)v;
+    });
 }
 
-// part[sp][p][u][w]: path p's weight gradient over the nodes of split sp
-__global__ void __launch_bounds__(256) k_mix_bwd_weight(MixShape m, int32_t nsplit, int32_t chunk,
+// part[sp][p][u][w]: rows = 64 input channels, cols = 64 output channels,
+// K = (2*l3+1) x the nodes of split sp
+__global__ void __launch_bounds__(256) k_mix_bwd_weight(MixShape m, bool vec, int32_t nsplit, int32_t chunk,
                                                         const float* __restrict__ mid, const float* __restrict__ G,
                                                         double* __restrict__ part)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int32_t r0 = (int32_t)blockIdx.x * (kRows * kWaves) + kRows * wave;  // input channels u
-    const int32_t c0 = (int32_t)blockIdx.y * kCols;                             // output channels w
+    __shared__ Tile T[2];
+    const int tid = threadIdx.x;
+    const int32_t r0 = (int32_t)blockIdx.x * kTM, c0 = (int32_t)blockIdx.y * kTN;
     const int32_t p = (int32_t)blockIdx.z / nsplit, sp = (int32_t)blockIdx.z % nsplit;
     const int32_t nb = sp * chunk, ne = nb + chunk < m.N ? nb + chunk : m.N;
-    const int i = lane % 16, kk = lane / 16;
-    const int32_t u = r0 + i, uc = clamp_idx(u, m.C);
     const int32_t d3 = 2 * m.l3[p] + 1, s0 = m.l3[p] * m.l3[p];
+    const int32_t nodes = ne > nb ? ne - nb : 0;
+    const int32_t kcn = (nodes + kTK - 1) / kTK;  // chunks per m
     v4d acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = v4d{0.0, 0.0, 0.0, 0.0};
-    for (int32_t mm = 0; mm < d3; ++mm) {
-        for (int32_t i0 = nb; i0 < ne; i0 += 4) {
-            const int32_t node = i0 + kk, nodec = clamp_idx(node, m.N);
-            const bool in = node < ne;
-            const double a = (in && u < m.C) ? (double)mid[((int64_t)nodec * m.Dmid + m.o[p] + mm) * m.C + uc] : 0.0;
-            const float* grow = G + ((int64_t)nodec * m.Dout + s0 + mm) * m.Co;
+    // A (mid rows, contiguous in u): node k = tid/8, u (tid%8)*8 + j, stored
+    // transposed; B (G rows, contiguous in w): node k = tid/8, w (tid%8)*8 + j
+    const int kr = tid / 8, c8 = (tid % 8) * 8;
+    const int32_t u = r0 + c8, w = c0 + c8;
+    auto load = [&](int32_t c, Chunk& ch) {
+        const int32_t mmi = c / kcn, i0 = nb + (c % kcn) * kTK;
+        const int32_t node = i0 + kr, nodec = clamp_idx(node, m.N);
+        const bool in = node < ne;
+        load8(ch.av, mid + ((int64_t)nodec * m.Dmid + m.o[p] + mmi) * m.C + (u < m.C ? u : 0), u, m.C, in, vec);
+        load8(ch.bv, G + ((int64_t)nodec * m.Dout + s0 + mmi) * m.Co + (w < m.Co ? w : 0), w, m.Co, in, vec);
+    };
+    auto put = [&](const Chunk& ch, Tile& t) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int32_t col = c0 + 16 * t + i;
-                const double b = (in && col < m.Co) ? (double)grow[clamp_idx(col, m.Co)] : 0.0;
-                acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[t], 0, 0, 0);
-            }
+        for (int j = 0; j < 8; ++j) {
+            t.a[c8 + j][kr] = ch.av[j];
+            t.b[kr][c8 + j] = ch.bv[j];
         }
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int32_t uu = r0 + 4 * r + kk, col = c0 + 16 * t + i;
-            if (uu < m.C && col < m.Co) part[(((int64_t)sp * m.P + p) * m.C + uu) * m.Co + col] = acc[t][r];
-        }
+    };
+    int buf = 0;
+    if (kcn > 0) gemm_chunks(d3 * kcn, T, buf, load, put, acc);
+    store_strip(acc, [&](int r, int cidx, double v) {
+        const int32_t uu = r0 + r, col = c0 + cidx;
+        if (uu < m.C && col < m.Co) part[(((int64_t)sp * m.P + p) * m.C + uu) * m.Co + col] = v;
+    });
 }
 
 // dWmix[p][u][w] = sum over the splits, in order
@@ -180,18 +278,25 @@ inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b);
 
 }  // namespace
 
-// Node-range splits of the weight gradient: enough blocks to fill the chip
-// (about 4096 with the tiles of every path) and at most 512 nodes per split,
-// but at least 16 nodes per split and at most 256 splits.
+// Node-range splits of the weight gradient: about four blocks per compute
+// unit over the tiles of every path, at least two chunks of nodes per split
+// (fewer splits write fewer fp64 partials) and at most 256 splits.
 int32_t mix_splits(int64_t N, int32_t P, int32_t C, int32_t Co)
 {
-    const int64_t tiles = (int64_t)P * ((C + 63) / 64) * ((Co + 63) / 64);
-    int64_t n = (4096 + tiles - 1) / (tiles > 0 ? tiles : 1);
-    if (n < (N + 511) / 512) n = (N + 511) / 512;
-    const int64_t by_nodes = (N + 15) / 16;
+    const int64_t tiles = (int64_t)P * ((C + kTM - 1) / kTM) * ((Co + kTN - 1) / kTN);
+    int64_t n = (1024 + tiles - 1) / (tiles > 0 ? tiles : 1);
+    const int64_t by_nodes = (N + 2 * kTK - 1) / (2 * kTK);
     if (n > by_nodes) n = by_nodes;
     if (n > 256) n = 256;
     return (int32_t)(n < 1 ? 1 : n);
+}
+
+// nodes per split: a whole number of chunks
+static int32_t mix_split_nodes(int64_t N, int32_t nsplit)
+{
+    const int64_t per = (N + nsplit - 1) / nsplit;
+    const int64_t r = (per + kTK - 1) / kTK * kTK;
+    return (int32_t)(r > 0 ? r : kTK);
 }
 
 size_t mix_workspace_bytes(int64_t N, int32_t P, int32_t C, int32_t Co)
@@ -199,11 +304,15 @@ size_t mix_workspace_bytes(int64_t N, int32_t P, int32_t C, int32_t Co)
     return sizeof(double) * (size_t)mix_splits(N, P, C, Co) * (size_t)P * (size_t)C * (size_t)Co;
 }
 
+// 16-byte operand loads need rows of a multiple of four floats (the entry
+// points only take 16-byte aligned arrays)
+static bool vec_ok(const MixShape& m) { return m.C % 4 == 0 && m.Co % 4 == 0; }
+
 hipError_t launch_mix_fwd(const MixShape& m, const float* mid, const float* Wmix, float* out, hipStream_t s)
 {
     if (m.N == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_mix_fwd, dim3(cdiv(m.N, kRows * kWaves), cdiv(m.Co, kCols), (unsigned)m.Dout), dim3(256), 0,
-                       s, m, mid, Wmix, out);
+    hipLaunchKernelGGL(k_mix_fwd, dim3(cdiv(m.N, kTM), cdiv(m.Co, kTN), (unsigned)m.Dout), dim3(256), 0,
+                       s, m, vec_ok(m), mid, Wmix, out);
     return hipGetLastError();
 }
 
@@ -220,16 +329,16 @@ hipError_t launch_mix_bwd(const MixShape& m, const float* mid, const float* Wmix
         return hipSuccess;
     }
     if (dmid && m.N > 0) {
-        hipLaunchKernelGGL(k_mix_bwd_data, dim3(cdiv(m.N, kRows * kWaves), cdiv(m.C, kCols), (unsigned)m.Dmid),
-                           dim3(256), 0, s, m, G, Wmix, dmid);
+        hipLaunchKernelGGL(k_mix_bwd_data, dim3(cdiv(m.N, kTM), cdiv(m.C, kTN), (unsigned)m.Dmid),
+                           dim3(256), 0, s, m, vec_ok(m), G, Wmix, dmid);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (dW) {
         const int32_t nsplit = mix_splits(m.N, m.P, m.C, m.Co);
-        const int32_t chunk = (int32_t)((m.N + nsplit - 1) / nsplit);
-        hipLaunchKernelGGL(k_mix_bwd_weight, dim3(cdiv(m.C, kRows * kWaves), cdiv(m.Co, kCols), (unsigned)(m.P * nsplit)),
-                           dim3(256), 0, s, m, nsplit, chunk > 0 ? chunk : 1, mid, G, part);
+        const int32_t chunk = mix_split_nodes(m.N, nsplit);
+        hipLaunchKernelGGL(k_mix_bwd_weight, dim3(cdiv(m.C, kTM), cdiv(m.Co, kTN), (unsigned)(m.P * nsplit)),
+                           dim3(256), 0, s, m, vec_ok(m), nsplit, chunk, mid, G, part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t n = (int64_t)m.P * m.C * m.Co;

@@ -5,9 +5,12 @@ fully connected product.
 
 The oracle's mixing is pinned on the CPU (identity matrices give the summed
 convolution, diagonal ones the weight-scaled convolution; finite
-differences).  Cases cover ragged node counts (partial 16-row tiles and
-node-range splits), input and output channel counts that are not multiples
-of the 4-deep or 16/64-wide tiles, every degree up to 3 and mixed degrees.
+differences).  Cases cover ragged node counts (partial 64-row tiles, a
+partial last 32-node chunk, empty node-range splits), input and output
+channel counts that are not multiples of the 32-deep chunks or the 64-wide
+tiles or not of four (element loads instead of 16-byte loads), every degree
+up to 3 and mixed degrees; operands that are not 16-byte aligned are
+refused.
 """
 import numpy as np
 import pytest
@@ -48,7 +51,9 @@ def run_mix(torch, dev, oracle, Ls, C, Co, N, seed=0):
 
 @pytest.mark.parametrize("Ls,C,Co,N", [((2, 2, 2), 128, 128, 2000), ((2, 2, 2), 64, 64, 70), ((1, 1, 1), 8, 8, 1),
                                        ((3, 3, 3), 64, 100, 333), ((2, 2, 2), 5, 7, 513), ((3, 3, 3), 16, 200, 1025),
-                                       ((2, 1, 3), 24, 48, 96), ((0, 1, 1), 1, 1, 17), ((1, 2, 2), 128, 3, 4097)])
+                                       ((2, 1, 3), 24, 48, 96), ((0, 1, 1), 1, 1, 17), ((1, 2, 2), 128, 3, 4097),
+                                       ((2, 2, 2), 36, 68, 2049), ((3, 2, 1), 96, 130, 95), ((2, 2, 2), 32, 40, 20001),
+                                       ((1, 1, 1), 30, 64, 65)])
 def test_path_mix(torch_dev, oracle, Ls, C, Co, N):
     torch, dev = torch_dev
     run_mix(torch, dev, oracle, Ls, C, Co, N)
@@ -92,6 +97,26 @@ def test_fully_connected_product_composed(torch_dev, oracle, L, C, Co):
     assert_parity(dx.cpu().numpy(), rdx, "dx")
     assert_parity(dW.cpu().numpy(), rdW, "dW")
     assert_parity(dY.cpu().numpy(), rdY, "dY")
+
+
+def test_path_mix_rejects_unaligned_operands(torch_dev):
+    """The header requires 16-byte aligned arrays (the kernels load 16 bytes
+    at a time): an operand 4 bytes into its allocation is refused."""
+    torch, dev = torch_dev
+    from clebsch_gordan_tensor_cgtp_amd import _lib
+    from clebsch_gordan_tensor_cgtp_amd.ops import Plan
+    plan = Plan(2, 2, 2, 64, path_outputs=True)
+    N = 30
+    shape = (N, plan.mid_rows, 64)
+    mid = torch.zeros(N * plan.mid_rows * 64 + 1, device=dev)[1:].view(shape)
+    assert mid.data_ptr() % 16 == 4
+    Wm = torch.randn(plan.num_paths, 64, 64, device=dev)
+    with pytest.raises(_lib.CgtpError) as ei:
+        plan.path_mix_fwd(mid, Wm)
+    assert ei.value.status == _lib.CGTP_ERR_INVALID_ARG
+    with pytest.raises(_lib.CgtpError) as ei:
+        plan.path_mix_bwd(mid, Wm, torch.zeros(N, 9, 64, device=dev))
+    assert ei.value.status == _lib.CGTP_ERR_INVALID_ARG
 
 
 def test_path_mix_no_nodes(torch_dev):
