@@ -80,8 +80,6 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v)
     return v;
 }
 
-constexpr int kDegBins = 1024;  // in-range order bins; degrees >= kDegBins-1 share the first bin
-
 __device__ __forceinline__ int deg_bin(int32_t d) { return kDegBins - 1 - (d < kDegBins - 1 ? d : kDegBins - 1); }
 
 // Inclusive prefix sum of one value per thread over a 1024-thread block:
@@ -109,20 +107,22 @@ __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* tot, int3
 
 }  // namespace
 
-// Step 1, one wave per receiver i: clear i's counters (used from step 2 on)
-// and, for the clustered schedule, key1(i) = min node_key over i and its
+// Step 1, one wave per receiver i: clear i's counters (used from step 2 on;
+// block 0 also clears the global degree bins of step 3) and, for the
+// clustered schedule, key1(i) = min node_key over i and its
 // senders.
 __global__ void __launch_bounds__(256) k_prep_keys(int32_t N, int32_t E, const int32_t* __restrict__ row_ptr,
                                                     const int32_t* __restrict__ src, int32_t locality,
                                                     uint64_t* __restrict__ key1, int32_t* __restrict__ cnt,
-                                                    int32_t* __restrict__ cursor, int32_t* __restrict__ ccnt)
+                                                    int32_t* __restrict__ ccnt, int32_t* __restrict__ bins)
 {
+    if (blockIdx.x == 0)
+        for (int k = threadIdx.x; k < 4 * kDegBins; k += 256) bins[k] = 0;
     const int32_t i = (int32_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (i >= N) return;
     if (lane == 0) {
         cnt[(int64_t)i * kCounterStride] = 0;
-        cursor[(int64_t)i * kCounterStride] = 0;
         ccnt[i] = 0;
     }
     if (!locality) return;
@@ -137,13 +137,15 @@ __global__ void __launch_bounds__(256) k_prep_keys(int32_t N, int32_t E, const i
     if (lane == 0) key1[i] = m;
 }
 
-// Step 2, one wave per receiver i: the out-degree count of every sender and,
-// for the locality schedule, i's cluster centre and its rank inside the
-// cluster (integer atomics).
+// Step 2, one wave per receiver i: the out-degree count of every sender, with
+// each in-edge's rank among its sender's edges (the value the count's atomic
+// returns, in arrival order) kept in urank, and, for the locality schedule,
+// i's cluster centre and its rank inside the cluster (integer atomics).
 __global__ void __launch_bounds__(256) k_prep_centers(int32_t N, int32_t E, const int32_t* __restrict__ row_ptr,
                                                        const int32_t* __restrict__ src, int32_t locality,
                                                        const uint64_t* __restrict__ key1, int32_t* __restrict__ center,
-                                                       int32_t* __restrict__ crank, int32_t* ccnt, int32_t* cnt)
+                                                       int32_t* __restrict__ crank, int32_t* ccnt, int32_t* cnt,
+                                                       int32_t* __restrict__ urank)
 {
     const int32_t i = (int32_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -162,13 +164,16 @@ __global__ void __launch_bounds__(256) k_prep_centers(int32_t N, int32_t E, cons
             crank[i] = atomicAdd(&ccnt[c], 1);
         }
     }
-    for (int32_t e = e0 + lane; e < e1; e += 64) atomicAdd(&cnt[(int64_t)valid_node(src[e], N) * kCounterStride], 1);
+    for (int32_t e = e0 + lane; e < e1; e += 64)
+        urank[e] = atomicAdd(&cnt[(int64_t)valid_node(src[e], N) * kCounterStride], 1);
 }
 
-// Step 3, one block of 1024 threads: the sender offsets srow (prefix sum of
-// the out-degrees) and the two block schedules.  Default: one range of all N
-// nodes, longest first (LDS histogram of degree bins), block b serving entry
-// b.  Locality: node i's place in the cluster order is g = coff[centre] +
+// Step 3 of the locality schedule (and of an empty graph), one block of 1024
+// threads: the sender offsets srow (prefix sum of the out-degrees) and the two
+// block schedules.  (The longest-first schedule of a non-empty graph runs
+// k_prep_hist and k_prep_place below instead; this kernel still implements it
+// as one range of all N nodes, longest first, block b serving entry b.)
+// Locality: node i's place in the cluster order is g = coff[centre] +
 // rank (coff the prefix sum of the cluster sizes), its range is x = g / Q,
 // and inside a range the nodes go longest first by LDS histograms of
 // (range, degree bin); block x + 8s serves entry s of range x.
@@ -281,12 +286,105 @@ __global__ void __launch_bounds__(1024) k_prep_orders(int32_t N, int32_t E, int3
     }
 }
 
+// Step 3 of the longest-first schedule over several blocks, part 1: block b
+// takes nodes [b*1024, (b+1)*1024), one per thread.  It writes the sum of
+// their out-degrees to bsum[b] and adds its LDS histograms of in-degree and
+// out-degree bins to the global bins (one integer atomic per non-empty bin).
+__global__ void __launch_bounds__(kOrderBlock) k_prep_hist(int32_t N, int32_t E, const int32_t* __restrict__ row_ptr,
+                                                            const int32_t* __restrict__ cnt, int32_t* bins,
+                                                            int32_t* __restrict__ bsum)
+{
+    static_assert(kOrderBlock == 1024 && kDegBins == 1024, "one node and one bin per thread");
+    __shared__ int32_t hin[kDegBins], hout[kDegBins], tot[16];
+    const int t = threadIdx.x;
+    const int64_t i64 = (int64_t)blockIdx.x * kOrderBlock + t;
+    const int32_t i = i64 < N ? (int32_t)i64 : N;  // i == N: no node
+    hin[t] = 0;
+    hout[t] = 0;
+    __syncthreads();
+    int32_t dout = 0;
+    if (i < N) {
+        const int32_t e0 = clampi(row_ptr[i], 0, E), e1 = clampi(row_ptr[i + 1], e0, E);
+        dout = cnt[(int64_t)i * kCounterStride];
+        atomicAdd(&hin[deg_bin(e1 - e0)], 1);
+        atomicAdd(&hout[deg_bin(dout)], 1);
+    }
+    int32_t total;
+    block_scan_1024(dout, tot, &total);  // ends with a barrier: the histograms are complete
+    if (t == 0) bsum[blockIdx.x] = total;
+    if (hin[t] > 0) atomicAdd(&bins[t], hin[t]);
+    if (hout[t] > 0) atomicAdd(&bins[kDegBins + t], hout[t]);
+}
+
+// Part 2, the same blocks: srow (the block's base is the sum of bsum over
+// the blocks before it, then a scan inside the block), the start of every bin
+// (a scan of the global bins), and the schedules: the block claims a run of
+// each non-empty bin with one atomic on the bin's cursor and places its nodes
+// in it through LDS atomics.  Block b of a convolution serves entry b; the
+// entries past N (up to the next multiple of kXcds) are idle blocks (-1).
+__global__ void __launch_bounds__(kOrderBlock) k_prep_place(int32_t N, int32_t E, const int32_t* __restrict__ row_ptr,
+                                                             const int32_t* __restrict__ cnt, int32_t* bins,
+                                                             const int32_t* __restrict__ bsum, int32_t* __restrict__ srow,
+                                                             int32_t* __restrict__ rorder, int32_t* __restrict__ sorder)
+{
+    __shared__ int32_t hin[kDegBins], hout[kDegBins], bin_in[kDegBins], bin_out[kDegBins], tot[16];
+    const int t = threadIdx.x;
+    const int32_t blk = (int32_t)blockIdx.x;
+    const int64_t i64 = (int64_t)blk * kOrderBlock + t;
+    const int32_t i = i64 < N ? (int32_t)i64 : N;  // i == N: no node
+    hin[t] = 0;
+    hout[t] = 0;
+    // sender offsets
+    int32_t before = 0;
+    for (int32_t k = t; k < blk; k += kOrderBlock) before += bsum[k];
+    int32_t base;
+    block_scan_1024(before, tot, &base);
+    int32_t din = 0, dout = 0;
+    if (i < N) {
+        const int32_t e0 = clampi(row_ptr[i], 0, E), e1 = clampi(row_ptr[i + 1], e0, E);
+        din = e1 - e0;
+        dout = cnt[(int64_t)i * kCounterStride];
+    }
+    int32_t tt;
+    const int32_t incl = block_scan_1024(dout, tot, &tt);
+    if (i < N) srow[i + 1] = base + incl;
+    if (i == 0) srow[0] = 0;
+    // exclusive start of bin t in each schedule
+    const int32_t gi = bins[t], go = bins[kDegBins + t];
+    const int32_t si = block_scan_1024(gi, tot, &tt) - gi;
+    const int32_t so = block_scan_1024(go, tot, &tt) - go;
+    if (i < N) {
+        atomicAdd(&hin[deg_bin(din)], 1);
+        atomicAdd(&hout[deg_bin(dout)], 1);
+    }
+    __syncthreads();
+    // this block's run of bin t, then hin/hout count the places taken in it
+    bin_in[t] = hin[t] > 0 ? si + atomicAdd(&bins[2 * kDegBins + t], hin[t]) : 0;
+    bin_out[t] = hout[t] > 0 ? so + atomicAdd(&bins[3 * kDegBins + t], hout[t]) : 0;
+    hin[t] = 0;
+    hout[t] = 0;
+    __syncthreads();
+    if (i < N) {
+        const int bi = deg_bin(din), bo = deg_bin(dout);
+        const int32_t pi = bin_in[bi] + atomicAdd(&hin[bi], 1), po = bin_out[bo] + atomicAdd(&hout[bo], 1);
+        if ((uint32_t)pi < (uint32_t)N) rorder[pi] = i;
+        if ((uint32_t)po < (uint32_t)N) sorder[po] = i;
+    }
+    if (blk == (int32_t)gridDim.x - 1) {
+        const int64_t grid = kXcds * (((int64_t)N + kXcds - 1) / kXcds);
+        if ((int64_t)N + t < grid) {
+            rorder[N + t] = -1;
+            sorder[N + t] = -1;
+        }
+    }
+}
+
 // Step 4, one wave per receiver i: place every in-edge of i in its sender's
-// bucket of the unsorted view (arbitrary order inside a bucket), with i
-// beside it.
+// bucket of the unsorted view at the rank step 2 gave it (arrival order
+// inside a bucket), with i beside it.
 __global__ void __launch_bounds__(256) k_prep_scatter(int32_t N, int32_t E, const int32_t* __restrict__ row_ptr,
                                                        const int32_t* __restrict__ src, const int32_t* __restrict__ srow,
-                                                       int32_t* cursor, int32_t* __restrict__ uperm,
+                                                       const int32_t* __restrict__ urank, int32_t* __restrict__ uperm,
                                                        int32_t* __restrict__ usdst)
 {
     const int32_t i = (int32_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -295,7 +393,7 @@ __global__ void __launch_bounds__(256) k_prep_scatter(int32_t N, int32_t E, cons
     segment(row_ptr, i, E, e0, e1);
     for (int32_t e = e0 + (threadIdx.x & 63); e < e1; e += 64) {
         const int32_t j = valid_node(src[e], N);
-        const int32_t k = srow[j] + atomicAdd(&cursor[(int64_t)j * kCounterStride], 1);
+        const int32_t k = srow[j] + urank[e];
         if ((uint32_t)k < (uint32_t)E) {
             uperm[k] = e;
             usdst[k] = i;
@@ -385,20 +483,31 @@ hipError_t launch_graph_prepare(int32_t N, int32_t E, const int32_t* row_ptr, co
     char* base = (char*)ws;
     auto at = [&](size_t off) { return (int32_t*)(base + off); };
     int32_t *srow = at(L.srow), *perm = at(L.perm), *sdst = at(L.sdst), *uperm = at(L.uperm), *usdst = at(L.usdst);
-    int32_t *cnt = at(L.cnt), *cursor = at(L.cursor), *center = at(L.center), *crank = at(L.crank);
+    int32_t *cnt = at(L.cnt), *center = at(L.center), *crank = at(L.crank);
+    // the edges' ranks inside their senders' buckets live in perm until step 5
+    // writes the sorted view over them
+    int32_t* urank = perm;
     int32_t *ccnt = at(L.ccnt), *coff = at(L.coff), *rorder = at(L.rorder), *sorder = at(L.sorder);
     uint64_t* key1 = (uint64_t*)(base + L.key1);
     const unsigned b4 = (unsigned)((N + 3) / 4);
     const int32_t loc = locality ? 1 : 0;
+    int32_t *bins = at(L.bins), *bsum = at(L.bsum);
     if (N > 0) {
-        hipLaunchKernelGGL(k_prep_keys, dim3(b4), dim3(256), 0, s, N, E, row_ptr, src, loc, key1, cnt, cursor, ccnt);
+        hipLaunchKernelGGL(k_prep_keys, dim3(b4), dim3(256), 0, s, N, E, row_ptr, src, loc, key1, cnt, ccnt, bins);
         hipLaunchKernelGGL(k_prep_centers, dim3(b4), dim3(256), 0, s, N, E, row_ptr, src, loc, key1, center, crank,
-                           ccnt, cnt);
+                           ccnt, cnt, urank);
     }
-    hipLaunchKernelGGL(k_prep_orders, dim3(1), dim3(1024), 0, s, N, E, loc, row_ptr, cnt, ccnt, center, crank, srow,
-                       coff, rorder, sorder);
+    if (N > 0 && !locality) {
+        const unsigned nb = (unsigned)((N + kOrderBlock - 1) / kOrderBlock);
+        hipLaunchKernelGGL(k_prep_hist, dim3(nb), dim3(kOrderBlock), 0, s, N, E, row_ptr, cnt, bins, bsum);
+        hipLaunchKernelGGL(k_prep_place, dim3(nb), dim3(kOrderBlock), 0, s, N, E, row_ptr, cnt, bins, bsum, srow,
+                           rorder, sorder);
+    } else {
+        hipLaunchKernelGGL(k_prep_orders, dim3(1), dim3(1024), 0, s, N, E, loc, row_ptr, cnt, ccnt, center, crank,
+                           srow, coff, rorder, sorder);
+    }
     if (E > 0 && N > 0) {
-        hipLaunchKernelGGL(k_prep_scatter, dim3(b4), dim3(256), 0, s, N, E, row_ptr, src, srow, cursor, uperm, usdst);
+        hipLaunchKernelGGL(k_prep_scatter, dim3(b4), dim3(256), 0, s, N, E, row_ptr, src, srow, urank, uperm, usdst);
         hipLaunchKernelGGL(k_prep_sort, dim3(b4), dim3(256), 0, s, N, E, srow, uperm, usdst, perm, sdst);
     }
     return hipGetLastError();

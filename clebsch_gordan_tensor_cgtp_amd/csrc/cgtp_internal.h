@@ -18,14 +18,20 @@ constexpr int kMaxPaths = 34;
 
 // Byte offsets of the graph view inside the caller's workspace.
 struct WsLayout {
-    size_t srow, perm, sdst, uperm, usdst, cnt, cursor, key1, center, crank, ccnt, coff, rorder, sorder, total;
+    size_t srow, perm, sdst, uperm, usdst, cnt, key1, center, crank, ccnt, coff, rorder, sorder, bins, bsum,
+        total;
 };
+
+// degree bins of the longest-first block schedules (degrees >= kDegBins-1
+// share the first bin), and the nodes per block of the multi-block schedule
+// kernels
+constexpr int kDegBins = 1024;
+constexpr int kOrderBlock = 1024;
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// the per-sender counters and cursors of the graph preparation are spaced one
-// 128-byte cache line apart, so their atomic updates do not serialise on
-// shared lines
+// the per-sender counters of the graph preparation are spaced one 128-byte
+// cache line apart, so their atomic updates do not serialise on shared lines
 constexpr int kCounterStride = 32;
 
 // grid size of the convolution kernels: N rounded up to a multiple of kXcds
@@ -49,7 +55,6 @@ inline WsLayout ws_layout(int64_t N, int64_t E)
     w.uperm = take(sizeof(int32_t) * e1);  // the view before its buckets are sorted
     w.usdst = take(sizeof(int32_t) * e1);
     w.cnt = take(sizeof(int32_t) * kCounterStride * n1);
-    w.cursor = take(sizeof(int32_t) * kCounterStride * n1);
     w.key1 = take(sizeof(uint64_t) * n1);
     w.center = take(sizeof(int32_t) * n1);
     w.crank = take(sizeof(int32_t) * n1);
@@ -57,6 +62,10 @@ inline WsLayout ws_layout(int64_t N, int64_t E)
     w.coff = take(sizeof(int32_t) * n1);
     w.rorder = take(sizeof(int32_t) * grid);
     w.sorder = take(sizeof(int32_t) * grid);
+    // global degree-bin counts and claim cursors (receiver and sender
+    // schedules), and the out-degree sum of every kOrderBlock nodes
+    w.bins = take(sizeof(int32_t) * 4 * kDegBins);
+    w.bsum = take(sizeof(int32_t) * ((n1 + kOrderBlock - 1) / kOrderBlock));
     w.total = o;
     return w;
 }

@@ -128,7 +128,7 @@ cgtp_status_t cgtp_plan_export_cg(cgtp_plan_t plan, int path, double* dense);
 
 /* Bytes of device workspace for N nodes and E edges (independent of the
  * plan's degrees): the sender-sorted view of the CSR and its temporaries and
- * the block schedules, about 16*E + 300*N bytes. */
+ * the block schedules, about 16*E + 170*N + 16384 bytes. */
 cgtp_status_t cgtp_workspace_size(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, size_t* bytes);
 
 /* Real spherical harmonics Y_l(r/|r|), degrees 0..l_sh, orthonormal, of every

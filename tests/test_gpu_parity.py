@@ -184,6 +184,30 @@ def test_graph_prepare(torch_dev, oracle, key, locality):
             assert xs.max() - xs.min() + 1 == xs.shape[0], cc
 
 
+@pytest.mark.parametrize("N", [1, 7, 1023, 1024, 1025, 2049, 3073])
+def test_graph_prepare_block_boundaries(torch_dev, oracle, N):
+    """The longest-first schedules are built 1024 nodes per block: node counts
+    at and around the block size, a last block with one node, nodes with no
+    in- or out-edges, degrees from 0 to 40."""
+    torch, dev = torch_dev
+    from clebsch_gordan_tensor_cgtp_amd.ops import Plan
+    rng = np.random.default_rng(N)
+    degs = np.minimum(rng.integers(0, 41, size=N), N - 1)
+    degs[rng.random(N) < 0.1] = 0
+    g = synth.random_graph(N, degs, seed=N + 3)
+    E = g.n_edges
+    _log(f"[prep-blocks] N={N} E={E}")
+    plan = Plan(1, 1, 1, 8)
+    ws = plan.graph_prepare(torch.from_numpy(g.row_ptr).to(dev), torch.from_numpy(g.src).to(dev)).cpu().numpy()
+    v = read_view(ws, N, E)
+    rs, rp, rd = oracle.graph_transpose(g.row_ptr, g.src)
+    np.testing.assert_array_equal(v["srow"], rs)
+    np.testing.assert_array_equal(v["perm"], rp)
+    np.testing.assert_array_equal(v["sdst"], rd)
+    check_schedule(v["rorder"], np.diff(g.row_ptr), N, "rorder", False)
+    check_schedule(v["sorder"], np.diff(rs), N, "sorder", False)
+
+
 def test_graph_prepare_hub_sender(torch_dev, oracle):
     """One sender with about 3000 out-edges (ranked chunk by chunk) and one
     with 1500, inside an otherwise sparse random graph."""
