@@ -478,9 +478,9 @@ cgtp::MixShape mix_shape(const cgtp_plan_s* plan, int64_t n_nodes, int c_out)
 
 cgtp_status_t cgtp_path_mix_workspace_size(cgtp_plan_t plan, int64_t n_nodes, int c_out, size_t* bytes)
 {
-    if (!plan || !bytes || n_nodes < 0 || c_out < 1) return CGTP_ERR_INVALID_ARG;
+    if (!plan || !bytes || n_nodes < 0 || n_nodes >= (int64_t)INT32_MAX || c_out < 1) return CGTP_ERR_INVALID_ARG;
     if (c_out > kMaxMixOut) return CGTP_ERR_UNSUPPORTED;
-    *bytes = cgtp::mix_workspace_bytes(n_nodes, plan->P, plan->channels, c_out);
+    *bytes = cgtp::mix_workspace_bytes(mix_shape(plan, n_nodes, c_out));
     return CGTP_OK;
 }
 
@@ -505,7 +505,7 @@ cgtp_status_t cgtp_path_mix_bwd(cgtp_plan_t plan, int64_t n_nodes, int c_out, co
     if (!Wmix || !aligned16(Wmix)) return CGTP_ERR_INVALID_ARG;
     if (grad_Wmix) {
         if (!aligned16(grad_Wmix)) return CGTP_ERR_INVALID_ARG;
-        if (!ws || ws_bytes < cgtp::mix_workspace_bytes(n_nodes, plan->P, plan->channels, c_out))
+        if (!ws || ws_bytes < cgtp::mix_workspace_bytes(mix_shape(plan, n_nodes, c_out)))
             return CGTP_ERR_WORKSPACE;
         if (((uintptr_t)ws & 255u) != 0) return CGTP_ERR_INVALID_ARG;
     }

@@ -213,33 +213,38 @@ __global__ void __launch_bounds__(256) k_mix_bwd_data(MixShape m, bool vec, cons
     });
 }
 
-// part[sp][p][u][w]: rows = 64 input channels, cols = 64 output channels,
-// K = (2*l3+1) x the nodes of split sp
-__global__ void __launch_bounds__(256) k_mix_bwd_weight(MixShape m, bool vec, int32_t nsplit, int32_t chunk,
+// part[g][u][w] of run g (path p's runs are g = off[p] .. off[p+1]-1):
+// rows = 64 input channels, cols = 64 output channels, K = the run's (m, node)
+// pairs, m-major (pair r is component m = r / N of node r % N)
+__global__ void __launch_bounds__(256) k_mix_bwd_weight(MixShape m, MixSplit sp, bool vec,
                                                         const float* __restrict__ mid, const float* __restrict__ G,
                                                         double* __restrict__ part)
 {
     __shared__ Tile T[2];
     const int tid = threadIdx.x;
     const int32_t r0 = (int32_t)blockIdx.x * kTM, c0 = (int32_t)blockIdx.y * kTN;
-    const int32_t p = (int32_t)blockIdx.z / nsplit, sp = (int32_t)blockIdx.z % nsplit;
-    const int32_t nb = sp * chunk, ne = nb + chunk < m.N ? nb + chunk : m.N;
-    const int32_t d3 = 2 * m.l3[p] + 1, s0 = m.l3[p] * m.l3[p];
-    const int32_t nodes = ne > nb ? ne - nb : 0;
-    const int32_t kcn = (nodes + kTK - 1) / kTK;  // chunks per m
+    const int32_t g = (int32_t)blockIdx.z;
+    int32_t p = 0;
+    while (p + 1 < m.P && sp.off[p + 1] <= g) ++p;
+    const int32_t s0 = m.l3[p] * m.l3[p];
+    const int64_t pairs = (int64_t)m.N * (2 * m.l3[p] + 1);
+    const int64_t rb = (int64_t)(g - sp.off[p]) * sp.rows;
+    const int64_t re = rb + sp.rows < pairs ? rb + sp.rows : pairs;
+    const int32_t nch = re > rb ? (int32_t)((re - rb + kTK - 1) / kTK) : 0;
     v4d acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = v4d{0.0, 0.0, 0.0, 0.0};
-    // A (mid rows, contiguous in u): node k = tid/8, u (tid%8)*8 + j, stored
-    // transposed; B (G rows, contiguous in w): node k = tid/8, w (tid%8)*8 + j
+    // A (mid rows, contiguous in u): pair k = tid/8, u (tid%8)*8 + j, stored
+    // transposed; B (G rows, contiguous in w): pair k = tid/8, w (tid%8)*8 + j
     const int kr = tid / 8, c8 = (tid % 8) * 8;
     const int32_t u = r0 + c8, w = c0 + c8;
     auto load = [&](int32_t c, Chunk& ch) {
-        const int32_t mmi = c / kcn, i0 = nb + (c % kcn) * kTK;
-        const int32_t node = i0 + kr, nodec = clamp_idx(node, m.N);
-        const bool in = node < ne;
-        load8(ch.av, mid + ((int64_t)nodec * m.Dmid + m.o[p] + mmi) * m.C + (u < m.C ? u : 0), u, m.C, in, vec);
-        load8(ch.bv, G + ((int64_t)nodec * m.Dout + s0 + mmi) * m.Co + (w < m.Co ? w : 0), w, m.Co, in, vec);
+        const int64_t r = rb + (int64_t)c * kTK + kr;
+        const bool in = r < re;
+        const int32_t mm = in ? (int32_t)(r / m.N) : 0;
+        const int32_t node = in ? (int32_t)(r - (int64_t)mm * m.N) : 0;
+        load8(ch.av, mid + ((int64_t)node * m.Dmid + m.o[p] + mm) * m.C + (u < m.C ? u : 0), u, m.C, in, vec);
+        load8(ch.bv, G + ((int64_t)node * m.Dout + s0 + mm) * m.Co + (w < m.Co ? w : 0), w, m.Co, in, vec);
     };
     auto put = [&](const Chunk& ch, Tile& t) {
 #pragma unroll
@@ -249,21 +254,24 @@ __global__ void __launch_bounds__(256) k_mix_bwd_weight(MixShape m, bool vec, in
         }
     };
     int buf = 0;
-    if (kcn > 0) gemm_chunks(d3 * kcn, T, buf, load, put, acc);
+    gemm_chunks(nch, T, buf, load, put, acc);
     store_strip(acc, [&](int r, int cidx, double v) {
         const int32_t uu = r0 + r, col = c0 + cidx;
-        if (uu < m.C && col < m.Co) part[(((int64_t)sp * m.P + p) * m.C + uu) * m.Co + col] = v;
+        if (uu < m.C && col < m.Co) part[((int64_t)g * m.C + uu) * m.Co + col] = v;
     });
 }
 
-// dWmix[p][u][w] = sum over the splits, in order
-__global__ void __launch_bounds__(256) k_mix_reduce(int64_t n, int32_t nsplit, const double* __restrict__ part,
+// dWmix[p][u][w] = sum of path p's runs, in order
+__global__ void __launch_bounds__(256) k_mix_reduce(MixShape m, MixSplit sp, const double* __restrict__ part,
                                                     float* __restrict__ dW)
 {
+    const int64_t n = (int64_t)m.C * m.Co;
     const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (q >= n) return;
+    if (q >= (int64_t)m.P * n) return;
+    const int32_t p = (int32_t)(q / n);
+    const int64_t r = q - (int64_t)p * n;
     double v = 0.0;
-    for (int32_t sp = 0; sp < nsplit; ++sp) v += part[(int64_t)sp * n + q];
+    for (int32_t g = sp.off[p]; g < sp.off[p + 1]; ++g) v += part[(int64_t)g * n + r];
     dW[q] = (float)v;
 }
 
@@ -278,30 +286,29 @@ inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b);
 
 }  // namespace
 
-// Node-range splits of the weight gradient: about four blocks per compute
-// unit over the tiles of every path, at least two chunks of nodes per split
-// (fewer splits write fewer fp64 partials) and at most 256 splits.
-int32_t mix_splits(int64_t N, int32_t P, int32_t C, int32_t Co)
+// Runs of the weight gradient: about four blocks per compute unit over the
+// output tiles, the (m, node) pairs of all paths cut into runs of equal length
+// (a whole number of chunks, at least two), so every block has the same work.
+MixSplit mix_split(const MixShape& m)
 {
-    const int64_t tiles = (int64_t)P * ((C + kTM - 1) / kTM) * ((Co + kTN - 1) / kTN);
-    int64_t n = (1024 + tiles - 1) / (tiles > 0 ? tiles : 1);
-    const int64_t by_nodes = (N + 2 * kTK - 1) / (2 * kTK);
-    if (n > by_nodes) n = by_nodes;
-    if (n > 256) n = 256;
-    return (int32_t)(n < 1 ? 1 : n);
+    MixSplit sp{};
+    const int64_t tiles = (int64_t)((m.C + kTM - 1) / kTM) * ((m.Co + kTN - 1) / kTN);
+    int64_t pairs = 0;
+    for (int p = 0; p < m.P; ++p) pairs += (int64_t)m.N * (2 * m.l3[p] + 1);
+    const int64_t target = (1024 + tiles - 1) / (tiles > 0 ? tiles : 1);
+    int64_t rows = (pairs + target - 1) / target;
+    rows = (rows + kTK - 1) / kTK * kTK;
+    if (rows < 2 * kTK) rows = 2 * kTK;
+    sp.rows = (int32_t)rows;
+    sp.off[0] = 0;
+    for (int p = 0; p < m.P; ++p)
+        sp.off[p + 1] = sp.off[p] + (int32_t)(((int64_t)m.N * (2 * m.l3[p] + 1) + rows - 1) / rows);
+    return sp;
 }
 
-// nodes per split: a whole number of chunks
-static int32_t mix_split_nodes(int64_t N, int32_t nsplit)
+size_t mix_workspace_bytes(const MixShape& m)
 {
-    const int64_t per = (N + nsplit - 1) / nsplit;
-    const int64_t r = (per + kTK - 1) / kTK * kTK;
-    return (int32_t)(r > 0 ? r : kTK);
-}
-
-size_t mix_workspace_bytes(int64_t N, int32_t P, int32_t C, int32_t Co)
-{
-    return sizeof(double) * (size_t)mix_splits(N, P, C, Co) * (size_t)P * (size_t)C * (size_t)Co;
+    return sizeof(double) * (size_t)mix_split(m).off[m.P] * (size_t)m.C * (size_t)m.Co;
 }
 
 // 16-byte operand loads need rows of a multiple of four floats (the entry
@@ -335,14 +342,13 @@ hipError_t launch_mix_bwd(const MixShape& m, const float* mid, const float* Wmix
         if (e != hipSuccess) return e;
     }
     if (dW) {
-        const int32_t nsplit = mix_splits(m.N, m.P, m.C, m.Co);
-        const int32_t chunk = mix_split_nodes(m.N, nsplit);
-        hipLaunchKernelGGL(k_mix_bwd_weight, dim3(cdiv(m.C, kTM), cdiv(m.Co, kTN), (unsigned)(m.P * nsplit)),
-                           dim3(256), 0, s, m, vec_ok(m), nsplit, chunk, mid, G, part);
+        const MixSplit sp = mix_split(m);
+        hipLaunchKernelGGL(k_mix_bwd_weight, dim3(cdiv(m.C, kTM), cdiv(m.Co, kTN), (unsigned)sp.off[m.P]),
+                           dim3(256), 0, s, m, sp, vec_ok(m), mid, G, part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t n = (int64_t)m.P * m.C * m.Co;
-        hipLaunchKernelGGL(k_mix_reduce, dim3(cdiv(n, 256)), dim3(256), 0, s, n, nsplit, part, dW);
+        hipLaunchKernelGGL(k_mix_reduce, dim3(cdiv(n, 256)), dim3(256), 0, s, m, sp, part, dW);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

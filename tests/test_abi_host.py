@@ -199,9 +199,11 @@ def test_path_mix_arguments_without_a_gpu(L):
     assert lib.cgtp_path_mix_workspace_size(plan._h, 1000, 0, ctypes.byref(b)) == L.CGTP_ERR_INVALID_ARG
     assert lib.cgtp_path_mix_workspace_size(plan._h, 1000, 1025, ctypes.byref(b)) == L.CGTP_ERR_UNSUPPORTED
     assert lib.cgtp_path_mix_workspace_size(plan._h, 1000, 128, ctypes.byref(b)) == L.CGTP_OK
-    # fp64 partials of the node-range splits: 15 paths x 1 x 2 tiles -> ceil(1024 / 30) = 35 splits,
-    # capped by ceil(1000 / 64) = 16 (two 32-node chunks per split at least)
-    assert b.value == 8 * 16 * 15 * 64 * 128
+    # fp64 partials of the weight gradient's runs: 1 x 2 output tiles -> 512 runs wanted over the
+    # 1000 x 51 (component, node) pairs -> runs of ceil(100 / 32) * 32 = 128 pairs; the 3, 6 and 6
+    # paths of l3 = 0, 1, 2 take 8, 24 and 40 runs each: 408 runs of [64][128] doubles
+    assert b.value == 8 * 408 * 64 * 128
+    assert lib.cgtp_path_mix_workspace_size(plan._h, 2**31 - 1, 128, ctypes.byref(b)) == L.CGTP_ERR_INVALID_ARG
     assert lib.cgtp_path_mix_fwd(None, 10, 8, fake, fake, fake, None) == L.CGTP_ERR_INVALID_ARG
     assert lib.cgtp_path_mix_fwd(plan._h, 10, 8, odd, fake, fake, None) == L.CGTP_ERR_INVALID_ARG
     assert lib.cgtp_path_mix_fwd(plan._h, 10, 2000, fake, fake, fake, None) == L.CGTP_ERR_UNSUPPORTED
