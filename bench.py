@@ -37,8 +37,8 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0
 PEAK_FP64_TFLOPS = 78.6
-KERNEL_SOURCES = ["clebsch_gordan_tensor_cgtp_amd/csrc/cgtp_kernels.h",
-                  "clebsch_gordan_tensor_cgtp_amd/csrc/cgtp_math.h"]
+KERNEL_SOURCES = ["clebsch_gordan_tensor_cgtp_amd/csrc/cgtp_kernels.h", "clebsch_gordan_tensor_cgtp_amd/csrc/cgtp_math.h",
+                  "clebsch_gordan_tensor_cgtp_amd/csrc/cgtp_sh.h"]
 HEADLINE = "layer"
 OTHERS = ["large", "dense", "high_l"]
 
@@ -567,7 +567,7 @@ def summarize(d, workload):
                  f"hbm_bytes_per_launch = {rd + wr:.0f}",
                  f"algorithmic_bytes_per_launch = {alg}", f"traffic_over_algorithmic = {(rd + wr) / alg:.3f}"]
         lines += [f"kernel_source_sha = {sha}",
-                  "# kernel_source_sha: first 16 hex digits of sha256 over cgtp_kernels.h + cgtp_math.h;",
+                  "# kernel_source_sha: first 16 hex digits of sha256 over cgtp_kernels.h + cgtp_math.h + cgtp_sh.h;",
                   "# bench.py reports traffic only while the sources still hash to this value"]
         open(os.path.join(out, f"pmc_{kern}_{workload}.txt"), "w").write("\n".join(lines) + "\n")
     # instruction issue (SQ) counters

@@ -47,6 +47,8 @@ SIGNATURES = {
                                      _vp]),
     "cgtp_conv_bwd": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, ctypes.c_size_t, _vp]),
+    "cgtp_conv_fwd_sh": (ctypes.c_int, [_vp, _c_i64, _c_i64] + [_vp] * 7 + [ctypes.c_size_t, _vp]),
+    "cgtp_conv_bwd_sh": (ctypes.c_int, [_vp, _c_i64, _c_i64] + [_vp] * 10 + [ctypes.c_size_t, _vp]),
     "cgtp_conv_bwd_bwd": (ctypes.c_int, [_vp, _c_i64, _c_i64] + [_vp] * 14 + [ctypes.c_size_t, _vp]),
     "cgtp_path_mix_workspace_size": (ctypes.c_int, [_vp, _c_i64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
     "cgtp_path_mix_fwd": (ctypes.c_int, [_vp, _c_i64, ctypes.c_int, _vp, _vp, _vp, _vp]),

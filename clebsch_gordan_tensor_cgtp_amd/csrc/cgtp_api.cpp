@@ -393,6 +393,68 @@ cgtp_status_t cgtp_conv_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
     return hip_status(plan->ks->bwd[plan->sub ? 1 : 0](a, stream));
 }
 
+cgtp_status_t cgtp_conv_fwd_sh(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
+                               const int32_t* src, const float* x, const float* r, const float* W, float* out,
+                               void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    cgtp_status_t st = check_graph_args(plan, n_nodes, n_edges, row_ptr, src);
+    if (st != CGTP_OK) return st;
+    if (plan->mid) return CGTP_ERR_UNSUPPORTED;
+    st = check_ws(n_nodes, n_edges, ws, ws_bytes);
+    if (st != CGTP_OK) return st;
+    if (n_nodes == 0) return CGTP_OK;
+    if (!out || !aligned16(out) || !x || !aligned16(x)) return CGTP_ERR_INVALID_ARG;
+    if (n_edges > 0 && (!r || !W || !aligned16(W) || !aligned16(r))) return CGTP_ERR_INVALID_ARG;
+    st = ensure_prepared(plan, n_nodes, n_edges, row_ptr, src, ws, stream);
+    if (st != CGTP_OK) return st;
+    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges);
+    cgtp::FwdArgs a{};
+    a.sh = launch_shape(plan, n_nodes, n_edges);
+    a.row_ptr = row_ptr;
+    a.src = src;
+    a.rorder = (const int32_t*)((const char*)ws + L.rorder);
+    a.x = x;
+    a.r = r;
+    a.W = W;
+    a.out = out;
+    return hip_status(plan->ks->fwd_sh[plan->sub ? 1 : 0](a, stream));
+}
+
+cgtp_status_t cgtp_conv_bwd_sh(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
+                               const int32_t* src, const float* x, const float* r, const float* W,
+                               const float* grad_out, float* grad_x, float* grad_W, float* grad_r, void* ws,
+                               size_t ws_bytes, hipStream_t stream)
+{
+    cgtp_status_t st = check_graph_args(plan, n_nodes, n_edges, row_ptr, src);
+    if (st != CGTP_OK) return st;
+    if (plan->mid) return CGTP_ERR_UNSUPPORTED;
+    st = check_ws(n_nodes, n_edges, ws, ws_bytes);
+    if (st != CGTP_OK) return st;
+    if ((!grad_x && !grad_W && !grad_r) || n_nodes == 0) return CGTP_OK;
+    if (!x || !aligned16(x) || !grad_out || !aligned16(grad_out)) return CGTP_ERR_INVALID_ARG;
+    if (grad_x && !aligned16(grad_x)) return CGTP_ERR_INVALID_ARG;
+    if (n_edges > 0 && (!r || !W || !aligned16(W) || !aligned16(r))) return CGTP_ERR_INVALID_ARG;
+    if (grad_W && !aligned16(grad_W)) return CGTP_ERR_INVALID_ARG;
+    if (grad_r && !aligned16(grad_r)) return CGTP_ERR_INVALID_ARG;
+    st = ensure_prepared(plan, n_nodes, n_edges, row_ptr, src, ws, stream);
+    if (st != CGTP_OK) return st;
+    const cgtp::WsLayout L = cgtp::ws_layout(n_nodes, n_edges);
+    const char* base = (const char*)ws;
+    cgtp::BwdArgs a{};
+    a.sh = launch_shape(plan, n_nodes, n_edges);
+    a.g = cgtp::GraphView{(const int32_t*)(base + L.srow), (const int32_t*)(base + L.perm),
+                          (const int32_t*)(base + L.sdst), (const int32_t*)(base + L.rorder),
+                          (const int32_t*)(base + L.sorder)};
+    a.x = x;
+    a.r = r;
+    a.W = W;
+    a.G = grad_out;
+    a.dx = grad_x;
+    a.dW = grad_W;
+    a.dr = grad_r;
+    return hip_status(plan->ks->bwd_sh[plan->sub ? 1 : 0](a, stream));
+}
+
 cgtp_status_t cgtp_conv_bwd_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
                                 const int32_t* src, const float* x, const float* Y, const float* W,
                                 const float* grad_out, const float* gg_x, const float* gg_Y, const float* gg_W,

@@ -12,6 +12,7 @@
 
 #include "cgtp_internal.h"
 #include "cgtp_math.h"
+#include "cgtp_sh.h"
 
 namespace cgtp {
 
@@ -35,48 +36,20 @@ __global__ void __launch_bounds__(256) k_sh_bwd(int64_t E, const float* __restri
     constexpr int D = (L + 1) * (L + 1);
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= E) return;
-    const double rx = r[3 * e + 0], ry = r[3 * e + 1], rz = r[3 * e + 2];
-    const double inv = 1.0 / sqrt(rx * rx + ry * ry + rz * rz);
-    const double x = rx * inv, y = ry * inv, z = rz * inv;
+    double x, y, z, inv;
+    shf::unit(r[3 * e + 0], r[3 * e + 1], r[3 * e + 2], x, y, z, inv);
     double w[D];
 #pragma unroll
     for (int k = 0; k < D; ++k) w[k] = (double)gY[e * D + k];
-    constexpr double pi = 3.14159265358979323846;
     double qx = 0.0, qy = 0.0, qz = 0.0;
-    if constexpr (L >= 1) {
-        // sqrt(3/4pi) (y, z, x)
-        constexpr double c = cgmath::csqrt(3.0 / (4.0 * pi));
-        qx = c * w[3];
-        qy = c * w[1];
-        qz = c * w[2];
-    }
-    if constexpr (L >= 2) {
-        constexpr double s15 = cgmath::csqrt(15.0 / pi), s5 = cgmath::csqrt(5.0 / pi);
-        // components 4..8: s15/2 xy, s15/2 yz, s5/4 (3z^2-1), s15/2 xz, s15/4 (x^2-y^2)
-        const double h = 0.5 * s15;
-        qx += h * (w[4] * y + w[7] * z + w[8] * x);
-        qy += h * (w[4] * x + w[5] * z - w[8] * y);
-        qz += h * (w[5] * y + w[7] * x) + 1.5 * s5 * w[6] * z;
-    }
-    if constexpr (L >= 3) {
-        constexpr double k9 = 0.25 * cgmath::csqrt(35.0 / (2.0 * pi));   // y(3x^2-y^2), x(x^2-3y^2)
-        constexpr double k10 = 0.5 * cgmath::csqrt(105.0 / pi);          // xyz
-        constexpr double k11 = 0.25 * cgmath::csqrt(21.0 / (2.0 * pi));  // y(5z^2-1), x(5z^2-1)
-        constexpr double k12 = 0.25 * cgmath::csqrt(7.0 / pi);           // 5z^3-3z
-        constexpr double k14 = 0.25 * cgmath::csqrt(105.0 / pi);         // z(x^2-y^2)
-        const double xx = x * x, yy = y * y, zz = z * z;
-        const double t = 5.0 * zz - 1.0;
-        qx += k9 * (6.0 * x * y * w[9] + 3.0 * (xx - yy) * w[15]) + k10 * y * z * w[10] + k11 * t * w[13] +
-              k14 * 2.0 * x * z * w[14];
-        qy += k9 * (3.0 * (xx - yy) * w[9] - 6.0 * x * y * w[15]) + k10 * x * z * w[10] + k11 * t * w[11] -
-              k14 * 2.0 * y * z * w[14];
-        qz += k10 * x * y * w[10] + k11 * 10.0 * z * (y * w[11] + x * w[13]) + k12 * (15.0 * zz - 3.0) * w[12] +
-              k14 * (xx - yy) * w[14];
-    }
-    const double uq = x * qx + y * qy + z * qz;
-    gr[3 * e + 0] = (float)((qx - x * uq) * inv);
-    gr[3 * e + 1] = (float)((qy - y * uq) * inv);
-    gr[3 * e + 2] = (float)((qz - z * uq) * inv);
+    if constexpr (L >= 1) shf::grad_degree<1>(x, y, z, w + 1, qx, qy, qz);
+    if constexpr (L >= 2) shf::grad_degree<2>(x, y, z, w + 4, qx, qy, qz);
+    if constexpr (L >= 3) shf::grad_degree<3>(x, y, z, w + 9, qx, qy, qz);
+    double g[3];
+    shf::tangent(x, y, z, inv, qx, qy, qz, g);
+    gr[3 * e + 0] = (float)g[0];
+    gr[3 * e + 1] = (float)g[1];
+    gr[3 * e + 2] = (float)g[2];
 }
 
 template <int L>

@@ -116,6 +116,7 @@ struct FwdArgs {
     const float* ggx;
     const float* ggY;
     const float* ggW;
+    const float* r;  // edge vectors [E][3] of the fused-SH kernels (Y is then unused)
 };
 
 struct BwdArgs {
@@ -131,6 +132,8 @@ struct BwdArgs {
     const float* ggx;
     const float* ggY;
     const float* ggW;
+    const float* r;  // edge vectors [E][3] of the fused-SH kernels (Y, dY are then unused)
+    float* dr;       // their gradient [E][3]
 };
 
 using ShLaunch = hipError_t (*)(int64_t E, const float* r, float* Y, hipStream_t s);
@@ -154,6 +157,11 @@ struct KernelSet {
     // of grad_out
     FwdLaunch fwd_mid;
     BwdLaunch bwd_mid;
+    // spherical harmonics evaluated inside the kernels from the edge vectors r
+    // ([0] complete degree set, [1] SUB): fwd_sh reads r instead of Y, bwd_sh
+    // writes grad_r (through the SH Jacobian) instead of grad_Y
+    FwdLaunch fwd_sh[2];
+    BwdLaunch bwd_sh[2];
 };
 
 // Kernels for compiled degree lm and channel count C, or nullptr.

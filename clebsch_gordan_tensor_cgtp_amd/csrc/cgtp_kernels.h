@@ -53,6 +53,7 @@
 
 #include "cgtp_internal.h"
 #include "cgtp_math.h"
+#include "cgtp_sh.h"
 
 namespace cgtp {
 
@@ -150,42 +151,8 @@ __global__ void __launch_bounds__(256) k_sh(int64_t E, const float* __restrict__
     if (e >= E) return;
     const double rx = r[3 * e + 0], ry = r[3 * e + 1], rz = r[3 * e + 2];
     const double n = sqrt(rx * rx + ry * ry + rz * rz);
-    const double x = rx / n, y = ry / n, z = rz / n;
-    (void)x, (void)y, (void)z;
-    constexpr double pi = 3.14159265358979323846;
-    constexpr double c0 = 0.5 * cgmath::csqrt(1.0 / pi);
     double o[D];
-    o[0] = c0;
-    if constexpr (L >= 1) {
-        constexpr double c1 = cgmath::csqrt(3.0 / (4.0 * pi));
-        o[1] = c1 * y;
-        o[2] = c1 * z;
-        o[3] = c1 * x;
-    }
-    if constexpr (L >= 2) {
-        constexpr double a = 0.5 * cgmath::csqrt(15.0 / pi);
-        constexpr double b = 0.25 * cgmath::csqrt(5.0 / pi);
-        constexpr double c = 0.25 * cgmath::csqrt(15.0 / pi);
-        o[4] = a * x * y;
-        o[5] = a * y * z;
-        o[6] = b * (3.0 * z * z - 1.0);
-        o[7] = a * x * z;
-        o[8] = c * (x * x - y * y);
-    }
-    if constexpr (L >= 3) {
-        constexpr double a = 0.25 * cgmath::csqrt(35.0 / (2.0 * pi));
-        constexpr double b = 0.5 * cgmath::csqrt(105.0 / pi);
-        constexpr double c = 0.25 * cgmath::csqrt(21.0 / (2.0 * pi));
-        constexpr double d = 0.25 * cgmath::csqrt(7.0 / pi);
-        constexpr double f = 0.25 * cgmath::csqrt(105.0 / pi);
-        o[9] = a * y * (3.0 * x * x - y * y);
-        o[10] = b * x * y * z;
-        o[11] = c * y * (5.0 * z * z - 1.0);
-        o[12] = d * (5.0 * z * z * z - 3.0 * z);
-        o[13] = c * x * (5.0 * z * z - 1.0);
-        o[14] = f * z * (x * x - y * y);
-        o[15] = a * x * (x * x - 3.0 * y * y);
-    }
+    shf::values<L>(rx / n, ry / n, rz / n, o);
     float* out = Y + e * D;
 #pragma unroll
     for (int k = 0; k < D; ++k) out[k] = (float)o[k];
@@ -290,6 +257,38 @@ __device__ __forceinline__ void edge_sh(const float (&y)[DSH], double (&yv)[DSH]
     }
 }
 
+// the edge's spherical harmonics evaluated from its vector r (the fused-SH
+// kernels), fp64; in scalar registers when the whole wave works on one edge
+template <int LM, int DSH, int LPE>
+__device__ __forceinline__ void edge_sh_r(const float (&r)[3], double (&yv)[DSH])
+{
+    double x, y, z, inv;
+    shf::unit(r[0], r[1], r[2], x, y, z, inv);
+    shf::values<LM>(x, y, z, yv);
+    if constexpr (LPE == 64)
+#pragma unroll
+        for (int k = 0; k < DSH; ++k) yv[k] = uniform(yv[k]);
+}
+
+// grad_r = sum_k w[k] dY_k/dr of the edge vector r (degrees 0..LM), the
+// weights w[0 .. (LM+1)^2) read from LDS one degree at a time; components
+// k >= d_sh (past the plan's SH width) count as zero
+template <int LM>
+__device__ __forceinline__ void edge_r_grad(const float (&r)[3], const double* w, int32_t d_sh, double (&g)[3])
+{
+    double x, y, z, inv;
+    shf::unit(r[0], r[1], r[2], x, y, z, inv);
+    double qx = 0.0, qy = 0.0, qz = 0.0;
+    static_for<1, LM + 1>([&](auto LI) {
+        constexpr int l = decltype(LI)::value;
+        double wl[2 * l + 1];
+#pragma unroll
+        for (int b = 0; b < 2 * l + 1; ++b) wl[b] = l * l + b < d_sh ? w[l * l + b] : 0.0;
+        shf::grad_degree<l>(x, y, z, wl, qx, qy, qz);
+    });
+    shf::tangent(x, y, z, inv, qx, qy, qz, g);
+}
+
 // Row widths and weight offsets of a launch: compile-time for the complete
 // degree set, run-time (from the Shape) for a SUB plan.
 template <class Tb, bool SUB>
@@ -325,6 +324,7 @@ template <class Tb>
 struct FwdEdge {
     static constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH;
     float w[P], x[DIN], y[DSH];
+    float r[3];  // the edge vector (fused-SH kernels, which load it instead of y)
 };
 
 // operands of edge e for the lane at byte offset chl (an in-range channel
@@ -332,7 +332,7 @@ struct FwdEdge {
 // addressed as a row pointer (uniform when the whole wave works on one edge)
 // plus the lane's channel as an unsigned 32-bit index, which the compiler
 // turns into scalar-base + lane-offset loads without 64-bit vector adds.
-template <class Tb, bool SUB, bool UNI>
+template <class Tb, bool SUB, bool UNI, bool FSH = false>
 __device__ __forceinline__ void fwd_load(FwdEdge<Tb>& d, int32_t e, uint32_t chl, const FwdArgs& a,
                                          const Dims<Tb, SUB>& dm)
 {
@@ -355,8 +355,14 @@ __device__ __forceinline__ void fwd_load(FwdEdge<Tb>& d, int32_t e, uint32_t chl
     static_for<0, DIN>([&](auto K) { d.x[K] = *at_lane(xrow + Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_in) * C, chl); });
     // (the edge's SH stay vector loads here: held across the prefetch, they
     // would occupy scalar registers the contraction needs)
-    const float* yp = a.Y + (int64_t)e * dm.d_sh;
-    static_for<0, DSH>([&](auto K) { d.y[K] = yp[Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_sh)]; });
+    if constexpr (FSH) {
+        const float* rp = a.r + 3 * (int64_t)e;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) d.r[k] = rp[k];
+    } else {
+        const float* yp = a.Y + (int64_t)e * dm.d_sh;
+        static_for<0, DSH>([&](auto K) { d.y[K] = yp[Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_sh)]; });
+    }
 }
 
 // acc[l3,m3] += sum_p W_p sum_{a,b} T_p[a][b][m3] x[l1,a] y[l2,b] for one channel
@@ -478,10 +484,11 @@ __device__ __forceinline__ void fwd_slice_dbl(const FwdEdgeD<Tb>& d, const doubl
     });
 }
 
-template <int LM, int LPE, int H, bool SUB, bool DBL = false>
+template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool FSH = false>
 __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_fwd_occ : Tune<LM, LPE>::fwd_occ))
     k_conv_fwd(FwdArgs a)
 {
+    static_assert(!(DBL && FSH), "the double backward takes Y");
     using Tb = cgmath::Tables<LM, LM, LM>;
     using Gm = Geo<LPE, H>;
     constexpr int DSH = Tb::DSH, DOUT = Tb::DOUT, S = Gm::S, CP = Gm::CP;
@@ -511,19 +518,20 @@ __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_fwd_occ : Tune<
     // alternating two named buffers, which would spill at this occupancy)
     int32_t e = e0 + ps.s;
     Edge cur;
-    if (kPf && e < end) fwd_load<Tb, SUB, LPE == 64>(cur, e, chl, a, dm);
+    if (kPf && e < end) fwd_load<Tb, SUB, LPE == 64, FSH>(cur, e, chl, a, dm);
     while (e < end) {
         const int32_t en = e + S;
         Edge nxt;
         if constexpr (kPf) {
-            if (en < end) fwd_load<Tb, SUB, LPE == 64>(nxt, en, chl, a, dm);
+            if (en < end) fwd_load<Tb, SUB, LPE == 64, FSH>(nxt, en, chl, a, dm);
         } else if constexpr (DBL) {
             fwd_load_dbl<Tb, SUB, LPE == 64>(cur, e, chl, a, dm);
         } else {
-            fwd_load<Tb, SUB, LPE == 64>(cur, e, chl, a, dm);
+            fwd_load<Tb, SUB, LPE == 64, FSH>(cur, e, chl, a, dm);
         }
         double yv[DSH];
-        edge_sh<DSH, LPE>(cur.y, yv);
+        if constexpr (FSH) edge_sh_r<LM, DSH, LPE>(cur.r, yv);
+        else edge_sh<DSH, LPE>(cur.y, yv);
         if constexpr (DBL) {
             double gyv[DSH];
             edge_sh<DSH, LPE>(cur.gy, gyv);
@@ -551,11 +559,12 @@ __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_fwd_occ : Tune<
     }
 }
 
-template <int LM, int LPE, int H, bool SUB, bool DBL = false>
+template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool FSH = false>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s)
 {
     if (a.sh.N == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_conv_fwd<LM, LPE, H, SUB, DBL>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_conv_fwd<LM, LPE, H, SUB, DBL, FSH>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0, s,
+                       a);
     return hipGetLastError();
 }
 
@@ -742,13 +751,14 @@ struct BwdEdge {
     int32_t e, i;
     bool ok;  // the view entry names a valid edge and receiver
     float w[P], g[DOUT], y[DSH];
+    float r[3];  // the edge vector (fused-SH kernels, which load it instead of y)
 };
 
 // operands of the q-th edge of the sender-sorted view for the lane at byte
 // offset chl; a
 // corrupt entry (possible only if the view was not prepared for this graph)
 // is read as edge 0 / receiver 0 and flagged, never used out of bounds
-template <class Tb, bool SUB, bool UNI, bool LOADG = true>
+template <class Tb, bool SUB, bool UNI, bool LOADG = true, bool FSH = false>
 __device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, uint32_t chl, const BwdArgs& a,
                                          const Dims<Tb, SUB>& dm)
 {
@@ -775,11 +785,17 @@ __device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, uint32_t chl
         const float* grow = a.G + (int64_t)i * (dm.d_out * C);
         static_for<0, DOUT>([&](auto K) { d.g[K] = *at_lane(grow + Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_out) * C, chl); });
     }
-    const float* yp = a.Y + (int64_t)e * dm.d_sh;
-    static_for<0, DSH>([&](auto K) {
-        const float* p = yp + Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_sh);
-        d.y[K] = UNI ? scalar_load(p) : *p;
-    });
+    if constexpr (FSH) {
+        const float* rp = a.r + 3 * (int64_t)e;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) d.r[k] = UNI ? scalar_load(rp + k) : rp[k];
+    } else {
+        const float* yp = a.Y + (int64_t)e * dm.d_sh;
+        static_for<0, DSH>([&](auto K) {
+            const float* p = yp + Dims<Tb, SUB>::template comp<decltype(K)::value>(dm.d_sh);
+            d.y[K] = UNI ? scalar_load(p) : *p;
+        });
+    }
 }
 
 // One edge of the backward for one channel:
@@ -1172,10 +1188,35 @@ __device__ __forceinline__ double wave_sum_tile(const double* __restrict__ red, 
 // a C > 64 backward block.
 constexpr int kDyChunk = 64;
 
-template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool MID = false>
-__global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_bwd_occ : Tune<LM, LPE>::bwd_occ))
+// fp64 value of lane `l` of the wave (l uniform)
+__device__ __forceinline__ double readlane_d(double v, int l)
+{
+    const int lo = __builtin_amdgcn_readlane(__double2loint(v), l);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(v), l);
+    return __hiloint2double(hi, lo);
+}
+
+// With FSH (the fused-SH backward) the kernel reads the edge vectors r
+// instead of Y, evaluates the harmonics itself, and where the plain kernel
+// stores an edge's grad_Y (once it is summed over the channels) it stores
+// grad_r = sum_k grad_Y[k] dY_k/dr instead.
+// Occupancy bound of a backward specialisation.  The fused-SH backward of a
+// SUB plan at degree 2 with one full-wave slice per edge holds a few more
+// scalar values than 4 waves per SIMD leave registers for (it would spill to
+// memory), so it runs at 3.
+template <int LM, int LPE, int H, bool SUB, bool DBL, bool FSH>
+constexpr int bwd_bound()
+{
+    if (DBL) return Tune<LM, LPE>::dbl_bwd_occ;
+    if (FSH && SUB && LM == 2 && LPE == 64 && H == 1) return 3;
+    return Tune<LM, LPE>::bwd_occ;
+}
+
+template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool MID = false, bool FSH = false>
+__global__ void __launch_bounds__(256, (bwd_bound<LM, LPE, H, SUB, DBL, FSH>()))
     k_conv_bwd(BwdArgs a)
 {
+    static_assert(!(FSH && (DBL || MID)), "the fused-SH form is the plain backward's");
     using Tb = cgmath::Tables<LM, LM, LM>;
     using Gm = Geo<LPE, H>;
     constexpr int DIN = Tb::DIN, DSH = Tb::DSH, S = Gm::S, CP = Gm::CP;
@@ -1191,6 +1232,9 @@ __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_bwd_occ : Tune<
     constexpr int kLds = kMain > kDx ? kMain : kDx;
     __shared__ double lds[kLds];
     __shared__ int32_t eslot[H == 2 ? S * K : 1];
+    // FSH with LPE < 64: one grad_Y slot per edge a wave holds at a time (apart
+    // from lds: the first waves to finish write their grad_x partials there)
+    __shared__ double stage[FSH && !kTile ? 4 * (64 / LPE) * DSH : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1202,7 +1246,8 @@ __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_bwd_occ : Tune<
     // every lane of this wave holds a channel below C (uniform)
     const bool full_c = C >= (ps.h + 1) * LPE;
     const Dims<Tb, SUB> dm(a.sh);
-    const bool want_dx = a.dx != nullptr, want_dw = a.dW != nullptr, want_dy = a.dY != nullptr;
+    // want_dy: grad_Y, or with FSH grad_r
+    const bool want_dx = a.dx != nullptr, want_dw = a.dW != nullptr, want_dy = (FSH ? a.dr : a.dY) != nullptr;
     const int32_t j = a.g.sorder[blockIdx.x];
     if ((uint32_t)j >= (uint32_t)N) return;  // idle block (or an unprepared schedule)
 
@@ -1237,12 +1282,13 @@ __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_bwd_occ : Tune<
             if (q >= end) continue;  // uniform over the lanes of one edge
             Edge cur;
             if constexpr (DBL) bwd_load_dbl<Tb, SUB, LPE == 64>(cur, q, chl, a, dm);
-            else bwd_load<Tb, SUB, LPE == 64, !MID>(cur, q, chl, a, dm);
+            else bwd_load<Tb, SUB, LPE == 64, !MID, FSH>(cur, q, chl, a, dm);
             if constexpr (H == 2)
                 if (ps.h == 0 && lane == 0) eslot[ps.s * K + (t - t0)] = cur.ok ? cur.e : -1;
             if (!cur.ok) continue;
             double yv[DSH];
-            edge_sh<DSH, LPE>(cur.y, yv);
+            if constexpr (FSH) edge_sh_r<LM, DSH, LPE>(cur.r, yv);
+            else edge_sh<DSH, LPE>(cur.y, yv);
             double gyv[DBL ? DSH : 1];
             if constexpr (DBL) edge_sh<DSH, LPE>(cur.gy, gyv);
             // the edge's contraction (the backward's, or the double backward's)
@@ -1295,14 +1341,48 @@ __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_bwd_occ : Tune<
                 const int k = lane >> 2;
                 if ((lane & 3) == 0 && k < DSH) {
                     if constexpr (H == 1) {
-                        if (want_dy && k < dm.d_sh) a.dY[(int64_t)cur.e * dm.d_sh + k] = (float)s;
+                        if constexpr (!FSH)
+                            if (want_dy && k < dm.d_sh) a.dY[(int64_t)cur.e * dm.d_sh + k] = (float)s;
                     } else {
                         dyl[((ps.h * S + ps.s) * K + (t - t0)) * DSH + k] = s;
+                    }
+                }
+                if constexpr (FSH && H == 1) {
+                    // component k's sum sits in lane 4k: read degree by degree
+                    // (uniform) straight into the SH Jacobian
+                    if (want_dy) {
+                        // r again (cached) rather than held through the contraction
+                        const float* rp = a.r + 3 * (int64_t)cur.e;
+                        double x, y, z, inv;
+                        shf::unit(scalar_load(rp), scalar_load(rp + 1), scalar_load(rp + 2), x, y, z, inv);
+                        double qx = 0.0, qy = 0.0, qz = 0.0;
+                        static_for<1, LM + 1>([&](auto LI) {
+                            constexpr int l = decltype(LI)::value;
+                            double wl[2 * l + 1];
+                            static_for<0, 2 * l + 1>([&](auto B) {
+                                constexpr int kk = l * l + decltype(B)::value;
+                                const double v = readlane_d(s, 4 * kk);
+                                wl[decltype(B)::value] = kk < dm.d_sh ? v : 0.0;
+                            });
+                            shf::grad_degree<l>(x, y, z, wl, qx, qy, qz);
+                        });
+                        double g[3];
+                        shf::tangent(x, y, z, inv, qx, qy, qz, g);
+                        if (lane == 0) {
+                            float* o = a.dr + 3 * (int64_t)cur.e;
+                            o[0] = (float)g[0];
+                            o[1] = (float)g[1];
+                            o[2] = (float)g[2];
+                        }
                     }
                 }
             } else {
                 // an edge spans LPE < 64 lanes: reduce each degree's partials over them
                 float* yp = a.dY + (int64_t)cur.e * dm.d_sh;
+                // FSH: the first lane of the edge keeps each degree's summed
+                // grad_Y in its own LDS slot until the edge is done (it alone
+                // writes and reads the slot), then applies the SH Jacobian
+                double* slot = stage + ((tid >> 6) * (64 / LPE) + (lane / LPE)) * DSH;
                 slice(store_w, [&](auto K2, const auto& dyb) {
                     constexpr int k2 = decltype(K2)::value;
 #pragma unroll
@@ -1310,13 +1390,55 @@ __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_bwd_occ : Tune<
                         double v = (full_c || live) ? dyb[b] : 0.0;  // lanes past C leave the sum
 #pragma unroll
                         for (int off = 1; off < LPE; off <<= 1) v += __shfl_xor(v, off, 64);
-                        if (want_dy && ps.cl == 0 && k2 + b < dm.d_sh) yp[k2 + b] = (float)v;
+                        if constexpr (FSH) {
+                            if (ps.cl == 0) slot[k2 + b] = v;
+                        } else if (want_dy && ps.cl == 0 && k2 + b < dm.d_sh) {
+                            yp[k2 + b] = (float)v;
+                        }
                     }
                 });
                 store_shared();
+                if constexpr (FSH) {
+                    if (want_dy && ps.cl == 0) {
+                        // r again (cached) rather than held through the contraction
+                        const float* rp = a.r + 3 * (int64_t)cur.e;
+                        const float rv[3] = {rp[0], rp[1], rp[2]};
+                        double g[3];
+                        edge_r_grad<LM>(rv, slot, dm.d_sh, g);
+                        float* o = a.dr + 3 * (int64_t)cur.e;
+                        o[0] = (float)g[0];
+                        o[1] = (float)g[1];
+                        o[2] = (float)g[2];
+                    }
+                }
             }
         }
-        if constexpr (H == 2) {
+        if constexpr (H == 2 && FSH) {
+            // grad_r of the chunk's edges: grad_Y is the two slices' sums, added
+            // in a fixed order, then the SH Jacobian (one thread per edge)
+            __syncthreads();
+            if (want_dy)
+                for (int idx = tid; idx < S * K; idx += 256) {
+                    const int s = idx / K, tt = idx % K;
+                    const int32_t t = t0 + tt;
+                    if (t >= t1 || q0 + s + S * t >= end) continue;
+                    const int32_t e = eslot[s * K + tt];
+                    if (e < 0) continue;
+                    // the two slices' sums, into the first slice's entries
+                    double* w = dyl + ((0 * S + s) * K + tt) * DSH;
+#pragma unroll
+                    for (int k = 0; k < DSH; ++k) w[k] += dyl[((1 * S + s) * K + tt) * DSH + k];
+                    const float* rp = a.r + 3 * (int64_t)e;
+                    const float rv[3] = {rp[0], rp[1], rp[2]};
+                    double g[3];
+                    edge_r_grad<LM>(rv, w, dm.d_sh, g);
+                    float* o = a.dr + 3 * (int64_t)e;
+                    o[0] = (float)g[0];
+                    o[1] = (float)g[1];
+                    o[2] = (float)g[2];
+                }
+            __syncthreads();
+        } else if constexpr (H == 2) {
             // grad_Y of the chunk's edges: the two slices' sums, added in a fixed order
             __syncthreads();
             if (want_dy)
@@ -1351,12 +1473,12 @@ __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_bwd_occ : Tune<
     }
 }
 
-template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool MID = false>
+template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool MID = false, bool FSH = false>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s)
 {
     if (a.sh.N == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_conv_bwd<LM, LPE, H, SUB, DBL, MID>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0, s,
-                       a);
+    hipLaunchKernelGGL((k_conv_bwd<LM, LPE, H, SUB, DBL, MID, FSH>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0,
+                       s, a);
     return hipGetLastError();
 }
 
@@ -1371,7 +1493,10 @@ constexpr KernelSet make_set()
                      &launch_fwd<LM, LPE, H, true, true>,
                      &launch_bwd<LM, LPE, H, true, true>,
                      &launch_fwd_mid<LM, LPE, H>,
-                     &launch_bwd<LM, LPE, H, true, false, true>};
+                     &launch_bwd<LM, LPE, H, true, false, true>,
+                     {&launch_fwd<LM, LPE, H, false, false, true>, &launch_fwd<LM, LPE, H, true, false, true>},
+                     {&launch_bwd<LM, LPE, H, false, false, false, true>,
+                      &launch_bwd<LM, LPE, H, true, false, false, true>}};
 }
 
 template <int LM>

@@ -192,6 +192,42 @@ class Plan:
             _ptr(grad_x), _ptr(grad_W), _ptr(grad_Y), _ptr(ws), ws.numel(), _stream(dev)))
         return grad_x, grad_W, grad_Y
 
+    def conv_fwd_sh(self, row_ptr, src, x, r, W, ws=None, out=None) -> torch.Tensor:
+        """conv_fwd with the spherical harmonics evaluated inside the kernel
+        from the edge vectors r [E][3] (fp64, not rounded to fp32)."""
+        N, E, C, dev = row_ptr.shape[0] - 1, src.shape[0], self.channels, row_ptr.device
+        _need(row_ptr, "row_ptr", torch.int32)
+        _need(src, "src", torch.int32, (E,), dev)
+        _need(x, "x", torch.float32, (N, self.dim_in, C), dev)
+        _need(r, "r", torch.float32, (E, 3), dev)
+        _need(W, "W", torch.float32, (E, self.weight_rows, C), dev)
+        ws = self._workspace(ws, row_ptr, src)
+        if out is None:
+            out = torch.empty((N, self.dim_out, C), dtype=torch.float32, device=dev)
+        _need(out, "out", torch.float32, (N, self.dim_out, C), dev)
+        L.check("cgtp_conv_fwd_sh", L.lib().cgtp_conv_fwd_sh(
+            self._h, N, E, _ptr(row_ptr), _ptr(src), _ptr(x), _ptr(r), _ptr(W), _ptr(out), _ptr(ws),
+            ws.numel(), _stream(dev)))
+        return out
+
+    def conv_bwd_sh(self, row_ptr, src, x, r, W, grad_out, ws=None, want=("dx", "dW", "dr")):
+        """(grad_x, grad_W, grad_r) of <grad_out, conv_fwd_sh(x, r, W)>; grad_r
+        [E][3] is the SH backward of the grad_Y conv_bwd would return."""
+        N, E, C, dev = row_ptr.shape[0] - 1, src.shape[0], self.channels, row_ptr.device
+        _need(row_ptr, "row_ptr", torch.int32)
+        _need(src, "src", torch.int32, (E,), dev)
+        _need(x, "x", torch.float32, (N, self.dim_in, C), dev)
+        _need(r, "r", torch.float32, (E, 3), dev)
+        _need(W, "W", torch.float32, (E, self.weight_rows, C), dev)
+        _need(grad_out, "grad_out", torch.float32, (N, self.dim_out, C), dev)
+        ws = self._workspace(ws, row_ptr, src)
+        f = lambda k, s: torch.empty(s, dtype=torch.float32, device=dev) if k in want else None
+        grad_x, grad_W, grad_r = f("dx", (N, self.dim_in, C)), f("dW", (E, self.weight_rows, C)), f("dr", (E, 3))
+        L.check("cgtp_conv_bwd_sh", L.lib().cgtp_conv_bwd_sh(
+            self._h, N, E, _ptr(row_ptr), _ptr(src), _ptr(x), _ptr(r), _ptr(W), _ptr(grad_out),
+            _ptr(grad_x), _ptr(grad_W), _ptr(grad_r), _ptr(ws), ws.numel(), _stream(dev)))
+        return grad_x, grad_W, grad_r
+
     def conv_bwd_bwd(self, row_ptr, src, x, Y, W, grad_out, gg_x=None, gg_Y=None, gg_W=None, ws=None,
                      want=("x", "Y", "W", "grad_out")):
         """Double backward: the gradients (dd_x, dd_Y, dd_W, dd_out) of

@@ -196,6 +196,34 @@ cgtp_status_t cgtp_conv_bwd(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
                             const float* grad_out, float* grad_x, float* grad_W, float* grad_Y,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Forward with the spherical harmonics evaluated inside the kernel: as
+ * cgtp_conv_fwd with Y = the real SH of degrees 0..l_sh of r[e]/|r[e]|,
+ * taken from the edge vectors r [E][3] in fp64 (not rounded to fp32 as
+ * cgtp_sh_fwd's output is) instead of read from memory.  Evaluating the
+ * harmonics where they are used saves writing Y and reading it back in both
+ * passes, and (cgtp_conv_bwd_sh) writing grad_Y and reading it back for the
+ * SH backward: 4*(l_sh+1)^2 bytes per edge each.  A zero-length r[e] is a
+ * precondition violation.  Not for CGTP_FLAG_PATH_OUTPUTS plans
+ * (CGTP_ERR_UNSUPPORTED). */
+cgtp_status_t cgtp_conv_fwd_sh(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
+                               const int32_t* src, const float* x, const float* r, const float* W, float* out,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward of L = <grad_out, out> of cgtp_conv_fwd_sh, with respect to x, W
+ * and the edge vectors:
+ *   grad_x [N][(l_in+1)^2][C], grad_W [E][P][C] as cgtp_conv_bwd's,
+ *   grad_r [E][3] = sum_k grad_Y[e][k] dY_k/dr, the SH backward of
+ *                   cgtp_sh_bwd applied inside the kernel to the grad_Y that
+ *                   cgtp_conv_bwd would return (which never reaches memory);
+ *                   the per-edge gradient that cgtp_node_grad turns into
+ *                   forces (AccelNet review, Referee Report).
+ * Each may be NULL to skip it.  Same workspace, schedule and determinism as
+ * cgtp_conv_bwd; not for CGTP_FLAG_PATH_OUTPUTS plans. */
+cgtp_status_t cgtp_conv_bwd_sh(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr,
+                               const int32_t* src, const float* x, const float* r, const float* W,
+                               const float* grad_out, float* grad_x, float* grad_W, float* grad_r,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Double backward (the higher-order derivatives LunaTP's abstract names;
  * training on forces differentiates the backward once more).  With
  * (grad_x, grad_W, grad_Y) = cgtp_conv_bwd(x, Y, W, grad_out) and cotangents

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     for n in names:
         assert hasattr(L.lib(), n), n
         assert n in L.SIGNATURES, n
@@ -153,7 +153,25 @@ def test_calls_reject_bad_arguments_without_a_gpu(L):
     assert dbl(fake, fake, fake, fake, odd, None, None, fake, None, None, None) == L.CGTP_ERR_INVALID_ARG
     assert dbl(fake, fake, fake, fake, None, None, None, None, None, None, odd) == L.CGTP_ERR_INVALID_ARG
     assert dbl(fake, fake, fake, fake, fake, fake, fake, None, None, None, None) == L.CGTP_OK
+    # fused-SH forward (x, r, W, out) and backward (x, r, W, grad_out, grad_x, grad_W, grad_r)
+    fsh = lambda *p, ws_=ws, n=big: lib.cgtp_conv_fwd_sh(h, 4, 4, fake, fake, *p, ws_, n, None)
+    bsh = lambda *p, ws_=ws, n=big: lib.cgtp_conv_bwd_sh(h, 4, 4, fake, fake, *p, ws_, n, None)
+    assert fsh(fake, fake, fake, fake, ws_=None) == L.CGTP_ERR_WORKSPACE
+    assert fsh(fake, None, fake, fake) == L.CGTP_ERR_INVALID_ARG
+    assert fsh(fake, odd, fake, fake) == L.CGTP_ERR_INVALID_ARG
+    assert fsh(fake, fake, fake, None) == L.CGTP_ERR_INVALID_ARG
+    assert bsh(fake, fake, fake, fake, None, None, None) == L.CGTP_OK
+    assert bsh(fake, None, fake, fake, None, None, fake) == L.CGTP_ERR_INVALID_ARG
+    assert bsh(fake, fake, fake, fake, None, None, odd) == L.CGTP_ERR_INVALID_ARG
+    assert bsh(fake, fake, fake, fake, None, None, fake, n=16) == L.CGTP_ERR_WORKSPACE
     lib.cgtp_plan_destroy(h)
+    # per-path-output plans have no fused-SH form
+    st, hm = _create(L, 2, 2, 2, 64, L.CGTP_FLAG_PATH_OUTPUTS)
+    assert st == L.CGTP_OK
+    assert lib.cgtp_conv_fwd_sh(hm, 4, 4, fake, fake, fake, fake, fake, fake, ws, big, None) == L.CGTP_ERR_UNSUPPORTED
+    assert lib.cgtp_conv_bwd_sh(hm, 4, 4, fake, fake, fake, fake, fake, fake, fake, None, fake, ws, big,
+                                None) == L.CGTP_ERR_UNSUPPORTED
+    lib.cgtp_plan_destroy(hm)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
