@@ -218,6 +218,7 @@ def run_workload(torch, dev, key, steps, warmup, settle, locality=False, extras=
         res["cp"] = time_cp(torch, plan, stream, rp, src, x, Y, G, (16, 32, 64) if key == HEADLINE else (32,),
                             steps)
         res["path_outputs"] = time_path_outputs(torch, stream, rp, src, x, Y, W, steps)
+        res["fused_sh"] = time_fused_sh(torch, plan, stream, rp, src, x, r, Y, W, G, ws, ab, steps)
     host = None
     if key == HEADLINE:
         host = (w, g, x.cpu().numpy(), W.cpu().numpy(), G.cpu().numpy())
@@ -253,6 +254,42 @@ def time_forces(torch, plan, stream, rp, src, r, Y, ws, steps):
         ms = statistics.median(a.elapsed_time(b) for a, b in ts)
         res[name] = {"ms": ms, "alg_bytes": nbytes, "alg_gbs": nbytes / (ms * 1e-3) / 1e9}
     log(f"  forces: sh_bwd {res['sh_bwd']['ms'] * 1e3:.1f} us | node_grad {res['node_grad']['ms'] * 1e3:.1f} us")
+    return res
+
+
+def time_fused_sh(torch, plan, stream, rp, src, x, r, Y, W, G, ws, ab, steps):
+    """The convolution with the SH evaluated in the kernels: median launch
+    times of conv_fwd_sh and conv_bwd_sh (grad_x, grad_W, grad_r), and of the
+    two chains from edge vectors to grad_r (graph already prepared): unfused
+    sh -> conv_fwd -> conv_bwd -> sh_bwd, fused conv_fwd_sh -> conv_bwd_sh.
+    Algorithmic bytes: the plain kernels' with Y (4 (l_sh+1)^2 bytes per edge)
+    read as r (12 bytes), and grad_Y written as grad_r (12 bytes)."""
+    E, dsh = r.shape[0], plan.dim_sh
+    out = torch.empty((x.shape[0], plan.dim_out, x.shape[2]), device=x.device)
+    fwd_b = ab["fwd"] - E * 4 * dsh + E * 12
+    bwd_b = ab["bwd"] - E * 8 * dsh + E * 24
+
+    def unfused():
+        Yc = plan.sh(r)
+        plan.conv_fwd(rp, src, x, Yc, W, ws, out=out)
+        _, _, dYc = plan.conv_bwd(rp, src, x, Yc, W, G, ws)
+        plan.sh_bwd(r, dYc)
+
+    def fused():
+        plan.conv_fwd_sh(rp, src, x, r, W, ws, out=out)
+        plan.conv_bwd_sh(rp, src, x, r, W, G, ws)
+
+    res = {"fwd_sh_ms": _median_ms(torch, stream, lambda: plan.conv_fwd_sh(rp, src, x, r, W, ws, out=out), steps),
+           "bwd_sh_ms": _median_ms(torch, stream, lambda: plan.conv_bwd_sh(rp, src, x, r, W, G, ws), steps),
+           "chain_unfused_ms": _median_ms(torch, stream, unfused, steps),
+           "chain_fused_ms": _median_ms(torch, stream, fused, steps)}
+    res["fwd_sh_alg_gbs"] = fwd_b / (res["fwd_sh_ms"] * 1e-3) / 1e9
+    res["bwd_sh_alg_gbs"] = bwd_b / (res["bwd_sh_ms"] * 1e-3) / 1e9
+    res["alg_bytes"] = {"fwd_sh": fwd_b, "bwd_sh": bwd_b}
+    log(f"  fused SH: fwd {res['fwd_sh_ms']:.3f} ms ({res['fwd_sh_alg_gbs']:.0f} GB/s alg) | bwd "
+        f"{res['bwd_sh_ms']:.3f} ms ({res['bwd_sh_alg_gbs']:.0f} GB/s alg) | r -> grad_r chain: unfused "
+        f"{res['chain_unfused_ms']:.3f} ms, fused {res['chain_fused_ms']:.3f} ms")
+    del out
     return res
 
 
@@ -527,10 +564,10 @@ def summarize(d, workload):
     lines = [f"# rocprofv3 kernel trace of bench.py on the {workload} workload",
              f"# command (repo root): rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- {cmd}",
              "# per-dispatch durations in microseconds (end - start) over every dispatch of the run",
-             f"{'kernel':44s} {'calls':>6s} {'avg_us':>9s} {'median_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_%':>8s}"]
+             f"{'kernel':52s} {'calls':>6s} {'avg_us':>9s} {'median_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_%':>8s}"]
     tot = sum(sum(v) for v in tr.values())
     for k, v in sorted(tr.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f"{_short(k)[:44]:44s} {len(v):6d} {statistics.mean(v):9.2f} {statistics.median(v):9.2f} "
+        lines.append(f"{_short(k)[:52]:52s} {len(v):6d} {statistics.mean(v):9.2f} {statistics.median(v):9.2f} "
                      f"{min(v):9.2f} {max(v):9.2f} {100 * sum(v) / tot:8.2f}")
     lines.append(f"kernel_source_sha = {sha}")
     open(os.path.join(out, f"kernel_trace_{workload}.txt"), "w").write("\n".join(lines) + "\n")
@@ -546,9 +583,9 @@ def summarize(d, workload):
     D = (w.l_max + 1) ** 2
     alg_all = algorithmic_bytes(g.n_nodes, g.n_edges, w.num_paths, w.channels, D, D, D)
     for kern in ("conv_fwd", "conv_bwd"):
-        # the step's kernel (the double backward and the per-path outputs instantiate the
-        # same template with DBL or MID = true)
-        name = [k for k in fetch if re.search(rf"k_{kern}<\d+, \d+, \d+, (true|false), false(, false)?>", k)][0]
+        # the step's kernel (the double backward, the per-path outputs and the fused-SH
+        # forms instantiate the same template with DBL, MID or FSH = true)
+        name = [k for k in fetch if re.search(rf"k_{kern}<\d+, \d+, \d+, (true|false), false(, false){{0,2}}>", k)][0]
         fk, wk = fetch[name]["FETCH_SIZE"], write[name]["WRITE_SIZE"]
         rd, wr = fk * 1024 * ff, wk * 1024 * wf
         alg = alg_all[kern.split("_")[1]]
@@ -583,7 +620,7 @@ def summarize(d, workload):
              "# 4 * SQ_ACTIVE_INST_VALU / (gpu_cycles * 1024 SIMDs) (SQ cycle counters count 4-cycle units);",
              "# mean resident waves per SIMD = 4 * SQ_WAVE_CYCLES / (gpu_cycles * 1024)"]
     for name, c in sq.items():
-        if not re.search(r"k_conv_(fwd|bwd)<\d+, \d+, \d+, (true|false), false(, false)?>", name):
+        if not re.search(r"k_conv_(fwd|bwd)<\d+, \d+, \d+, (true|false), false(, false){0,2}>", name):
             continue
         c = dict(c)
         c.update(sq2.get(name, {}))
