@@ -161,5 +161,10 @@ def test_fused_sh_empty_graph_and_optional_outputs(torch_dev, oracle):
     x, W, G = (rng.standard_normal(s, dtype=np.float32) for s in ((70, 9, 64), (g.n_edges, 15, 64), (70, 9, 64)))
     gx, gW, gr = plan.conv_bwd_sh(T(g.row_ptr), T(g.src), T(x), T(g.r), T(W), T(G), want=("dr",))
     assert gx is None and gW is None
-    _, _, _, rdr = _reference(oracle, 2, 2, 2, g, x, W, G, False, 15)
+    _, rdx, rdW, rdr = _reference(oracle, 2, 2, 2, g, x, W, G, False, 15)
     assert_parity(gr.cpu().numpy(), rdr, "grad_r alone")
+    # grad_x and grad_W without grad_r
+    gx, gW, gr = plan.conv_bwd_sh(T(g.row_ptr), T(g.src), T(x), T(g.r), T(W), T(G), want=("dx", "dW"))
+    assert gr is None
+    assert_parity(gx.cpu().numpy(), rdx, "grad_x without grad_r")
+    assert_parity(gW.cpu().numpy(), rdW, "grad_W without grad_r")
