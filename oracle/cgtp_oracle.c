@@ -210,8 +210,8 @@ void orc_sh(int L, int64_t E, const double* r, double* Y)
  * (delta_ab - u_a u_b)/|r|, the chain rule gives dr = (g - u (u.g)) / |r|:
  * only the part of g tangent to the sphere survives, so any polynomial that
  * agrees with Y_k on the sphere gives the same result.  This is the edge
- * term of the forces the benchmark spec's backward Y term feeds (and the
- * finite-difference-validated analytic force of the AccelNet review,
+ * term of the forces that the convolution backward's grad_Y feeds (the
+ * finite-difference-validated analytic forces of the AccelNet review,
  * Referee Report). */
 void orc_sh_bwd(int L, int64_t E, const double* r, const double* dY, double* dr)
 {

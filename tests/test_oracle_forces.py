@@ -1,8 +1,8 @@
 """Pins of the oracle's spherical-harmonics backward and per-node gradient.
 
 The backward's grad_Y term feeds the forces of an interatomic potential
-(the benchmark spec names it; the AccelNet review, Referee Report, validates
-analytic forces by finite differences).  The pages give no formula, so the
+(the AccelNet review, Referee Report, validates analytic forces by finite
+differences).  The pages give no formula, so the
 pins are the mathematics: central finite differences of independently
 computed spherical harmonics (scipy's complex SH through the change of
 basis), the SH depending on the direction only (tangency, scale), rotation
