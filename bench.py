@@ -219,6 +219,7 @@ def run_workload(torch, dev, key, steps, warmup, settle, locality=False, extras=
                             steps)
         res["path_outputs"] = time_path_outputs(torch, stream, rp, src, x, Y, W, steps)
         res["fused_sh"] = time_fused_sh(torch, plan, stream, rp, src, x, r, Y, W, G, ws, ab, steps)
+        res["graph_replay"] = time_graph_replay(torch, step, ms_step, steps)
     host = None
     if key == HEADLINE:
         host = (w, g, x.cpu().numpy(), W.cpu().numpy(), G.cpu().numpy())
@@ -254,6 +255,34 @@ def time_forces(torch, plan, stream, rp, src, r, Y, ws, steps):
         ms = statistics.median(a.elapsed_time(b) for a, b in ts)
         res[name] = {"ms": ms, "alg_bytes": nbytes, "alg_gbs": nbytes / (ms * 1e-3) / 1e9}
     log(f"  forces: sh_bwd {res['sh_bwd']['ms'] * 1e3:.1f} us | node_grad {res['node_grad']['ms'] * 1e3:.1f} us")
+    return res
+
+
+def time_graph_replay(torch, step, ms_step, steps):
+    """The same step captured once in a HIP graph and replayed (the inputs
+    stay in place): ms per step over `steps` replays, HIP events on the
+    current stream, beside the eager launches' figure."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(5):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    res = {"ms_per_step": e0.elapsed_time(e1) / steps, "eager_ms_per_step": ms_step}
+    log(f"  graph replay: {res['ms_per_step']:.3f} ms per step (eager launches {ms_step:.3f} ms)")
+    del graph
     return res
 
 
