@@ -95,10 +95,11 @@ __device__ __forceinline__ void grad_degree(double x, double y, double z, const 
     }
 }
 
-// unit vector and 1/|r| of an edge vector
+// unit vector and 1/|r| of an edge vector (rsqrt: the hardware estimate and
+// one refinement, a third of the instructions of a square root and a division)
 __device__ __forceinline__ void unit(double rx, double ry, double rz, double& x, double& y, double& z, double& inv)
 {
-    inv = 1.0 / sqrt(rx * rx + ry * ry + rz * rz);
+    inv = rsqrt(rx * rx + ry * ry + rz * rz);
     x = rx * inv;
     y = ry * inv;
     z = rz * inv;
