@@ -205,20 +205,23 @@ struct Pos {
 // allocation must allow, and whether the forward loads the next edge's
 // operands before the current edge is computed.  Chosen so that no
 // specialisation spills vector registers (a spill costs far more than the
-// occupancy it buys).  From degree 2 on the forward is bound by fp64 issue,
-// and the copies that rotate a prefetched edge into place cost more than the
-// latency they hide (measured: 4% slower on the 50,000-atom layer), so only
-// degree 1 prefetches.
+// occupancy it buys), with one measured exception below.  From degree 2 on
+// the forward is bound by fp64 issue, and the copies that rotate a prefetched
+// edge into place cost more than the latency they hide (measured: 4% slower
+// on the 50,000-atom layer), so only degree 1 prefetches.
 // The double-backward kernels carry a second set of operands (the
-// cotangents) and run at lower occupancy (at degree 2 the receiver side fits
-// 3 waves per SIMD without spilling, the sender side 2).
+// cotangents) and run at lower occupancy.  At degree 2 the receiver side fits
+// 3 waves per SIMD without spilling.  The sender side needs 171 registers for
+// 2 waves; held to 3 waves it spills 12-20 bytes per lane with one 64-lane
+// slice per edge and is still 7-8% faster (2000- and 4000-atom layers), while
+// narrower slices would spill 80-100 bytes and keep 2.
 template <int LM, int LPE>
 struct Tune {
     static constexpr int fwd_occ = LM <= 2 ? 4 : 2;
     static constexpr int bwd_occ = LM == 1 || (LM == 2 && LPE == 64) ? 4 : (LM == 2 ? 3 : 2);
     static constexpr bool fwd_prefetch = LM == 1;
     static constexpr int dbl_fwd_occ = LM == 1 ? 4 : (LM == 2 ? 3 : 1);
-    static constexpr int dbl_bwd_occ = LM == 1 ? 4 : (LM == 2 ? 2 : 1);
+    static constexpr int dbl_bwd_occ = LM == 1 ? 4 : (LM == 2 ? (LPE == 64 ? 3 : 2) : 1);
 };
 
 // acc += a*b, where the first term of a sum (`started` false, known at
