@@ -531,13 +531,18 @@ def cpu_single(key, seconds=4.0):
                                 f"{dt:.1f} s"}))
 
 
-def copy_ceiling(torch, dev, nbytes=2 << 30, reps=5):
+def copy_ceiling(torch, dev, nbytes=2 << 30, reps=20, settle=1.0):
     """Best-of-`reps` rates of plain device copies of `nbytes`: the runtime's
-    device-to-device copy and an elementwise kernel, read + write bytes."""
+    device-to-device copy and an elementwise kernel, read + write bytes, each
+    after `settle` seconds of the same copy so that the clocks have settled."""
     a = torch.randn(nbytes // 4, device=dev)
     b = torch.empty_like(a)
     res = {}
     for name, fn in (("memcpy_d2d", lambda: b.copy_(a)), ("elementwise_neg", lambda: torch.neg(a, out=b))):
+        t0 = time.time()
+        while time.time() - t0 < settle:
+            fn()
+            torch.cuda.synchronize()
         best = float("inf")
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

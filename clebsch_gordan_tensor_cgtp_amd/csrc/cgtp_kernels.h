@@ -220,6 +220,7 @@ struct Tune {
     static constexpr int fwd_occ = LM <= 2 ? 4 : 2;
     static constexpr int bwd_occ = LM == 1 || (LM == 2 && LPE == 64) ? 4 : (LM == 2 ? 3 : 2);
     static constexpr bool fwd_prefetch = LM == 1;
+    static constexpr int ps_bwd_occ = 3;
     static constexpr int dbl_fwd_occ = LM == 1 ? 4 : (LM == 2 ? 3 : 1);
     static constexpr int dbl_bwd_occ = LM == 1 ? 4 : (LM == 2 ? (LPE == 64 ? 3 : 2) : 1);
 };
@@ -239,6 +240,95 @@ __device__ __forceinline__ void mac(double& acc, double a, double b, bool& start
 // they are sunk to the end of the edge and every path's intermediates stay
 // live) and to keep per-path products from being shared across paths.
 __device__ __forceinline__ void opaque(double& v) { asm volatile("" : "+v"(v)); }
+
+// ---- CG coefficients in scalar registers -----------------------------------
+// A coefficient other than an inline constant of the instruction set (+-1,
+// +-0.5, +-2, +-4) is an fp64 value the FMAs read from a scalar register
+// pair.  Left to itself the compiler materialises every distinct coefficient
+// of a kernel once, before the edge loop; at degree 3 (42 distinct
+// magnitudes) that is more scalar registers than a wave has, and the excess is
+// spilled into vector-register lanes, which costs a vector instruction per
+// read inside the loop.  Instead each path materialises its own few
+// magnitudes (at most 9 at degree 3) where it starts, two scalar moves each
+// that cannot be hoisted out of the loop: scalar issue has room here, vector
+// issue is the bound.  Signs become operand modifiers.  Up to degree 2 the
+// compiler's own placement fits the scalar registers and is kept (the extra
+// moves measured 1-2% slower in the degree-2 forward).
+constexpr double cabs(double v) { return v < 0.0 ? -v : v; }
+constexpr bool inline_coef(double m) { return m == 1.0 || m == 0.5 || m == 2.0 || m == 4.0; }
+
+template <class Tb, int p>
+struct PathMags {
+    using K = PathK<Tb, p>;
+    struct M {
+        double v[64];
+        int n;
+    };
+    static constexpr M make()
+    {
+        M m{};
+        m.n = 0;
+        for (int a = 0; a < K::d1; ++a)
+            for (int b = 0; b < K::d2; ++b)
+                for (int c = 0; c < K::d3; ++c) {
+                    const double t = cabs(K::T(a, b, c));
+                    if (t == 0.0 || inline_coef(t) || Tb::DIN < 16) continue;
+                    bool seen = false;
+                    for (int i = 0; i < m.n; ++i) seen = seen || m.v[i] == t;
+                    if (!seen) m.v[m.n++] = t;
+                }
+        return m;
+    }
+    static constexpr M mags = make();
+    static constexpr int N = mags.n;
+    static_assert(N <= 64, "distinct coefficient magnitudes of a path");
+    // slot of coefficient t, or -1 for an inline constant
+    static constexpr int slot(double t)
+    {
+        for (int i = 0; i < N; ++i)
+            if (mags.v[i] == cabs(t)) return i;
+        return -1;
+    }
+};
+
+// 32-bit value in a scalar register, defined here (never hoisted or merged)
+template <uint32_t V>
+__device__ __forceinline__ uint32_t sreg32()
+{
+    uint32_t r;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "i"(V));
+    return r;
+}
+
+// the magnitudes of path p's coefficients, in scalar registers
+template <class Tb, int p>
+struct PathCoefs {
+    using Mg = PathMags<Tb, p>;
+    double c[Mg::N > 0 ? Mg::N : 1];
+    __device__ __forceinline__ PathCoefs()
+    {
+        static_for<0, Mg::N>([&](auto I) {
+            constexpr uint64_t bits = __builtin_bit_cast(uint64_t, Mg::mags.v[decltype(I)::value]);
+            const uint32_t lo = sreg32<(uint32_t)bits>(), hi = sreg32<(uint32_t)(bits >> 32)>();
+            c[decltype(I)::value] = __hiloint2double((int)hi, (int)lo);
+        });
+    }
+    // acc += t * v for the coefficient t at (a, b, m3) of the path (the first
+    // term of a sum a plain product; see mac)
+    template <int a, int b, int m3>
+    __device__ __forceinline__ void mac(double& acc, double v, bool& started) const
+    {
+        constexpr double t = PathK<Tb, p>::T(a, b, m3);
+        constexpr int i = Mg::slot(t);
+        if constexpr (i < 0) {
+            cgtp::mac(acc, t, v, started);
+        } else if constexpr (t > 0.0) {
+            cgtp::mac(acc, c[i], v, started);
+        } else {
+            cgtp::mac(acc, -c[i], v, started);
+        }
+    }
+};
 
 // fp64 value known to be equal in every lane, moved to a scalar register pair
 __device__ __forceinline__ double uniform(double v)
@@ -380,6 +470,7 @@ __device__ __forceinline__ void fwd_slice(const float (&w)[Tb::P], const float (
         constexpr int p = decltype(PI)::value;
         using K = PathK<Tb, p>;
         const double wd = (double)w[p];
+        const PathCoefs<Tb, p> cf;
         static_for<0, K::d3>([&](auto M3) {
             constexpr int m3 = decltype(M3)::value;
             double z = 0.0;
@@ -388,7 +479,7 @@ __device__ __forceinline__ void fwd_slice(const float (&w)[Tb::P], const float (
                 static_for<0, K::d2>([&](auto B) {
                     constexpr int a = decltype(A)::value, b = decltype(B)::value;
                     constexpr double t = K::T(a, b, m3);
-                    if constexpr (t != 0.0) mac(z, t, xv[K::k1 + a] * yv[K::k2 + b], any);
+                    if constexpr (t != 0.0) cf.template mac<a, b, m3>(z, xv[K::k1 + a] * yv[K::k2 + b], any);
                 });
             });
             if (any) acc[K::k3 + m3] = __builtin_fma(wd, z, acc[K::k3 + m3]);
@@ -758,10 +849,10 @@ struct BwdEdge {
 };
 
 // operands of the q-th edge of the sender-sorted view for the lane at byte
-// offset chl; a
+// offset chl (the weights only of the paths whose l1 is in the mask L1M); a
 // corrupt entry (possible only if the view was not prepared for this graph)
 // is read as edge 0 / receiver 0 and flagged, never used out of bounds
-template <class Tb, bool SUB, bool UNI, bool LOADG = true, bool FSH = false>
+template <class Tb, bool SUB, bool UNI, bool LOADG = true, bool FSH = false, int L1M = 0xF>
 __device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, uint32_t chl, const BwdArgs& a,
                                          const Dims<Tb, SUB>& dm)
 {
@@ -777,7 +868,9 @@ __device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, uint32_t chl
     const float* wrow = a.W + (int64_t)e * (dm.P * C);
     static_for<0, P>([&](auto PI) {
         constexpr int p = decltype(PI)::value;
-        if constexpr (SUB) {
+        if constexpr (!((L1M >> Tb::data.l1[p]) & 1)) {
+            d.w[p] = 0.0f;  // another wave's path
+        } else if constexpr (SUB) {
             const float v = __builtin_nontemporal_load(at_lane(wrow + a.sh.woff[p], chl));
             d.w[p] = ((a.sh.active >> p) & 1) ? v : 0.0f;
         } else {
@@ -808,8 +901,9 @@ __device__ __forceinline__ void bwd_load(BwdEdge<Tb>& d, int32_t q, uint32_t chl
 // The paths are taken grouped by l2, so only one degree's grad_Y partials
 // are live at a time; flush_y(k2, dy) receives each degree's partials
 // (components k2 .. k2+2*l2) as soon as its last path is done.  store_w(p, v)
-// receives grad_W of path p.
-template <class Tb, class StoreW, class FlushY>
+// receives grad_W of path p.  Only the paths whose l1 is in the mask L1M are
+// taken (path-group split: the other paths belong to another wave).
+template <class Tb, int L1M = 0xF, class StoreW, class FlushY>
 __device__ __forceinline__ void bwd_slice(const float (&w)[Tb::P], const float (&g)[Tb::DOUT],
                                           const double (&yv)[Tb::DSH], const double (&xv)[Tb::DIN],
                                           double (&dxa)[Tb::DIN], StoreW&& store_w, FlushY&& flush_y)
@@ -832,9 +926,10 @@ __device__ __forceinline__ void bwd_slice(const float (&w)[Tb::P], const float (
             static_for<0, Tb::P>([&](auto PI) {
                 constexpr int p = decltype(PI)::value;
                 using K = PathK<Tb, p>;
-                if constexpr (K::l2 == l2) {
+                if constexpr (K::l2 == l2 && ((L1M >> K::l1) & 1)) {
                     const double wd = (double)w[p];
                     static_for<0, K::d3>([&](auto M3) { opaque(gv[K::k3 + decltype(M3)::value]); });
+                    const PathCoefs<Tb, p> cf;
                     double v[d2];
                     bool vs[d2];
                     static_for<0, d2>([&](auto B) {
@@ -855,7 +950,7 @@ __device__ __forceinline__ void bwd_slice(const float (&w)[Tb::P], const float (
                                 static_for<0, K::d3>([&](auto M3) {
                                     constexpr int m3 = decltype(M3)::value;
                                     constexpr double t = K::T(a, b, m3);
-                                    if constexpr (t != 0.0) mac(r, t, gv[K::k3 + m3], any);
+                                    if constexpr (t != 0.0) cf.template mac<a, b, m3>(r, gv[K::k3 + m3], any);
                                 });
                                 if (any) {
                                     mac(h, r, yv[k2 + b], hs);
@@ -1207,47 +1302,78 @@ __device__ __forceinline__ double readlane_d(double v, int l)
 // SUB plan at degree 2 with one full-wave slice per edge holds a few more
 // scalar values than 4 waves per SIMD leave registers for (it would spill to
 // memory), so it runs at 3.
-template <int LM, int LPE, int H, bool SUB, bool DBL, bool FSH>
+template <int LM, int LPE, int H, bool SUB, bool DBL, bool FSH, bool PS = false>
 constexpr int bwd_bound()
 {
+    if (PS) return Tune<LM, LPE>::ps_bwd_occ;
     if (DBL) return Tune<LM, LPE>::dbl_bwd_occ;
     if (FSH && SUB && LM == 2 && LPE == 64 && H == 1) return 3;
     return Tune<LM, LPE>::bwd_occ;
 }
 
-template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool MID = false, bool FSH = false>
-__global__ void __launch_bounds__(256, (bwd_bound<LM, LPE, H, SUB, DBL, FSH>()))
-    k_conv_bwd(BwdArgs a)
-{
-    static_assert(!(FSH && (DBL || MID)), "the fused-SH form is the plain backward's");
+// Path-group split of the backward (the path-group parallelism of the LunaTP
+// abstract): with PS the two waves of a pair serve the same edge and the same
+// 64 channels, each taking the paths of a set of input degrees l1 (l1 in
+// {1, 2} and l1 in {0, 3} at degree 3, near equal halves of the work).  A
+// wave then holds x and grad_x of its own degrees only and the weights of its
+// own paths, which roughly halves its registers and raises occupancy; the
+// two waves' grad_Y partials of an edge meet in LDS like the two channel
+// slices of a C > 64 block.  Only the degree-3 plain backward uses it.
+constexpr int kPsMask0 = 0x6, kPsMask1 = 0x9;
+
+// LDS of a backward block: per-wave grad_Y transpose tiles and, with two
+// waves per edge, the two waves' per-edge grad_Y sums of the current chunk
+// [wave of the pair][stream][edge][k] during the edge loop; the streams'
+// grad_x partials at the end
+template <int LM, int LPE, int H, bool FSH, bool PS>
+struct BwdLds {
     using Tb = cgmath::Tables<LM, LM, LM>;
-    using Gm = Geo<LPE, H>;
-    constexpr int DIN = Tb::DIN, DSH = Tb::DSH, S = Gm::S, CP = Gm::CP;
-    constexpr int K = kDyChunk;
-    // LDS: per-wave grad_Y transpose tiles and, for H = 2, the slices'
-    // per-edge grad_Y sums of the current chunk [slice][stream][edge][k]
-    // during the edge loop; the streams' grad_x partials at the end
-    constexpr bool kTile = LPE == 64;
-    constexpr int kTiles = kTile ? 4 * DSH * 64 : 0;
-    constexpr int kDyl = H == 2 ? 2 * S * K * DSH : 0;
-    constexpr int kDx = S * DIN * CP;
-    constexpr int kMain = kTiles + kDyl;
-    constexpr int kLds = kMain > kDx ? kMain : kDx;
-    __shared__ double lds[kLds];
-    __shared__ int32_t eslot[H == 2 ? S * K : 1];
+    static constexpr int HW = PS ? 2 : H;  // waves per edge
+    using Gm = Geo<LPE, HW>;
+    static constexpr int DIN = Tb::DIN, DSH = Tb::DSH, S = Gm::S;
+    static constexpr int CP = PS ? LPE : Gm::CP;  // padded channels of a node row
+    // edges per stream between two grad_Y combines of a pair (smaller with
+    // PS, so that three blocks fit a CU's LDS)
+    static constexpr int K = PS ? kDyChunk / 2 : kDyChunk;
+    static constexpr bool kTile = LPE == 64;
+    static constexpr int kTiles = kTile ? 4 * DSH * 64 : 0;
+    static constexpr int kDyl = HW == 2 ? 2 * S * K * DSH : 0;
+    static constexpr int kDx = S * DIN * CP;
+    static constexpr int kMain = kTiles + kDyl;
+    static constexpr int kLds = kMain > kDx ? kMain : kDx;
+    static constexpr int kEslot = HW == 2 ? S * K : 1;
     // FSH with LPE < 64: one grad_Y slot per edge a wave holds at a time (apart
     // from lds: the first waves to finish write their grad_x partials there)
-    __shared__ double stage[FSH && !kTile ? 4 * (64 / LPE) * DSH : 1];
+    static constexpr int kStage = FSH && !kTile ? 4 * (64 / LPE) * DSH : 1;
+};
+
+// degree l of component k (k < 16)
+constexpr int degree_of(int k) { return k < 1 ? 0 : (k < 4 ? 1 : (k < 9 ? 2 : 3)); }
+
+// The backward of one block; the paths are those whose l1 is in L1M.
+template <int LM, int LPE, int H, bool SUB, bool DBL, bool MID, bool FSH, bool PS, int L1M>
+__device__ __forceinline__ void bwd_body(const BwdArgs& a, double* __restrict__ lds, int32_t* __restrict__ eslot,
+                                         double* __restrict__ stage)
+{
+    static_assert(!(FSH && (DBL || MID)), "the fused-SH form is the plain backward's");
+    static_assert(!PS || (!SUB && !DBL && !MID && !FSH && LPE == 64 && H == 1), "path split: plain, one slice");
+    using Tb = cgmath::Tables<LM, LM, LM>;
+    using Lz = BwdLds<LM, LPE, H, FSH, PS>;
+    constexpr int HW = Lz::HW;
+    constexpr int DIN = Tb::DIN, DSH = Tb::DSH, S = Lz::S, CP = Lz::CP;
+    constexpr int K = Lz::K;
+    constexpr bool kTile = Lz::kTile;
+    constexpr int kTiles = Lz::kTiles;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const Pos<LPE, H> ps(tid);
-    const int ch = ps.channel();
+    const Pos<LPE, HW> ps(tid);
+    const int ch = PS ? ps.cl : ps.channel();
     const int32_t C = a.sh.C, N = a.sh.N, E = a.sh.E;
     const bool live = ch < C;
     const uint32_t chl = live ? 4u * ch : 0u;  // byte offset of the lane's channel
     // every lane of this wave holds a channel below C (uniform)
-    const bool full_c = C >= (ps.h + 1) * LPE;
+    const bool full_c = C >= (PS ? 1 : ps.h + 1) * LPE;
     const Dims<Tb, SUB> dm(a.sh);
     // want_dy: grad_Y, or with FSH grad_r
     const bool want_dx = a.dx != nullptr, want_dw = a.dW != nullptr, want_dy = (FSH ? a.dr : a.dY) != nullptr;
@@ -1260,8 +1386,12 @@ __global__ void __launch_bounds__(256, (bwd_bound<LM, LPE, H, SUB, DBL, FSH>()))
     {
         const float* xrow = a.x + (int64_t)j * (dm.d_in * C);
         static_for<0, DIN>([&](auto Kc) {
-            xv[Kc] = (double)*at_lane(xrow + Dims<Tb, SUB>::template comp<decltype(Kc)::value>(dm.d_in) * C, chl);
-            dxa[Kc] = 0.0;
+            constexpr int k = decltype(Kc)::value;
+            if constexpr ((L1M >> degree_of(k)) & 1)
+                xv[k] = (double)*at_lane(xrow + Dims<Tb, SUB>::template comp<k>(dm.d_in) * C, chl);
+            else
+                xv[k] = 0.0;  // another wave's degree: never read
+            dxa[k] = 0.0;
         });
         if constexpr (DBL) {
             const float* grow = a.ggx ? a.ggx + (int64_t)j * (dm.d_in * C) : nullptr;
@@ -1278,15 +1408,15 @@ __global__ void __launch_bounds__(256, (bwd_bound<LM, LPE, H, SUB, DBL, FSH>()))
     double* tile = lds + (tid >> 6) * (DSH * 64);
     double* dyl = lds + kTiles;
 
-    for (int32_t t0 = 0; t0 < T; t0 += (H == 2 ? K : T)) {
-        const int32_t t1 = H == 2 ? (t0 + K < T ? t0 + K : T) : T;
+    for (int32_t t0 = 0; t0 < T; t0 += (HW == 2 ? K : T)) {
+        const int32_t t1 = HW == 2 ? (t0 + K < T ? t0 + K : T) : T;
         for (int32_t t = t0; t < t1; ++t) {
             const int32_t q = q0 + ps.s + S * t;
             if (q >= end) continue;  // uniform over the lanes of one edge
             Edge cur;
             if constexpr (DBL) bwd_load_dbl<Tb, SUB, LPE == 64>(cur, q, chl, a, dm);
-            else bwd_load<Tb, SUB, LPE == 64, !MID, FSH>(cur, q, chl, a, dm);
-            if constexpr (H == 2)
+            else bwd_load<Tb, SUB, LPE == 64, !MID, FSH, L1M>(cur, q, chl, a, dm);
+            if constexpr (HW == 2)
                 if (ps.h == 0 && lane == 0) eslot[ps.s * K + (t - t0)] = cur.ok ? cur.e : -1;
             if (!cur.ok) continue;
             double yv[DSH];
@@ -1303,7 +1433,7 @@ __global__ void __launch_bounds__(256, (bwd_bound<LM, LPE, H, SUB, DBL, FSH>()))
                     bwd_slice_mid<Tb>(cur.w, a.G + (int64_t)cur.i * (dm.d_out * Cg), Cg, lane_offset(chl), a.sh, yv,
                                       xv, dxa, store_w, flush_y);
                 } else {
-                    bwd_slice<Tb>(cur.w, cur.g, yv, xv, dxa, store_w, flush_y);
+                    bwd_slice<Tb, L1M>(cur.w, cur.g, yv, xv, dxa, store_w, flush_y);
                 }
             };
             const int32_t Ce = edge_stride(C);
@@ -1343,14 +1473,14 @@ __global__ void __launch_bounds__(256, (bwd_bound<LM, LPE, H, SUB, DBL, FSH>()))
                 const double s = wave_sum_tile<DSH>(tile, lane);
                 const int k = lane >> 2;
                 if ((lane & 3) == 0 && k < DSH) {
-                    if constexpr (H == 1) {
+                    if constexpr (HW == 1) {
                         if constexpr (!FSH)
                             if (want_dy && k < dm.d_sh) a.dY[(int64_t)cur.e * dm.d_sh + k] = (float)s;
                     } else {
                         dyl[((ps.h * S + ps.s) * K + (t - t0)) * DSH + k] = s;
                     }
                 }
-                if constexpr (FSH && H == 1) {
+                if constexpr (FSH && HW == 1) {
                     // component k's sum sits in lane 4k: read degree by degree
                     // (uniform) straight into the SH Jacobian
                     if (want_dy) {
@@ -1416,7 +1546,7 @@ __global__ void __launch_bounds__(256, (bwd_bound<LM, LPE, H, SUB, DBL, FSH>()))
                 }
             }
         }
-        if constexpr (H == 2 && FSH) {
+        if constexpr (HW == 2 && FSH) {
             // grad_r of the chunk's edges: grad_Y is the two slices' sums, added
             // in a fixed order, then the SH Jacobian (one thread per edge)
             __syncthreads();
@@ -1441,7 +1571,7 @@ __global__ void __launch_bounds__(256, (bwd_bound<LM, LPE, H, SUB, DBL, FSH>()))
                     o[2] = (float)g[2];
                 }
             __syncthreads();
-        } else if constexpr (H == 2) {
+        } else if constexpr (HW == 2) {
             // grad_Y of the chunk's edges: the two slices' sums, added in a fixed order
             __syncthreads();
             if (want_dy)
@@ -1459,9 +1589,12 @@ __global__ void __launch_bounds__(256, (bwd_bound<LM, LPE, H, SUB, DBL, FSH>()))
     }
     if (want_dx) {
         // combine the streams in a fixed order; dx[j] has this block as its only writer
-        if constexpr (kTile && H == 1) __syncthreads();  // every wave is done with its grad_Y tile
-#pragma unroll
-        for (int k = 0; k < DIN; ++k) lds[(ps.s * DIN + k) * CP + ch] = dxa[k];
+        if constexpr (kTile && HW == 1) __syncthreads();  // every wave is done with its grad_Y tile
+        // (with the path split each wave writes the components of its degrees)
+        static_for<0, DIN>([&](auto Kc) {
+            constexpr int k = decltype(Kc)::value;
+            if constexpr ((L1M >> degree_of(k)) & 1) lds[(ps.s * DIN + k) * CP + ch] = dxa[k];
+        });
         __syncthreads();
         float* dp = a.dx + (int64_t)j * (dm.d_in * C);
         for (int t = tid; t < DIN * CP; t += 256) {
@@ -1476,12 +1609,31 @@ __global__ void __launch_bounds__(256, (bwd_bound<LM, LPE, H, SUB, DBL, FSH>()))
     }
 }
 
-template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool MID = false, bool FSH = false>
+template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool MID = false, bool FSH = false, bool PS = false>
+__global__ void __launch_bounds__(256, (bwd_bound<LM, LPE, H, SUB, DBL, FSH, PS>()))
+    k_conv_bwd(BwdArgs a)
+{
+    using Lz = BwdLds<LM, LPE, H, FSH, PS>;
+    __shared__ double lds[Lz::kLds];
+    __shared__ int32_t eslot[Lz::kEslot];
+    __shared__ double stage[Lz::kStage];
+    if constexpr (PS) {
+        // the pair's first wave (even wave index) takes the l1 = 1, 2 paths
+        if ((__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) == 0)
+            bwd_body<LM, LPE, H, SUB, DBL, MID, FSH, PS, kPsMask0>(a, lds, eslot, stage);
+        else
+            bwd_body<LM, LPE, H, SUB, DBL, MID, FSH, PS, kPsMask1>(a, lds, eslot, stage);
+    } else {
+        bwd_body<LM, LPE, H, SUB, DBL, MID, FSH, PS, 0xF>(a, lds, eslot, stage);
+    }
+}
+
+template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool MID = false, bool FSH = false, bool PS = false>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s)
 {
     if (a.sh.N == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_conv_bwd<LM, LPE, H, SUB, DBL, MID, FSH>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0,
-                       s, a);
+    hipLaunchKernelGGL((k_conv_bwd<LM, LPE, H, SUB, DBL, MID, FSH, PS>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256),
+                       0, s, a);
     return hipGetLastError();
 }
 
@@ -1492,7 +1644,8 @@ constexpr KernelSet make_set()
                      LPE,
                      H,
                      {&launch_fwd<LM, LPE, H, false>, &launch_fwd<LM, LPE, H, true>},
-                     {&launch_bwd<LM, LPE, H, false>, &launch_bwd<LM, LPE, H, true>},
+                     {&launch_bwd<LM, LPE, H, false, false, false, false, (LM == 3 && LPE == 64 && H == 1)>,
+                      &launch_bwd<LM, LPE, H, true>},
                      &launch_fwd<LM, LPE, H, true, true>,
                      &launch_bwd<LM, LPE, H, true, true>,
                      &launch_fwd_mid<LM, LPE, H>,

@@ -335,11 +335,13 @@ def test_conv_whole_tensor_parity_chunked(torch_dev, oracle, key):
         assert abs(acc.dot(t, u) - Lval) <= 1e-6 * scale, (key, name)
 
 
-def test_conv_deterministic(torch_dev, oracle):
+@pytest.mark.parametrize("key", ["layer", "high_l"])
+def test_conv_deterministic(torch_dev, oracle, key):
     """Bitwise equal results from repeated calls and from a re-prepared
-    graph (whose block placement may differ)."""
+    graph (whose block placement may differ); high_l runs the degree-3
+    backward whose two waves per edge split the paths."""
     torch, dev = torch_dev
-    run = get_run(torch_dev, "layer", oracle)
+    run = get_run(torch_dev, key, oracle)
     for k in range(3):
         ws = run.plan.graph_prepare(run.row_ptr, run.src) if k else run.ws
         out = run.plan.conv_fwd(run.row_ptr, run.src, run.x, run.Y, run.W, ws)
@@ -348,9 +350,10 @@ def test_conv_deterministic(torch_dev, oracle):
         assert torch.equal(dx, run.dx) and torch.equal(dW, run.dW) and torch.equal(dY, run.dY)
 
 
-def test_optional_gradients(torch_dev, oracle):
+@pytest.mark.parametrize("key", ["layer", "high_l"])
+def test_optional_gradients(torch_dev, oracle, key):
     torch, dev = torch_dev
-    run = get_run(torch_dev, "layer", oracle)
+    run = get_run(torch_dev, key, oracle)
     args = (run.row_ptr, run.src, run.x, run.Y, run.W, run.G, run.ws)
     for want in (("dx",), ("dW",), ("dY",), ("dx", "dY"), ("dW", "dY"), ("dx", "dW")):
         got = run.plan.conv_bwd(*args, want=want)
