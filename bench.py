@@ -579,6 +579,13 @@ def _short(name):
     return name.replace("void ", "").replace("(anonymous namespace)::", "").replace("cgtp::", "").split("(")[0]
 
 
+# the step's forward and backward kernels by name: k_conv_fwd<LM, LPE, H, SUB, DBL, FSH> and
+# k_conv_bwd<LM, LPE, H, SUB, DBL, MID, FSH, PS> with DBL, MID and FSH false (PS, the path-split
+# backward, is the degree-3 step's)
+STEP_KERNEL = {"conv_fwd": r"k_conv_fwd<\d+, \d+, \d+, (true|false), false, false>",
+               "conv_bwd": r"k_conv_bwd<\d+, \d+, \d+, (true|false), false, false, false, (true|false)>"}
+
+
 def summarize(d, workload):
     """Write profiles/{kernel_trace,pmc_conv_fwd,pmc_conv_bwd,sq}_<workload>.txt
     from the rocprofv3 output under `d` (subdirectories named as in the
@@ -619,7 +626,7 @@ def summarize(d, workload):
     for kern in ("conv_fwd", "conv_bwd"):
         # the step's kernel (the double backward, the per-path outputs and the fused-SH
         # forms instantiate the same template with DBL, MID or FSH = true)
-        name = [k for k in fetch if re.search(rf"k_{kern}<\d+, \d+, \d+, (true|false), false(, false){{0,2}}>", k)][0]
+        name = [k for k in fetch if re.search(STEP_KERNEL[kern], k)][0]
         fk, wk = fetch[name]["FETCH_SIZE"], write[name]["WRITE_SIZE"]
         rd, wr = fk * 1024 * ff, wk * 1024 * wf
         alg = alg_all[kern.split("_")[1]]
@@ -654,7 +661,7 @@ def summarize(d, workload):
              "# 4 * SQ_ACTIVE_INST_VALU / (gpu_cycles * 1024 SIMDs) (SQ cycle counters count 4-cycle units);",
              "# mean resident waves per SIMD = 4 * SQ_WAVE_CYCLES / (gpu_cycles * 1024)"]
     for name, c in sq.items():
-        if not re.search(r"k_conv_(fwd|bwd)<\d+, \d+, \d+, (true|false), false(, false){0,2}>", name):
+        if not any(re.search(p, name) for p in STEP_KERNEL.values()):
             continue
         c = dict(c)
         c.update(sq2.get(name, {}))
