@@ -221,6 +221,8 @@ struct Tune {
     static constexpr int bwd_occ = LM == 1 || (LM == 2 && LPE == 64) ? 4 : (LM == 2 ? 3 : 2);
     static constexpr bool fwd_prefetch = LM == 1;
     static constexpr int ps_bwd_occ = 3;
+    static constexpr int dbl_ps_bwd_occ = 2;
+    static constexpr int dbl_ps_fwd_occ = 2;
     static constexpr int dbl_fwd_occ = LM == 1 ? 4 : (LM == 2 ? 3 : 1);
     static constexpr int dbl_bwd_occ = LM == 1 ? 4 : (LM == 2 ? (LPE == 64 ? 3 : 2) : 1);
 };
@@ -425,7 +427,8 @@ struct FwdEdge {
 // addressed as a row pointer (uniform when the whole wave works on one edge)
 // plus the lane's channel as an unsigned 32-bit index, which the compiler
 // turns into scalar-base + lane-offset loads without 64-bit vector adds.
-template <class Tb, bool SUB, bool UNI, bool FSH = false>
+// (L3M: the weights only of the paths whose l3 is in the mask)
+template <class Tb, bool SUB, bool UNI, bool FSH = false, int L3M = 0xF>
 __device__ __forceinline__ void fwd_load(FwdEdge<Tb>& d, int32_t e, uint32_t chl, const FwdArgs& a,
                                          const Dims<Tb, SUB>& dm)
 {
@@ -437,7 +440,9 @@ __device__ __forceinline__ void fwd_load(FwdEdge<Tb>& d, int32_t e, uint32_t chl
     const float* wrow = a.W + (int64_t)e * (dm.P * C);
     static_for<0, P>([&](auto PI) {
         constexpr int p = decltype(PI)::value;
-        if constexpr (SUB) {
+        if constexpr (!((L3M >> Tb::data.l3[p]) & 1)) {
+            d.w[p] = 0.0f;  // another wave's path
+        } else if constexpr (SUB) {
             const float v = __builtin_nontemporal_load(at_lane(wrow + a.sh.woff[p], chl));
             d.w[p] = ((a.sh.active >> p) & 1) ? v : 0.0f;
         } else {
@@ -501,11 +506,11 @@ struct FwdEdgeD : FwdEdge<Tb> {
 };
 
 // the cotangent rows of edge e (zero where the caller passed none)
-template <class Tb, bool SUB, bool UNI>
+template <class Tb, bool SUB, bool UNI, int L3M = 0xF>
 __device__ __forceinline__ void fwd_load_dbl(FwdEdgeD<Tb>& d, int32_t e, uint32_t chl, const FwdArgs& a,
                                              const Dims<Tb, SUB>& dm)
 {
-    fwd_load<Tb, SUB, UNI>(d, e, chl, a, dm);
+    fwd_load<Tb, SUB, UNI, false, L3M>(d, e, chl, a, dm);
     constexpr int P = Tb::P, DIN = Tb::DIN, DSH = Tb::DSH;
     const int32_t C = edge_stride(a.sh.C);
     chl = lane_offset(chl);
@@ -515,7 +520,9 @@ __device__ __forceinline__ void fwd_load_dbl(FwdEdgeD<Tb>& d, int32_t e, uint32_
         const float* wrow = a.ggW + (int64_t)e * (dm.P * C);
         static_for<0, P>([&](auto PI) {
             constexpr int p = decltype(PI)::value;
-            if constexpr (SUB) {
+            if constexpr (!((L3M >> Tb::data.l3[p]) & 1)) {
+                d.gw[p] = 0.0f;  // another wave's path
+            } else if constexpr (SUB) {
                 const float v = __builtin_nontemporal_load(at_lane(wrow + a.sh.woff[p], chl));
                 d.gw[p] = ((a.sh.active >> p) & 1) ? v : 0.0f;
             } else {
@@ -543,7 +550,8 @@ __device__ __forceinline__ void fwd_load_dbl(FwdEdgeD<Tb>& d, int32_t e, uint32_
 }
 
 // acc[l3,m3] += sum_p sum_{a,b} T_p[a][b][m3] (W_p (ggx[a] y[b] + x[a] ggy[b]) + ggW_p x[a] y[b])
-template <class Tb>
+// over the paths whose l3 is in the mask L3M
+template <class Tb, int L3M = 0xF>
 __device__ __forceinline__ void fwd_slice_dbl(const FwdEdgeD<Tb>& d, const double (&yv)[Tb::DSH],
                                               const double (&gyv)[Tb::DSH], double (&acc)[Tb::DOUT])
 {
@@ -556,7 +564,9 @@ __device__ __forceinline__ void fwd_slice_dbl(const FwdEdgeD<Tb>& d, const doubl
     static_for<0, Tb::P>([&](auto PI) {
         constexpr int p = decltype(PI)::value;
         using K = PathK<Tb, p>;
+        if constexpr (!((L3M >> K::l3) & 1)) return;  // another wave's path
         const double wd = (double)d.w[p], gwd = (double)d.gw[p];
+        const PathCoefs<Tb, p> cf;
         static_for<0, K::d3>([&](auto M3) {
             constexpr int m3 = decltype(M3)::value;
             double z1 = 0.0, z2 = 0.0;
@@ -567,8 +577,8 @@ __device__ __forceinline__ void fwd_slice_dbl(const FwdEdgeD<Tb>& d, const doubl
                     constexpr double t = K::T(a, b, m3);
                     if constexpr (t != 0.0) {
                         const double x = xv[K::k1 + a], y = yv[K::k2 + b];
-                        mac(z1, t, __builtin_fma(x, gyv[K::k2 + b], gxv[K::k1 + a] * y), any1);
-                        mac(z2, t, x * y, any2);
+                        cf.template mac<a, b, m3>(z1, __builtin_fma(x, gyv[K::k2 + b], gxv[K::k1 + a] * y), any1);
+                        cf.template mac<a, b, m3>(z2, x * y, any2);
                     }
                 });
             });
@@ -578,22 +588,50 @@ __device__ __forceinline__ void fwd_slice_dbl(const FwdEdgeD<Tb>& d, const doubl
     });
 }
 
-template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool FSH = false>
-__global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_fwd_occ : Tune<LM, LPE>::fwd_occ))
-    k_conv_fwd(FwdArgs a)
+// the two halves of a path-group split (degree masks): l = 1, 2 and l = 0, 3
+constexpr int kPsMask0 = 0x6, kPsMask1 = 0x9;
+
+// degree l of component k (k < 16)
+constexpr int degree_of(int k) { return k < 1 ? 0 : (k < 4 ? 1 : (k < 9 ? 2 : 3)); }
+
+// Geometry of a forward block: with PS (the path-group split, see the
+// backward) two waves serve each edge and its 64 channels, one taking the
+// paths whose output degree l3 is in {1, 2}, the other those in {0, 3}; each
+// holds the accumulators of its own degrees and the weights of its own paths,
+// and every output row keeps one writer.  Used by the receiver side of the
+// degree-3 double backward with one 64-lane slice.
+template <int LM, int LPE, int H, bool PS>
+struct FwdGeo {
+    using Tb = cgmath::Tables<LM, LM, LM>;
+    static constexpr int HW = PS ? 2 : H;  // waves per edge
+    using Gm = Geo<LPE, HW>;
+    static constexpr int S = Gm::S, CP = PS ? LPE : Gm::CP, DOUT = Tb::DOUT;
+    static constexpr int kRed = S * DOUT * CP;
+};
+
+template <int LM, int LPE, bool DBL, bool PS>
+constexpr int fwd_bound()
+{
+    if (PS) return Tune<LM, LPE>::dbl_ps_fwd_occ;
+    return DBL ? Tune<LM, LPE>::dbl_fwd_occ : Tune<LM, LPE>::fwd_occ;
+}
+
+// The forward of one block over the paths whose l3 is in L3M; red: the LDS
+// of the streams' partial sums [stream][k][channel].
+template <int LM, int LPE, int H, bool SUB, bool DBL, bool FSH, bool PS, int L3M>
+__device__ __forceinline__ void fwd_body(const FwdArgs& a, double* __restrict__ red)
 {
     static_assert(!(DBL && FSH), "the double backward takes Y");
+    static_assert(!PS || (DBL && LPE == 64 && H == 1), "path split: double backward, one slice");
     using Tb = cgmath::Tables<LM, LM, LM>;
-    using Gm = Geo<LPE, H>;
-    constexpr int DSH = Tb::DSH, DOUT = Tb::DOUT, S = Gm::S, CP = Gm::CP;
+    using Fg = FwdGeo<LM, LPE, H, PS>;
+    constexpr int DSH = Tb::DSH, DOUT = Tb::DOUT, S = Fg::S, CP = Fg::CP;
     constexpr bool kPf = Tune<LM, LPE>::fwd_prefetch && !DBL;
     using Edge = std::conditional_t<DBL, FwdEdgeD<Tb>, FwdEdge<Tb>>;
-    // LDS: the streams' partial sums [stream][k][channel]
-    __shared__ double red[S * DOUT * CP];
 
     const int tid = threadIdx.x;
-    const Pos<LPE, H> ps(tid);
-    const int ch = ps.channel();
+    const Pos<LPE, Fg::HW> ps(tid);
+    const int ch = PS ? ps.cl : ps.channel();
     const int32_t C = a.sh.C;
     const uint32_t chl = ch < C ? 4u * ch : 0u;  // byte offset; lanes past C read channel 0 and store nothing
     const Dims<Tb, SUB> dm(a.sh);
@@ -619,7 +657,7 @@ __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_fwd_occ : Tune<
         if constexpr (kPf) {
             if (en < end) fwd_load<Tb, SUB, LPE == 64, FSH>(nxt, en, chl, a, dm);
         } else if constexpr (DBL) {
-            fwd_load_dbl<Tb, SUB, LPE == 64>(cur, e, chl, a, dm);
+            fwd_load_dbl<Tb, SUB, LPE == 64, L3M>(cur, e, chl, a, dm);
         } else {
             fwd_load<Tb, SUB, LPE == 64, FSH>(cur, e, chl, a, dm);
         }
@@ -629,7 +667,7 @@ __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_fwd_occ : Tune<
         if constexpr (DBL) {
             double gyv[DSH];
             edge_sh<DSH, LPE>(cur.gy, gyv);
-            fwd_slice_dbl<Tb>(cur, yv, gyv, acc);
+            fwd_slice_dbl<Tb, L3M>(cur, yv, gyv, acc);
         } else {
             fwd_slice<Tb>(cur.w, cur.x, yv, acc);
         }
@@ -638,8 +676,11 @@ __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_fwd_occ : Tune<
     }
 
     // combine the streams in a fixed order; out[i] has this block as its only writer
-#pragma unroll
-    for (int k = 0; k < DOUT; ++k) red[(ps.s * DOUT + k) * CP + ch] = acc[k];
+    // (with the path split each wave writes the components of its degrees)
+    static_for<0, DOUT>([&](auto Kc) {
+        constexpr int k = decltype(Kc)::value;
+        if constexpr ((L3M >> degree_of(k)) & 1) red[(ps.s * DOUT + k) * CP + ch] = acc[k];
+    });
     __syncthreads();
     float* op = a.out + (int64_t)i * (dm.d_out * C);
     for (int t = tid; t < DOUT * CP; t += 256) {
@@ -653,13 +694,36 @@ __global__ void __launch_bounds__(256, (DBL ? Tune<LM, LPE>::dbl_fwd_occ : Tune<
     }
 }
 
-template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool FSH = false>
+template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool FSH = false, bool PS = false>
+__global__ void __launch_bounds__(256, (fwd_bound<LM, LPE, DBL, PS>())) k_conv_fwd(FwdArgs a)
+{
+    __shared__ double red[FwdGeo<LM, LPE, H, PS>::kRed];
+    if constexpr (PS) {
+        // the pair's first wave (even wave index) takes the l3 = 1, 2 paths
+        if ((__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) == 0)
+            fwd_body<LM, LPE, H, SUB, DBL, FSH, PS, kPsMask0>(a, red);
+        else
+            fwd_body<LM, LPE, H, SUB, DBL, FSH, PS, kPsMask1>(a, red);
+    } else {
+        fwd_body<LM, LPE, H, SUB, DBL, FSH, PS, 0xF>(a, red);
+    }
+}
+
+template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool FSH = false, bool PS = false>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s)
 {
     if (a.sh.N == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_conv_fwd<LM, LPE, H, SUB, DBL, FSH>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0, s,
-                       a);
+    hipLaunchKernelGGL((k_conv_fwd<LM, LPE, H, SUB, DBL, FSH, PS>), dim3((unsigned)conv_grid(a.sh.N)), dim3(256), 0,
+                       s, a);
     return hipGetLastError();
+}
+
+// the double backward's receiver side; at degree 3 with one 64-lane slice
+// the path-split form
+template <int LM, int LPE, int H>
+hipError_t launch_fwd_dbl(const FwdArgs& a, hipStream_t s)
+{
+    return launch_fwd<LM, LPE, H, true, true, false, (LM == 3 && LPE == 64 && H == 1)>(a, s);
 }
 
 // ----------------------------------------------------------------------------
@@ -996,11 +1060,11 @@ struct BwdEdgeD : BwdEdge<Tb> {
     float gw[Tb::P], gy[Tb::DSH];
 };
 
-template <class Tb, bool SUB, bool UNI>
+template <class Tb, bool SUB, bool UNI, int L1M = 0xF>
 __device__ __forceinline__ void bwd_load_dbl(BwdEdgeD<Tb>& d, int32_t q, uint32_t chl, const BwdArgs& a,
                                              const Dims<Tb, SUB>& dm)
 {
-    bwd_load<Tb, SUB, UNI>(d, q, chl, a, dm);
+    bwd_load<Tb, SUB, UNI, true, false, L1M>(d, q, chl, a, dm);
     constexpr int P = Tb::P, DSH = Tb::DSH;
     const int32_t C = edge_stride(a.sh.C);
     chl = lane_offset(chl);
@@ -1009,7 +1073,9 @@ __device__ __forceinline__ void bwd_load_dbl(BwdEdgeD<Tb>& d, int32_t q, uint32_
         const float* wrow = a.ggW + (int64_t)e * (dm.P * C);
         static_for<0, P>([&](auto PI) {
             constexpr int p = decltype(PI)::value;
-            if constexpr (SUB) {
+            if constexpr (!((L1M >> Tb::data.l1[p]) & 1)) {
+                d.gw[p] = 0.0f;  // another wave's path
+            } else if constexpr (SUB) {
                 const float v = __builtin_nontemporal_load(at_lane(wrow + a.sh.woff[p], chl));
                 d.gw[p] = ((a.sh.active >> p) & 1) ? v : 0.0f;
             } else {
@@ -1032,7 +1098,7 @@ __device__ __forceinline__ void bwd_load_dbl(BwdEdgeD<Tb>& d, int32_t q, uint32_
     }
 }
 
-template <class Tb, class StoreW, class FlushY>
+template <class Tb, int L1M = 0xF, class StoreW, class FlushY>
 __device__ __forceinline__ void bwd_slice_dbl(const BwdEdgeD<Tb>& d, const double (&yv)[Tb::DSH],
                                               const double (&gyv)[Tb::DSH], const double (&xv)[Tb::DIN],
                                               const double (&gxv)[Tb::DIN], double (&dxa)[Tb::DIN],
@@ -1056,9 +1122,10 @@ __device__ __forceinline__ void bwd_slice_dbl(const BwdEdgeD<Tb>& d, const doubl
             static_for<0, Tb::P>([&](auto PI) {
                 constexpr int p = decltype(PI)::value;
                 using K = PathK<Tb, p>;
-                if constexpr (K::l2 == l2) {
+                if constexpr (K::l2 == l2 && ((L1M >> K::l1) & 1)) {
                     const double wd = (double)d.w[p], gwd = (double)d.gw[p];
                     static_for<0, K::d3>([&](auto M3) { opaque(gv[K::k3 + decltype(M3)::value]); });
+                    const PathCoefs<Tb, p> cf;
                     double v[d2];
                     bool vs[d2];
                     static_for<0, d2>([&](auto B) {
@@ -1080,7 +1147,7 @@ __device__ __forceinline__ void bwd_slice_dbl(const BwdEdgeD<Tb>& d, const doubl
                                 static_for<0, K::d3>([&](auto M3) {
                                     constexpr int m3 = decltype(M3)::value;
                                     constexpr double t = K::T(a, b, m3);
-                                    if constexpr (t != 0.0) mac(r, t, gv[K::k3 + m3], any);
+                                    if constexpr (t != 0.0) cf.template mac<a, b, m3>(r, gv[K::k3 + m3], any);
                                 });
                                 if (any) {
                                     mac(h, r, yv[k2 + b], hs);
@@ -1305,7 +1372,7 @@ __device__ __forceinline__ double readlane_d(double v, int l)
 template <int LM, int LPE, int H, bool SUB, bool DBL, bool FSH, bool PS = false>
 constexpr int bwd_bound()
 {
-    if (PS) return Tune<LM, LPE>::ps_bwd_occ;
+    if (PS) return DBL ? Tune<LM, LPE>::dbl_ps_bwd_occ : Tune<LM, LPE>::ps_bwd_occ;
     if (DBL) return Tune<LM, LPE>::dbl_bwd_occ;
     if (FSH && SUB && LM == 2 && LPE == 64 && H == 1) return 3;
     return Tune<LM, LPE>::bwd_occ;
@@ -1318,8 +1385,11 @@ constexpr int bwd_bound()
 // wave then holds x and grad_x of its own degrees only and the weights of its
 // own paths, which roughly halves its registers and raises occupancy; the
 // two waves' grad_Y partials of an edge meet in LDS like the two channel
-// slices of a C > 64 block.  Only the degree-3 plain backward uses it.
-constexpr int kPsMask0 = 0x6, kPsMask1 = 0x9;
+// slices of a C > 64 block.  The degree-3 backward with one slice per edge
+// uses it, and so does the sender side of its double backward (which also
+// holds the cotangent row ggx and ggW) unless the plan shares one weight over
+// all paths: that grad_W sums every path, which the split spreads over two
+// waves.
 
 // LDS of a backward block: per-wave grad_Y transpose tiles and, with two
 // waves per edge, the two waves' per-edge grad_Y sums of the current chunk
@@ -1347,8 +1417,6 @@ struct BwdLds {
     static constexpr int kStage = FSH && !kTile ? 4 * (64 / LPE) * DSH : 1;
 };
 
-// degree l of component k (k < 16)
-constexpr int degree_of(int k) { return k < 1 ? 0 : (k < 4 ? 1 : (k < 9 ? 2 : 3)); }
 
 // The backward of one block; the paths are those whose l1 is in L1M.
 template <int LM, int LPE, int H, bool SUB, bool DBL, bool MID, bool FSH, bool PS, int L1M>
@@ -1356,7 +1424,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a, double* __restrict__ 
                                          double* __restrict__ stage)
 {
     static_assert(!(FSH && (DBL || MID)), "the fused-SH form is the plain backward's");
-    static_assert(!PS || (!SUB && !DBL && !MID && !FSH && LPE == 64 && H == 1), "path split: plain, one slice");
+    static_assert(!PS || (!MID && !FSH && LPE == 64 && H == 1), "path split: plain or double backward, one slice");
     using Tb = cgmath::Tables<LM, LM, LM>;
     using Lz = BwdLds<LM, LPE, H, FSH, PS>;
     constexpr int HW = Lz::HW;
@@ -1396,8 +1464,11 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a, double* __restrict__ 
         if constexpr (DBL) {
             const float* grow = a.ggx ? a.ggx + (int64_t)j * (dm.d_in * C) : nullptr;
             static_for<0, DIN>([&](auto Kc) {
-                gxv[Kc] = grow ? (double)*at_lane(grow + Dims<Tb, SUB>::template comp<decltype(Kc)::value>(dm.d_in) * C, chl)
-                               : 0.0;
+                constexpr int k = decltype(Kc)::value;
+                if constexpr ((L1M >> degree_of(k)) & 1)
+                    gxv[k] = grow ? (double)*at_lane(grow + Dims<Tb, SUB>::template comp<k>(dm.d_in) * C, chl) : 0.0;
+                else
+                    gxv[k] = 0.0;  // another wave's degree: never read
             });
         }
     }
@@ -1414,7 +1485,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a, double* __restrict__ 
             const int32_t q = q0 + ps.s + S * t;
             if (q >= end) continue;  // uniform over the lanes of one edge
             Edge cur;
-            if constexpr (DBL) bwd_load_dbl<Tb, SUB, LPE == 64>(cur, q, chl, a, dm);
+            if constexpr (DBL) bwd_load_dbl<Tb, SUB, LPE == 64, L1M>(cur, q, chl, a, dm);
             else bwd_load<Tb, SUB, LPE == 64, !MID, FSH, L1M>(cur, q, chl, a, dm);
             if constexpr (HW == 2)
                 if (ps.h == 0 && lane == 0) eslot[ps.s * K + (t - t0)] = cur.ok ? cur.e : -1;
@@ -1427,7 +1498,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a, double* __restrict__ 
             // the edge's contraction (the backward's, or the double backward's)
             auto slice = [&](auto&& store_w, auto&& flush_y) {
                 if constexpr (DBL) {
-                    bwd_slice_dbl<Tb>(cur, yv, gyv, xv, gxv, dxa, store_w, flush_y);
+                    bwd_slice_dbl<Tb, L1M>(cur, yv, gyv, xv, gxv, dxa, store_w, flush_y);
                 } else if constexpr (MID) {
                     const int32_t Cg = edge_stride(C);
                     bwd_slice_mid<Tb>(cur.w, a.G + (int64_t)cur.i * (dm.d_out * Cg), Cg, lane_offset(chl), a.sh, yv,
@@ -1637,6 +1708,17 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
+// the double backward's sender side; at degree 3 with one 64-lane slice the
+// path-split form unless the plan shares one weight over all paths (its
+// grad_W sums every path, which the split spreads over two waves)
+template <int LM, int LPE, int H>
+hipError_t launch_bwd_dbl(const BwdArgs& a, hipStream_t s)
+{
+    if constexpr (LM == 3 && LPE == 64 && H == 1)
+        if (!a.sh.shared) return launch_bwd<LM, LPE, H, true, true, false, false, true>(a, s);
+    return launch_bwd<LM, LPE, H, true, true>(a, s);
+}
+
 template <int LM, int LPE, int H>
 constexpr KernelSet make_set()
 {
@@ -1646,8 +1728,8 @@ constexpr KernelSet make_set()
                      {&launch_fwd<LM, LPE, H, false>, &launch_fwd<LM, LPE, H, true>},
                      {&launch_bwd<LM, LPE, H, false, false, false, false, (LM == 3 && LPE == 64 && H == 1)>,
                       &launch_bwd<LM, LPE, H, true>},
-                     &launch_fwd<LM, LPE, H, true, true>,
-                     &launch_bwd<LM, LPE, H, true, true>,
+                     &launch_fwd_dbl<LM, LPE, H>,
+                     &launch_bwd_dbl<LM, LPE, H>,
                      &launch_fwd_mid<LM, LPE, H>,
                      &launch_bwd<LM, LPE, H, true, false, true>,
                      {&launch_fwd<LM, LPE, H, false, false, true>, &launch_fwd<LM, LPE, H, true, false, true>},

@@ -89,7 +89,7 @@ def test_double_backward_every_geometry(torch_dev, oracle, L, C):
 
 
 @pytest.mark.parametrize("li,ls,lo,C", [(2, 1, 3, 24), (3, 2, 1, 24), (1, 3, 2, 96), (0, 1, 1, 16), (2, 2, 0, 8),
-                                        (3, 3, 2, 128), (1, 0, 1, 40), (0, 0, 0, 64)])
+                                        (3, 3, 2, 128), (1, 0, 1, 40), (0, 0, 0, 64), (3, 2, 1, 64), (2, 3, 3, 48)])
 def test_double_backward_mixed_degrees(torch_dev, oracle, li, ls, lo, C):
     torch, dev = torch_dev
     run_dbl(torch, dev, oracle, li, ls, lo, C)
@@ -105,19 +105,20 @@ def test_double_backward_shared_path_weights(torch_dev, oracle, li, ls, lo, C):
 def test_double_backward_missing_cotangents(torch_dev, oracle, drop):
     """A cotangent passed as NULL counts as zero (all three NULL: zero results)."""
     torch, dev = torch_dev
-    for L, C in ((2, 32), (3, 128)):
+    for L, C in ((2, 32), (3, 128), (3, 64)):
         _, got = run_dbl(torch, dev, oracle, L, L, L, C, drop=drop)
         if len(drop) == 3:
             assert all(np.count_nonzero(t) == 0 for t in got)
 
 
 @pytest.mark.parametrize("want", [("grad_out",), ("x",), ("Y", "W"), ("x", "W")])
-def test_double_backward_partial_results(torch_dev, oracle, want):
+@pytest.mark.parametrize("L", [2, 3])
+def test_double_backward_partial_results(torch_dev, oracle, want, L):
     torch, dev = torch_dev
-    run_dbl(torch, dev, oracle, 2, 2, 2, 64, want=want)
+    run_dbl(torch, dev, oracle, L, L, L, 64, want=want)
 
 
-@pytest.mark.parametrize("L,C", [(1, 128), (2, 64), (3, 16)])
+@pytest.mark.parametrize("L,C", [(1, 128), (2, 64), (3, 16), (3, 48)])
 def test_double_backward_many_nodes(torch_dev, oracle, L, C):
     """A grid many rounds of resident blocks deep with short ragged segments."""
     torch, dev = torch_dev
