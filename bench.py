@@ -579,10 +579,10 @@ def _short(name):
     return name.replace("void ", "").replace("(anonymous namespace)::", "").replace("cgtp::", "").split("(")[0]
 
 
-# the step's forward and backward kernels by name: k_conv_fwd<LM, LPE, H, SUB, DBL, FSH> and
+# the step's forward and backward kernels by name: k_conv_fwd<LM, LPE, H, SUB, DBL, FSH, PS> and
 # k_conv_bwd<LM, LPE, H, SUB, DBL, MID, FSH, PS> with DBL, MID and FSH false (PS, the path-split
-# backward, is the degree-3 step's)
-STEP_KERNEL = {"conv_fwd": r"k_conv_fwd<\d+, \d+, \d+, (true|false), false, false>",
+# form, is the degree-3 step's backward)
+STEP_KERNEL = {"conv_fwd": r"k_conv_fwd<\d+, \d+, \d+, (true|false), false, false, (true|false)>",
                "conv_bwd": r"k_conv_bwd<\d+, \d+, \d+, (true|false), false, false, false, (true|false)>"}
 
 

@@ -215,6 +215,10 @@ struct Pos {
 // 2 waves; held to 3 waves it spills 12-20 bytes per lane with one 64-lane
 // slice per edge and is still 7-8% faster (2000- and 4000-atom layers), while
 // narrower slices would spill 80-100 bytes and keep 2.
+// The path-split kernels (degree 3, one 64-lane slice, two waves per edge)
+// hold half of a single wave's per-edge state: the backward fits 3 waves per
+// SIMD (168 registers and a 4-byte spill, measured 6% faster than 2 waves
+// with the whole path set), both sides of the double backward 2 (from 1).
 template <int LM, int LPE>
 struct Tune {
     static constexpr int fwd_occ = LM <= 2 ? 4 : 2;
