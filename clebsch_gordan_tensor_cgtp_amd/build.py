@@ -16,7 +16,7 @@ BUILD = os.path.join(ROOT, "_build")
 
 # the degree-3 kernels are split by lane geometry, one translation unit each,
 # so the slowest compiles run in parallel (longest first)
-SOURCES = ["cgtp_kernels_l3_c128.hip", "cgtp_kernels_l3_c64.hip", "cgtp_kernels_l3_c32.hip",
+SOURCES = ["cgtp_kernels_l3_c64_bwd.hip", "cgtp_kernels_l3_c64_bwd2.hip", "cgtp_kernels_l3_c128.hip", "cgtp_kernels_l3_c64.hip", "cgtp_kernels_l3_c32.hip",
            "cgtp_kernels_l3_c16.hip", "cgtp_kernels_l3_c8.hip", "cgtp_kernels_l2_wide.hip", "cgtp_kernels_l2.hip",
            "cgtp_kernels_l1.hip", "cgtp_cp.hip", "cgtp_mix.hip", "cgtp_registry.hip", "cgtp_graph.hip", "cgtp_forces.hip",
            "cgtp_cp_fit.cpp", "cgtp_api.cpp"]

@@ -1192,21 +1192,25 @@ __device__ __forceinline__ void bwd_slice_dbl(const BwdEdgeD<Tb>& d, const doubl
 // l3 slot.  Those rows are gathered per path; the next path's rows are loaded
 // before the current path is computed, so their latency overlaps its
 // arithmetic.
-template <class Tb>
+template <class Tb, int L1M = 0xF>
 struct L2Order {
     struct O {
         int p[kMaxPaths];
+        int n;
     };
+    // the paths whose l1 is in L1M, grouped by l2
     static constexpr O make()
     {
         O o{};
         int k = 0;
         for (int l2 = 0; l2 < 4; ++l2)
             for (int p = 0; p < Tb::P; ++p)
-                if (Tb::data.l2[p] == l2) o.p[k++] = p;
+                if (Tb::data.l2[p] == l2 && ((L1M >> Tb::data.l1[p]) & 1)) o.p[k++] = p;
+        o.n = k;
         return o;
     }
     static constexpr O ord = make();
+    static constexpr int N = ord.n;
 };
 
 template <class Tb, int p>
@@ -1224,24 +1228,41 @@ __device__ __forceinline__ void load_mid_rows(float (&g)[7], const float* grow, 
     }
 }
 
-template <class Tb, class StoreW, class FlushY>
+template <class Tb, int L1M = 0xF, class StoreW, class FlushY>
 __device__ __forceinline__ void bwd_slice_mid(const float (&w)[Tb::P], const float* grow, int32_t Cs, uint32_t chl,
                                               const Shape& sh, const double (&yv)[Tb::DSH],
                                               const double (&xv)[Tb::DIN], double (&dxa)[Tb::DIN],
                                               StoreW&& store_w, FlushY&& flush_y)
 {
-    using Ord = L2Order<Tb>;
+    // the paths whose l1 is in L1M (path-group split), grouped by l2; a degree
+    // l2 none of them has gets no grad_Y partials from this wave (zeros below)
+    using Ord = L2Order<Tb, L1M>;
+    constexpr int NP = Ord::N;
+    static_for<0, 4>([&](auto L2I) {
+        constexpr int l2 = decltype(L2I)::value;
+        constexpr bool has = [] {
+            for (int k = 0; k < NP; ++k)
+                if (Tb::data.l2[Ord::ord.p[k]] == l2) return true;
+            return false;
+        }();
+        if constexpr (!has && (l2 + 1) * (l2 + 1) <= Tb::DSH) {
+            double out[2 * l2 + 1];
+#pragma unroll
+            for (int b = 0; b < 2 * l2 + 1; ++b) out[b] = 0.0;
+            flush_y(std::integral_constant<int, l2 * l2>{}, out);
+        }
+    });
     float gcur[7], gnext[7];
     load_mid_rows<Tb, Ord::ord.p[0]>(gcur, grow, Cs, chl, sh);
     double dyb[7];
     bool dys[7];
-    static_for<0, Tb::P>([&](auto KI) {
+    static_for<0, NP>([&](auto KI) {
         constexpr int k = decltype(KI)::value;
         constexpr int p = Ord::ord.p[k];
         using K = PathK<Tb, p>;
         constexpr int l2 = K::l2, d2 = 2 * l2 + 1, k2 = l2 * l2;
         constexpr bool first = k == 0 || Tb::data.l2[Ord::ord.p[k > 0 ? k - 1 : 0]] != l2;
-        constexpr bool last = k + 1 == Tb::P || Tb::data.l2[Ord::ord.p[k + 1 < Tb::P ? k + 1 : k]] != l2;
+        constexpr bool last = k + 1 == NP || Tb::data.l2[Ord::ord.p[k + 1 < NP ? k + 1 : k]] != l2;
         if constexpr (first) {
 #pragma unroll
             for (int b = 0; b < 7; ++b) {
@@ -1249,7 +1270,7 @@ __device__ __forceinline__ void bwd_slice_mid(const float (&w)[Tb::P], const flo
                 dys[b] = false;
             }
         }
-        if constexpr (k + 1 < Tb::P) load_mid_rows<Tb, Ord::ord.p[k + 1 < Tb::P ? k + 1 : k]>(gnext, grow, Cs, chl, sh);
+        if constexpr (k + 1 < NP) load_mid_rows<Tb, Ord::ord.p[k + 1 < NP ? k + 1 : k]>(gnext, grow, Cs, chl, sh);
         const double wd = (double)w[p];
         double gv[K::d3];
 #pragma unroll
@@ -1302,7 +1323,7 @@ __device__ __forceinline__ void bwd_slice_mid(const float (&w)[Tb::P], const flo
             for (int b = 0; b < d2; ++b) out[b] = dys[b] ? dyb[b] : 0.0;
             flush_y(std::integral_constant<int, k2>{}, out);
         }
-        if constexpr (k + 1 < Tb::P)
+        if constexpr (k + 1 < NP)
 #pragma unroll
             for (int m = 0; m < 7; ++m) gcur[m] = gnext[m];
         __builtin_amdgcn_sched_barrier(0);
@@ -1428,7 +1449,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a, double* __restrict__ 
                                          double* __restrict__ stage)
 {
     static_assert(!(FSH && (DBL || MID)), "the fused-SH form is the plain backward's");
-    static_assert(!PS || (!MID && !FSH && LPE == 64 && H == 1), "path split: plain or double backward, one slice");
+    static_assert(!PS || (LPE == 64 && H == 1), "path split: one 64-lane slice per edge");
     using Tb = cgmath::Tables<LM, LM, LM>;
     using Lz = BwdLds<LM, LPE, H, FSH, PS>;
     constexpr int HW = Lz::HW;
@@ -1505,8 +1526,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a, double* __restrict__ 
                     bwd_slice_dbl<Tb, L1M>(cur, yv, gyv, xv, gxv, dxa, store_w, flush_y);
                 } else if constexpr (MID) {
                     const int32_t Cg = edge_stride(C);
-                    bwd_slice_mid<Tb>(cur.w, a.G + (int64_t)cur.i * (dm.d_out * Cg), Cg, lane_offset(chl), a.sh, yv,
-                                      xv, dxa, store_w, flush_y);
+                    bwd_slice_mid<Tb, L1M>(cur.w, a.G + (int64_t)cur.i * (dm.d_out * Cg), Cg, lane_offset(chl), a.sh,
+                                           yv, xv, dxa, store_w, flush_y);
                 } else {
                     bwd_slice<Tb, L1M>(cur.w, cur.g, yv, xv, dxa, store_w, flush_y);
                 }
@@ -1712,33 +1733,87 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
-// the double backward's sender side; at degree 3 with one 64-lane slice the
-// path-split form unless the plan shares one weight over all paths (its
-// grad_W sums every path, which the split spreads over two waves)
-template <int LM, int LPE, int H>
-hipError_t launch_bwd_dbl(const BwdArgs& a, hipStream_t s)
+// A backward launch (plain, SUB, double backward, per-path or fused-SH form).
+// At degree 3 with one 64-lane slice it is the path-split kernel, unless the
+// plan shares one weight over all paths: that grad_W sums every path, which
+// the split spreads over two waves.
+template <int LM, int LPE, int H, bool SUB, bool DBL = false, bool MID = false, bool FSH = false>
+hipError_t launch_bwd_any(const BwdArgs& a, hipStream_t s)
 {
-    if constexpr (LM == 3 && LPE == 64 && H == 1)
-        if (!a.sh.shared) return launch_bwd<LM, LPE, H, true, true, false, false, true>(a, s);
-    return launch_bwd<LM, LPE, H, true, true>(a, s);
+    if constexpr (LM == 3 && LPE == 64 && H == 1) {
+        if constexpr (SUB)
+            if (a.sh.shared) return launch_bwd<LM, LPE, H, SUB, DBL, MID, FSH, false>(a, s);
+        return launch_bwd<LM, LPE, H, SUB, DBL, MID, FSH, true>(a, s);
+    } else {
+        return launch_bwd<LM, LPE, H, SUB, DBL, MID, FSH, false>(a, s);
+    }
+}
+
+// The forward launchers of a lane geometry (backward fields null) and its
+// backward launchers in two parts (other fields null): a geometry's kernels
+// can be compiled in units that run in parallel.
+template <int LM, int LPE, int H>
+constexpr KernelSet make_set_fwd()
+{
+    KernelSet k{};
+    k.lm = LM;
+    k.lpe = LPE;
+    k.h = H;
+    k.fwd[0] = &launch_fwd<LM, LPE, H, false>;
+    k.fwd[1] = &launch_fwd<LM, LPE, H, true>;
+    k.fwd_dbl = &launch_fwd_dbl<LM, LPE, H>;
+    k.fwd_mid = &launch_fwd_mid<LM, LPE, H>;
+    k.fwd_sh[0] = &launch_fwd<LM, LPE, H, false, false, true>;
+    k.fwd_sh[1] = &launch_fwd<LM, LPE, H, true, false, true>;
+    return k;
+}
+
+// the backward launchers: the plain and fused-SH forms (part 1) and the
+// double-backward and per-path forms (part 2)
+template <int LM, int LPE, int H>
+constexpr KernelSet make_set_bwd1()
+{
+    KernelSet k{};
+    k.lm = LM;
+    k.lpe = LPE;
+    k.h = H;
+    k.bwd[0] = &launch_bwd_any<LM, LPE, H, false>;
+    k.bwd[1] = &launch_bwd_any<LM, LPE, H, true>;
+    k.bwd_sh[0] = &launch_bwd_any<LM, LPE, H, false, false, false, true>;
+    k.bwd_sh[1] = &launch_bwd_any<LM, LPE, H, true, false, false, true>;
+    return k;
+}
+
+template <int LM, int LPE, int H>
+constexpr KernelSet make_set_bwd2()
+{
+    KernelSet k{};
+    k.lm = LM;
+    k.lpe = LPE;
+    k.h = H;
+    k.bwd_dbl = &launch_bwd_any<LM, LPE, H, true, true>;
+    k.bwd_mid = &launch_bwd_any<LM, LPE, H, true, false, true>;
+    return k;
+}
+
+// the forward fields of f, the plain and fused-SH backward fields of b1 and
+// the double-backward and per-path backward fields of b2
+constexpr KernelSet merge_sets(const KernelSet& f, const KernelSet& b1, const KernelSet& b2)
+{
+    KernelSet k = f;
+    k.bwd[0] = b1.bwd[0];
+    k.bwd[1] = b1.bwd[1];
+    k.bwd_sh[0] = b1.bwd_sh[0];
+    k.bwd_sh[1] = b1.bwd_sh[1];
+    k.bwd_dbl = b2.bwd_dbl;
+    k.bwd_mid = b2.bwd_mid;
+    return k;
 }
 
 template <int LM, int LPE, int H>
 constexpr KernelSet make_set()
 {
-    return KernelSet{LM,
-                     LPE,
-                     H,
-                     {&launch_fwd<LM, LPE, H, false>, &launch_fwd<LM, LPE, H, true>},
-                     {&launch_bwd<LM, LPE, H, false, false, false, false, (LM == 3 && LPE == 64 && H == 1)>,
-                      &launch_bwd<LM, LPE, H, true>},
-                     &launch_fwd_dbl<LM, LPE, H>,
-                     &launch_bwd_dbl<LM, LPE, H>,
-                     &launch_fwd_mid<LM, LPE, H>,
-                     &launch_bwd<LM, LPE, H, true, false, true>,
-                     {&launch_fwd<LM, LPE, H, false, false, true>, &launch_fwd<LM, LPE, H, true, false, true>},
-                     {&launch_bwd<LM, LPE, H, false, false, false, true>,
-                      &launch_bwd<LM, LPE, H, true, false, false, true>}};
+    return merge_sets(make_set_fwd<LM, LPE, H>(), make_set_bwd1<LM, LPE, H>(), make_set_bwd2<LM, LPE, H>());
 }
 
 template <int LM>

@@ -445,7 +445,8 @@ CHANNELS = (1, 3, 8, 12, 16, 24, 32, 40, 64, 72, 96, 128)
 CASES = [(L, L, L, C) for L in (1, 2, 3) for C in CHANNELS]
 TRIPLES = [(a, b, c) for a in range(4) for b in range(4) for c in range(4)]
 MIXED = [(a, b, c, 24) for (a, b, c) in TRIPLES if not (a == b == c and a > 0)] + \
-        [(a, b, c, 96) for (a, b, c) in ((0, 0, 0), (2, 3, 2), (3, 1, 2), (1, 3, 3), (3, 3, 0), (2, 2, 1))]
+        [(a, b, c, 96) for (a, b, c) in ((0, 0, 0), (2, 3, 2), (3, 1, 2), (1, 3, 3), (3, 3, 0), (2, 2, 1))] + \
+        [(2, 3, 2, 64), (3, 1, 2, 48), (1, 3, 3, 40), (0, 3, 3, 33)]  # degree 3, one 64-lane slice: path-split
 
 
 def run_small(torch, dev, oracle, li, ls, lo, C, N=70, seed=0):
