@@ -44,3 +44,23 @@ def test_traffic_is_read_only_for_the_current_kernel_sources(tmp_path, monkeypat
     assert bench.read_traffic("conv_bwd", "layer") is None  # other sources
     f.write_text(f"hbm_bytes_per_launch = 123456\nkernel_source_sha = {sha}\n")
     assert bench.read_traffic("conv_bwd", "layer") == pytest.approx(123456.0)
+
+
+def test_step_kernel_names_pick_the_step_kernels():
+    """The summaries find the step's forward and backward among every
+    instantiation of the two templates by their full signature: the plain
+    (or SUB) form with DBL, MID and FSH false, either PS."""
+    step = ["void cgtp::k_conv_fwd<2, 64, 2, false, false, false, false>(cgtp::FwdArgs)",
+            "void cgtp::k_conv_bwd<2, 64, 2, false, false, false, false, false>(cgtp::BwdArgs)",
+            "void cgtp::k_conv_bwd<3, 64, 1, false, false, false, false, true>(cgtp::BwdArgs)"]
+    other = ["void cgtp::k_conv_fwd<2, 64, 2, true, true, false, false>(cgtp::FwdArgs)",       # double backward
+             "void cgtp::k_conv_fwd<3, 64, 1, true, true, false, true>(cgtp::FwdArgs)",
+             "void cgtp::k_conv_fwd<2, 64, 2, false, false, true, false>(cgtp::FwdArgs)",      # fused SH
+             "void cgtp::k_conv_bwd<2, 64, 2, true, true, false, false, false>(cgtp::BwdArgs)",
+             "void cgtp::k_conv_bwd<2, 64, 2, true, false, true, false, false>(cgtp::BwdArgs)",  # per-path
+             "void cgtp::k_conv_bwd<3, 64, 1, false, false, false, true, true>(cgtp::BwdArgs)"]  # fused SH
+    for name in step:
+        kern = "conv_fwd" if "k_conv_fwd" in name else "conv_bwd"
+        assert bench.re.search(bench.STEP_KERNEL[kern], name), name
+    for name in other:
+        assert not any(bench.re.search(p, name) for p in bench.STEP_KERNEL.values()), name
