@@ -1189,9 +1189,9 @@ __device__ __forceinline__ void bwd_slice_dbl(const BwdEdgeD<Tb>& d, const doubl
 // ---- per-path outputs, sender side ------------------------------------------
 // The backward of the per-path-output forward: as bwd_slice, with path p's
 // R_p formed from its own block of grad_out (rows moff[p] ..) instead of the
-// l3 slot.  Those rows are gathered per path; the next path's rows are loaded
-// before the current path is computed, so their latency overlaps its
-// arithmetic.
+// l3 slot.  Those rows are gathered per path, some paths ahead of the one
+// that uses them (kMidPrefetch), so their latency overlaps the arithmetic of
+// the paths in between.
 template <class Tb, int L1M = 0xF>
 struct L2Order {
     struct O {
@@ -1212,6 +1212,11 @@ struct L2Order {
     static constexpr O ord = make();
     static constexpr int N = ord.n;
 };
+
+// paths a per-path backward loads grad_out rows ahead (degree 3 holds up to
+// 156 rows per edge and has no registers to spare)
+template <class Tb>
+constexpr int kMidPrefetch = Tb::DIN <= 9 ? 4 : 1;
 
 template <class Tb, int p>
 __device__ __forceinline__ void load_mid_rows(float (&g)[7], const float* grow, int32_t Cs, uint32_t chl,
@@ -1252,13 +1257,20 @@ __device__ __forceinline__ void bwd_slice_mid(const float (&w)[Tb::P], const flo
             flush_y(std::integral_constant<int, l2 * l2>{}, out);
         }
     });
-    float gcur[7], gnext[7];
-    load_mid_rows<Tb, Ord::ord.p[0]>(gcur, grow, Cs, chl, sh);
+    // rows of path k are loaded PD paths ahead of its computation (every
+    // path's gather would otherwise wait out its own latency)
+    constexpr int PD = kMidPrefetch<Tb>;
+    float gb[NP][7];
+    static_for<0, (PD < NP ? PD : NP)>([&](auto KI) {
+        constexpr int k = decltype(KI)::value;
+        load_mid_rows<Tb, Ord::ord.p[k]>(gb[k], grow, Cs, chl, sh);
+    });
     double dyb[7];
     bool dys[7];
     static_for<0, NP>([&](auto KI) {
         constexpr int k = decltype(KI)::value;
         constexpr int p = Ord::ord.p[k];
+        const float(&gcur)[7] = gb[k];
         using K = PathK<Tb, p>;
         constexpr int l2 = K::l2, d2 = 2 * l2 + 1, k2 = l2 * l2;
         constexpr bool first = k == 0 || Tb::data.l2[Ord::ord.p[k > 0 ? k - 1 : 0]] != l2;
@@ -1270,7 +1282,7 @@ __device__ __forceinline__ void bwd_slice_mid(const float (&w)[Tb::P], const flo
                 dys[b] = false;
             }
         }
-        if constexpr (k + 1 < NP) load_mid_rows<Tb, Ord::ord.p[k + 1 < NP ? k + 1 : k]>(gnext, grow, Cs, chl, sh);
+        if constexpr (k + PD < NP) load_mid_rows<Tb, Ord::ord.p[k + PD < NP ? k + PD : k]>(gb[k + PD < NP ? k + PD : k], grow, Cs, chl, sh);
         const double wd = (double)w[p];
         double gv[K::d3];
 #pragma unroll
@@ -1323,9 +1335,6 @@ __device__ __forceinline__ void bwd_slice_mid(const float (&w)[Tb::P], const flo
             for (int b = 0; b < d2; ++b) out[b] = dys[b] ? dyb[b] : 0.0;
             flush_y(std::integral_constant<int, k2>{}, out);
         }
-        if constexpr (k + 1 < NP)
-#pragma unroll
-            for (int m = 0; m < 7; ++m) gcur[m] = gnext[m];
         __builtin_amdgcn_sched_barrier(0);
     });
 }
