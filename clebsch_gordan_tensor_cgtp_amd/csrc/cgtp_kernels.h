@@ -12,6 +12,10 @@
 //     sender keep x_j and grad_x[j] in registers, gather the grad_out rows of
 //     its receivers, write grad_W[e] per edge and grad_Y[e] reduced over the
 //     channels; no atomics                                   (k_conv_bwd)
+//   * at degree 3 with one 64-lane slice per edge, the backward and both
+//     sides of the double backward give each edge to a pair of waves that
+//     split its paths by degree (the abstract's path-group parallelism),
+//     halving each wave's registers
 // (graph preparation lives in cgtp_graph.hip)
 //
 // Arithmetic is fp64 on fp32 data: the per-edge contraction and the sums over
