@@ -30,17 +30,17 @@ def _case(torch, dev, oracle, N, L, C, seed):
     return g, T(g.row_ptr), T(g.src), T(x), T(Y), T(W), T(G)
 
 
-def test_noalloc_backward_matches_workspace_backward(torch_dev, oracle):
+@pytest.mark.parametrize("L,C", [(2, 128), (3, 64)])  # (3, 64): the path-split backward
+def test_noalloc_backward_matches_workspace_backward(torch_dev, oracle, L, C):
     torch, dev = torch_dev
     from clebsch_gordan_tensor_cgtp_amd import _lib
     from clebsch_gordan_tensor_cgtp_amd.ops import Plan, _ptr, _stream
-    L, C = 2, 128
     plan = Plan(L, L, L, C)
     lib = _lib.lib()
     for N, seed in ((3000, 11), (700, 12)):            # the second call is smaller
         g, rp, src, x, Y, W, G = _case(torch, dev, oracle, N, L, C, seed)
         E = g.n_edges
-        print(f"[noalloc] N={N} E={E}", flush=True)
+        print(f"[noalloc] L={L} C={C} N={N} E={E}", flush=True)
         ref = plan.conv_bwd(rp, src, x, Y, W, G)       # workspace path
         dx = torch.full((N, plan.dim_in, C), float("nan"), device=dev)
         dW = torch.full((E, plan.num_paths, C), float("nan"), device=dev)
