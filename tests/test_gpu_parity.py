@@ -517,28 +517,31 @@ def test_conv_many_nodes(torch_dev, oracle, L, C):
     assert_parity(dY, rdY, "dY")
 
 
-def test_conv_empty_graph(torch_dev, oracle):
+@pytest.mark.parametrize("L", [2, 3])  # 3: the path-split backward
+def test_conv_empty_graph(torch_dev, oracle, L):
     torch, dev = torch_dev
     from clebsch_gordan_tensor_cgtp_amd.ops import Plan
-    plan = Plan(2, 2, 2, 64)
+    C = 64
+    plan = Plan(L, L, L, C)
+    D, P = plan.dim_in, plan.num_paths
     for N in (9, 1):
         rp = torch.zeros(N + 1, dtype=torch.int32, device=dev)
         sr = torch.zeros(0, dtype=torch.int32, device=dev)
-        x = torch.randn(N, 9, 64, device=dev)
-        Y = torch.zeros(0, 9, device=dev)
-        W = torch.zeros(0, 15, 64, device=dev)
+        x = torch.randn(N, D, C, device=dev)
+        Y = torch.zeros(0, D, device=dev)
+        W = torch.zeros(0, P, C, device=dev)
         ws = plan.graph_prepare(rp, sr)
         out = plan.conv_fwd(rp, sr, x, Y, W, ws)
-        dx, dW, dY = plan.conv_bwd(rp, sr, x, Y, W, torch.randn(N, 9, 64, device=dev), ws)
+        dx, dW, dY = plan.conv_bwd(rp, sr, x, Y, W, torch.randn(N, D, C, device=dev), ws)
         torch.cuda.synchronize()
         assert torch.count_nonzero(out) == 0 and torch.count_nonzero(dx) == 0
-        assert dW.shape == (0, 15, 64) and dY.shape == (0, 9)
+        assert dW.shape == (0, P, C) and dY.shape == (0, D)
     # no nodes at all
     rp0 = torch.zeros(1, dtype=torch.int32, device=dev)
     ws0 = plan.graph_prepare(rp0, sr)
-    out0 = plan.conv_fwd(rp0, sr, torch.zeros(0, 9, 64, device=dev), Y, W, ws0)
-    assert out0.shape == (0, 9, 64)
-    assert plan.sh(torch.zeros(0, 3, device=dev)).shape == (0, 9)
+    out0 = plan.conv_fwd(rp0, sr, torch.zeros(0, D, C, device=dev), Y, W, ws0)
+    assert out0.shape == (0, D, C)
+    assert plan.sh(torch.zeros(0, 3, device=dev)).shape == (0, D)
 
 
 def test_validate_flag_rejects_malformed_csr(torch_dev):
